@@ -1,0 +1,460 @@
+"""CPU oracle for the ConvRot-quantized linear forward.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this module.  The GPU library never calls it and shares no code with
+it: the two meet only through the seeded inputs of ``synthetic_inputs``.
+
+Plain NumPy, written for a reader to check against the pages by eye.  Vector
+operations run over independent rows / groups; the arithmetic order inside one
+output follows the definitions below and nothing is blocked, fused or
+reordered.
+
+Sources (web pages; cited by title and section):
+
+* [QIE]  "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4 (+ConvRot, mixed int8
+         fallback)" model card: intro paragraph (packed signed INT4, 2/byte,
+         group-256 regular-Hadamard ConvRot, online activation rotation,
+         dynamic INT4 activations, calibration-free); "Speed" table (fused
+         ConvRot + rank-one s4 MMA kernel; int8_tensorwise kernels).
+* [Q3N]  "qwen3-4b-nvfp4-convrot" asset page: file table and converter
+         flags (ConvRot INT8 row-scaled, group size 256).
+* [QVL]  "Qwen3-VL-4B-W4A8-ConvRot" model page: file table
+         (asym_w4a8_int8, group 16, convrot_groupsize 256).
+* [REB]  "Rebels_w4a8s" collection page: "What's inside a file" table (int4
+         codes two per byte, fp8 scale per group of 16, one scale per output
+         channel, 16 Lloyd-Max levels); "Mixed formats where the kernel
+         demands it" (group exactly 256, int8_tensorwise for other widths);
+         "Why W4A8 instead of GGUF" (int8 GEMM, ~0.56 B/param, ~7% weight
+         error).
+* [ZIT]  "Z-Image-Turbo-W4A4-ConvRot" model card: "Where Z-Image sits"
+         (convrot_groupsize sweep 256 / 64 / 16; a size-N rotation spreads
+         an outlier over N channels).
+
+Readings taken where the pages are silent (each also listed in the design
+notes of the repository):
+
+R1  Hadamard: Sylvester order-256 matrix H[i,j] = (-1)^popcount(i&j), scaled
+    by 1/16 so it is orthonormal.  ("regular-Hadamard" read as the standard
+    Sylvester construction.)
+R2  Rotation arithmetic: float32, fast Walsh-Hadamard butterflies with strides
+    1,2,4,...,128 in that order, each (a, b) -> (a+b, a-b), then one multiply
+    by 0.0625 (exact).  The rotated value stays float32 until quantised.
+R3  Activation scale: per row over the full K, s = absmax / 7 in float32
+    (IEEE division); code = clip(rint(v / s), -8, 7) with round-half-even.
+    A row of zeros has s = 0 and codes 0.
+R4  Weight scale (W4A4): one per tensor, absmax of the *rotated* weight / 7.
+R5  Accumulation: exact integer sum over the full K (int32 range).
+R6  Epilogue: y = fl(fl(float32(acc) * s_x[m]) * s_w) + float32(bias[n]),
+    in float32; the GPU result is this value rounded to bf16.
+R7  int8_tensorwise: no rotation; x per row absmax/127, W per tensor
+    absmax/127, codes clip(rint(v/s), -128, 127); any K.
+R8  W4A8 decode: w8 = clip(rint(float32(cb[idx]) * e4m3(s_rel)), -127, 127)
+    with one float32 multiply; one int32 accumulation over the full K; the
+    epilogue uses s_channel[n] in place of s_w.  Activations: rotated, per
+    row absmax/127, clip [-128, 127].
+R9  fp8 is OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF are NaN, max 448).
+R10 W4A8 encode (offline): s_channel[n] = absmax_k |W~[n,:]| / 127;
+    s_rel[n,g] = e4m3_rne(min(absmax_{k in g} |W~| / s_channel[n], 127));
+    u = W~ / (s_channel * s_rel) (0 where the divisor is 0); 16-level
+    Lloyd-Max quantiser of all u of the tensor, decision thresholds at the
+    midpoints, levels at the cell means, initialised at the (j+1/2)/16
+    quantiles, at most 100 iterations; idx = the cell of u (a value on a
+    threshold goes to the lower level).
+R11 Canonical int4 storage: two's complement nibbles, low nibble = even k.
+
+Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
+codebooks are correct and the GPU consumes whatever codebook it is given; its
+tests check only properties (sorted levels, non-increasing distortion,
+plausible weight error).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 256
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float32
+# ---------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32; exact."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_rne(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits.
+
+    NaN maps to a quiet NaN."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))
+    r = r.astype(np.uint16)
+    nan = np.isnan(a)
+    if np.any(nan):
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# The rotation  [QIE intro: group-256 regular-Hadamard ConvRot; ZIT "Where
+# Z-Image sits": rotation of size N spreads an outlier over N channels]
+# ---------------------------------------------------------------------------
+
+def hadamard(n: int = GROUP) -> np.ndarray:
+    """Closed form of the normalised Sylvester Hadamard matrix (float64).
+
+    H[i, j] = (-1)^popcount(i & j) / sqrt(n)   (reading R1)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bits = np.bitwise_and(i, j)
+    pop = np.zeros_like(bits)
+    b = bits.copy()
+    while np.any(b):
+        pop += b & 1
+        b >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0) / np.sqrt(n)
+
+
+def fwht(v: np.ndarray, group: int = GROUP, dtype=np.float32) -> np.ndarray:
+    """Group-wise rotation along the last axis: each contiguous block of
+    ``group`` values is multiplied by the normalised Sylvester Hadamard.
+
+    Reading R2: butterflies with strides 1, 2, 4, ... group/2 in that order,
+    each pair (i, i+h) with i & h == 0 becoming (a+b, a-b), computed in
+    ``dtype``; then one multiply by 1/sqrt(group) (a power of two for the
+    group sizes used: 16, 64, 256)."""
+    v = np.asarray(v)
+    K = v.shape[-1]
+    if K % group != 0:
+        raise ValueError(f"K={K} is not a multiple of the rotation group {group}")
+    lead = v.shape[:-1]
+    y = np.array(v, dtype=dtype).reshape(-1, K // group, group)
+    R, G = y.shape[0], y.shape[1]
+    h = 1
+    while h < group:
+        y = y.reshape(R, G, group // (2 * h), 2, h)
+        a = y[:, :, :, 0, :].copy()
+        b = y[:, :, :, 1, :].copy()
+        y[:, :, :, 0, :] = a + b
+        y[:, :, :, 1, :] = a - b
+        h *= 2
+    y = y.reshape(R, G, group)
+    scale = dtype(1.0 / np.sqrt(group))
+    y = y * scale
+    return y.reshape(*lead, K).astype(dtype)
+
+
+# ---------------------------------------------------------------------------
+# Symmetric quantisation  [QIE intro: activations "dynamically quantized to
+# INT4"; weights packed signed INT4, tensorwise]
+# ---------------------------------------------------------------------------
+
+def _quant_with_scale(v: np.ndarray, amax: np.ndarray, qmax: int, lo: int, hi: int):
+    """s = fl(amax / qmax); q = clip(rint(v / s), lo, hi); s == 0 -> q = 0.
+
+    ``amax`` broadcasts against ``v`` (per row: shape [R, 1]; per tensor: a
+    scalar)."""
+    amax = np.asarray(amax, dtype=F32)
+    s = (amax / F32(qmax)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(v.astype(F32) / s)
+    r = np.where(s == 0, F32(0), r)
+    q = np.clip(r, lo, hi).astype(np.int8)
+    return q, s
+
+
+def quant_rows(v: np.ndarray, qmax: int, lo: int, hi: int):
+    """Per-row dynamic symmetric quantisation (readings R3, R7).
+
+    Returns (codes int8 [R, K], scales float32 [R])."""
+    v = np.asarray(v, dtype=F32)
+    amax = np.max(np.abs(v), axis=1, keepdims=True) if v.shape[1] else np.zeros((v.shape[0], 1), F32)
+    q, s = _quant_with_scale(v, amax, qmax, lo, hi)
+    return q, s.reshape(-1)
+
+
+def quant_tensor(v: np.ndarray, qmax: int, lo: int, hi: int):
+    """Tensorwise symmetric quantisation (readings R4, R7).
+
+    Returns (codes int8, scale float32 scalar)."""
+    v = np.asarray(v, dtype=F32)
+    amax = np.max(np.abs(v)) if v.size else F32(0)
+    q, s = _quant_with_scale(v, F32(amax), qmax, lo, hi)
+    return q, F32(s)
+
+
+# --- W4A4 ----------------------------------------------------------------
+
+def quant_act_w4a4(x_bits: np.ndarray, group: int = GROUP):
+    """Online rotation + dynamic per-row INT4 codes of the activations."""
+    xr = fwht(bf16_to_f32(x_bits), group)
+    return quant_rows(xr, 7, -8, 7)
+
+
+def quant_weight_w4(w_bits: np.ndarray, group: int = GROUP):
+    """Offline rotation + tensorwise INT4 codes of the weight [N, K]."""
+    wr = fwht(bf16_to_f32(w_bits), group)
+    return quant_tensor(wr, 7, -8, 7)
+
+
+# --- int8_tensorwise -------------------------------------------------------
+
+def quant_act_int8(x_bits: np.ndarray):
+    """int8_tensorwise activations: no rotation, per row absmax/127."""
+    return quant_rows(bf16_to_f32(x_bits), 127, -128, 127)
+
+
+def quant_weight_int8tw(w_bits: np.ndarray):
+    """int8_tensorwise weight: no rotation, per tensor absmax/127."""
+    return quant_tensor(bf16_to_f32(w_bits), 127, -128, 127)
+
+
+# --- W4A8 activations ------------------------------------------------------
+
+def quant_act_w4a8(x_bits: np.ndarray, group: int = GROUP):
+    """W4A8 activations: group-256 rotation, then per-row int8 (absmax/127)."""
+    xr = fwht(bf16_to_f32(x_bits), group)
+    return quant_rows(xr, 127, -128, 127)
+
+
+# ---------------------------------------------------------------------------
+# Canonical nibble packing (reading R11)
+# ---------------------------------------------------------------------------
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """int4 codes [R, K] (values in [-8, 7]) -> bytes [R, K/2], low nibble =
+    even k, two's complement."""
+    q = np.asarray(q, dtype=np.int8)
+    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_int4` (signed codes)."""
+    p = np.asarray(p, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def unpack_uint4(p: np.ndarray) -> np.ndarray:
+    """Unsigned nibbles (codebook indices) [R, K/2] -> [R, K], low = even k."""
+    p = np.asarray(p, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def pack_uint4(idx: np.ndarray) -> np.ndarray:
+    idx = np.asarray(idx, dtype=np.uint8)
+    return (idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Integer GEMM and rank-one epilogue  [QIE "Speed": rank-one s4 MMA]
+# ---------------------------------------------------------------------------
+
+def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k qx[m, k] * qw[n, k], exact (reading R5).
+
+    Computed with a float64 matrix product on integer-valued operands: every
+    product and partial sum is an integer of magnitude below 2^53 for the
+    sizes used (|code| <= 128, K < 2^30 / 2^14), so the float64 result is the
+    exact integer.  Raises if the result leaves the int32 range."""
+    qx = np.asarray(qx)
+    qw = np.asarray(qw)
+    K = qx.shape[1]
+    assert qw.shape[1] == K
+    bound = int(np.max(np.abs(qx.astype(np.int64)), initial=0)) * \
+        int(np.max(np.abs(qw.astype(np.int64)), initial=0)) * K
+    if bound >= 2 ** 53:
+        raise OverflowError("float64 product would not be exact")
+    acc = qx.astype(np.float64) @ qw.astype(np.float64).T
+    acc = acc.astype(np.int64)
+    if acc.size and (acc.max() > 2 ** 31 - 1 or acc.min() < -2 ** 31):
+        raise OverflowError("accumulator leaves int32")
+    return acc.astype(np.int32)
+
+
+def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w, bias_bits: np.ndarray | None):
+    """Rank-one rescale (reading R6): fl(fl(float32(acc)*s_x[m])*s_w) + bias[n].
+
+    ``s_w`` is a scalar (tensorwise) or a per-column vector (W4A8 s_channel).
+    Returns float32 [M, N] (not rounded to bf16)."""
+    a = np.asarray(acc).astype(F32)
+    y = (a * np.asarray(s_x, dtype=F32)[:, None]).astype(F32)
+    sw = np.asarray(s_w, dtype=F32)
+    y = (y * (sw[None, :] if sw.ndim == 1 else sw)).astype(F32)
+    if bias_bits is not None:
+        y = (y + bf16_to_f32(bias_bits)[None, :]).astype(F32)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# End-to-end linears (float32 pre-bf16 output)
+# ---------------------------------------------------------------------------
+
+def linear_w4a4(x_bits, w_bits, bias_bits=None, group: int = GROUP):
+    """ConvRot W4A4 linear [QIE intro + "Speed"].
+
+    Returns dict with codes, scales, acc and the float32 output."""
+    qx, sx = quant_act_w4a4(x_bits, group)
+    qw, sw = quant_weight_w4(w_bits, group)
+    acc = int_gemm(qx, qw)
+    return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
+
+
+def linear_int8tw(x_bits, w_bits, bias_bits=None):
+    """int8_tensorwise linear [QIE intro "stock int8_tensorwise"; REB "Mixed
+    formats": no group constraint]."""
+    qx, sx = quant_act_int8(x_bits)
+    qw, sw = quant_weight_int8tw(w_bits)
+    acc = int_gemm(qx, qw)
+    return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
+
+
+# ---------------------------------------------------------------------------
+# OCP E4M3FN  (reading R9; [REB] "fp8 scale, one per group of 16")
+# ---------------------------------------------------------------------------
+
+def e4m3_to_f32(code: np.ndarray) -> np.ndarray:
+    """Decode E4M3FN bytes: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    exponent 0: subnormal m/8 * 2^-6; S.1111.111 is NaN; no infinities."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * val
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return val.astype(F32)
+
+
+def _e4m3_positive_table() -> np.ndarray:
+    return e4m3_to_f32(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float64)  # 0x00..0x7E
+
+
+def f32_to_e4m3_rne(v: np.ndarray) -> np.ndarray:
+    """Encode finite values of magnitude <= 448 to E4M3FN, nearest value,
+    ties to the even code (even mantissa).  Raises on larger magnitudes."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(~np.isfinite(v)) or np.any(np.abs(v) > 448.0):
+        raise ValueError("value outside the finite E4M3FN range")
+    table = _e4m3_positive_table()          # increasing, codes 0..126
+    a = np.abs(v)
+    hi = np.searchsorted(table, a, side="left")          # first table >= a
+    hi = np.clip(hi, 0, len(table) - 1)
+    lo = np.clip(hi - 1, 0, len(table) - 1)
+    dlo = a - table[lo]
+    dhi = table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    sign = np.where(v < 0, 0x80, 0).astype(np.uint8)
+    return (code | sign).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# W4A8 codebook format  ([REB] "What's inside a file"; [QVL] group 16,
+# convrot_groupsize 256)
+# ---------------------------------------------------------------------------
+
+def w4a8_decode(idx: np.ndarray, s_rel: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """Decode to int8 weights (reading R8).
+
+    idx: uint8 codebook indices [N, K] (already unpacked); s_rel: e4m3 bytes
+    [N, K/16]; codebook: float32 [16].  w8 = clip(rint(cb[idx]*s), -127, 127)
+    with one float32 multiply."""
+    idx = np.asarray(idx)
+    N, K = idx.shape
+    cb = np.asarray(codebook, dtype=F32)
+    s = e4m3_to_f32(s_rel)                         # [N, K/16]
+    s_full = np.repeat(s, 16, axis=1)              # [N, K]
+    prod = (cb[idx] * s_full).astype(F32)
+    prod = np.where(np.isnan(prod), F32(0), prod)
+    return np.clip(np.rint(prod), -127, 127).astype(np.int8)
+
+
+def linear_w4a8(x_bits, idx_packed, s_rel, codebook, s_channel, bias_bits=None,
+                group: int = GROUP):
+    """Asym W4A8 codebook linear ([REB] "int8 tensor cores do the work",
+    "keeps compute in int8 end to end"; reading R8)."""
+    qx, sx = quant_act_w4a8(x_bits, group)
+    w8 = w4a8_decode(unpack_uint4(idx_packed), s_rel, codebook)
+    acc = int_gemm(qx, w8)
+    return dict(qx=qx, sx=sx, w8=w8, acc=acc,
+                y=epilogue(acc, sx, np.asarray(s_channel, F32), bias_bits))
+
+
+def lloyd_max_16(u: np.ndarray, iters: int = 100):
+    """16-level Lloyd-Max scalar quantiser of the samples ``u`` (reading R10).
+
+    Thresholds are midpoints of adjacent levels, levels are the means of their
+    cells.  Works on sorted samples with prefix sums, which gives the same
+    cells as assigning each sample to its nearest level.  Returns
+    (levels float32 [16] sorted, list of distortion per iteration)."""
+    s = np.sort(np.asarray(u, dtype=np.float64).ravel())
+    n = s.size
+    if n == 0:
+        return np.zeros(16, F32), []
+    csum = np.concatenate([[0.0], np.cumsum(s)])
+    csq = np.concatenate([[0.0], np.cumsum(s * s)])
+    q = (np.arange(16) + 0.5) / 16.0
+    levels = np.quantile(s, q)
+    hist = []
+
+    def cells(lv):
+        thr = 0.5 * (lv[:-1] + lv[1:])
+        # a sample equal to a threshold belongs to the lower cell
+        return np.concatenate([[0], np.searchsorted(s, thr, side="right"), [n]])
+
+    for _ in range(iters):
+        b = cells(levels)
+        cnt = b[1:] - b[:-1]
+        sums = csum[b[1:]] - csum[b[:-1]]
+        sq = csq[b[1:]] - csq[b[:-1]]
+        dist = float(np.sum(sq - 2 * levels * sums + cnt * levels ** 2))
+        hist.append(dist)
+        new = np.where(cnt > 0, sums / np.maximum(cnt, 1), levels)
+        new = np.sort(new)
+        if np.array_equal(new, levels):
+            break
+        levels = new
+    return levels.astype(F32), hist
+
+
+def w4a8_encode(w_bits: np.ndarray, group: int = GROUP, iters: int = 100):
+    """Offline W4A8 encode of a bf16 weight [N, K] (reading R10).
+
+    Returns dict(idx_packed uint8 [N,K/2], s_rel e4m3 [N,K/16], codebook
+    float32 [16], s_channel float32 [N], distortion history)."""
+    wr = fwht(bf16_to_f32(w_bits), group)                       # float32 [N, K]
+    N, K = wr.shape
+    if K % 16 != 0:
+        raise ValueError("K must be a multiple of 16")
+    s_ch = (np.max(np.abs(wr), axis=1) / F32(127)).astype(F32)  # [N]
+    gmax = np.max(np.abs(wr).reshape(N, K // 16, 16), axis=2)   # [N, K/16]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(s_ch[:, None] > 0, gmax / s_ch[:, None], F32(0)).astype(F32)
+    rel = np.minimum(rel, F32(127))
+    s_rel = f32_to_e4m3_rne(rel)
+    s_rel_f = e4m3_to_f32(s_rel)
+    div = (np.repeat(s_rel_f, 16, axis=1) * s_ch[:, None]).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(div > 0, wr / div, F32(0)).astype(F32)
+    cb, hist = lloyd_max_16(u, iters)
+    thr = 0.5 * (cb[:-1].astype(np.float64) + cb[1:].astype(np.float64))
+    idx = np.searchsorted(thr, u.astype(np.float64).ravel(), side="left").reshape(N, K)
+    idx = idx.astype(np.uint8)
+    return dict(idx_packed=pack_uint4(idx), idx=idx, s_rel=s_rel, codebook=cb,
+                s_channel=s_ch, distortion=hist, w_rot=wr)

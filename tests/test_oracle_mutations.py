@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching) and
+check that the pins in test_oracle_pins catch every one of them."""
+import numpy as np
+import pytest
+
+from oracle import convrot_oracle as O
+import tests.test_oracle_pins as P
+
+F32 = np.float32
+_real_fwht = O.fwht
+_real_quant = O._quant_with_scale
+
+
+def _fwht_generic(v, group=256, dtype=np.float32, order="asc", sign_swap=False, scale=True):
+    v = np.asarray(v)
+    K = v.shape[-1]
+    lead = v.shape[:-1]
+    y = np.array(v, dtype=dtype).reshape(-1, K // group, group)
+    R, G = y.shape[0], y.shape[1]
+    hs = []
+    h = 1
+    while h < group:
+        hs.append(h)
+        h *= 2
+    if order == "desc":
+        hs = hs[::-1]
+    for h in hs:
+        y = y.reshape(R, G, group // (2 * h), 2, h)
+        a = y[:, :, :, 0, :].copy()
+        b = y[:, :, :, 1, :].copy()
+        y[:, :, :, 0, :] = a + b
+        y[:, :, :, 1, :] = (b - a) if sign_swap else (a - b)
+    y = y.reshape(R, G, group)
+    if scale:
+        y = y * dtype(1.0 / np.sqrt(group))
+    return y.reshape(*lead, K).astype(dtype)
+
+
+def _quant_floor(v, amax, qmax, lo, hi):
+    amax = np.asarray(amax, dtype=F32)
+    s = (amax / F32(qmax)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.trunc(v.astype(F32) / s)
+    r = np.where(s == 0, F32(0), r)
+    return np.clip(r, lo, hi).astype(np.int8), s
+
+
+def _quant_qmax8(v, amax, qmax, lo, hi):
+    return _real_quant(v, amax, qmax + 1 if qmax == 7 else qmax, lo, hi)
+
+
+def _quant_rows_tensor_scale(v, qmax, lo, hi):
+    v = np.asarray(v, dtype=F32)
+    amax = np.full((v.shape[0], 1), np.max(np.abs(v)), F32)
+    q, s = _real_quant(v, amax, qmax, lo, hi)
+    return q, s.reshape(-1)
+
+
+def _gemm_reversed_k(qx, qw):
+    return (qx.astype(np.float64) @ qw[:, ::-1].astype(np.float64).T).astype(np.int64).astype(np.int32)
+
+
+def _epilogue_no_sw(acc, s_x, s_w, bias_bits):
+    a = np.asarray(acc).astype(F32)
+    y = (a * np.asarray(s_x, F32)[:, None]).astype(F32)
+    if bias_bits is not None:
+        y = y + O.bf16_to_f32(bias_bits)[None, :]
+    return y
+
+
+def _e4m3_bias8(code):
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    val = np.where((e == 15) & (m == 7), np.nan, sign * val)
+    return val.astype(F32)
+
+
+def _decode_clamp128(idx, s_rel, codebook):
+    cb = np.asarray(codebook, F32)
+    s = np.repeat(O.e4m3_to_f32(s_rel), 16, axis=1)
+    return np.clip(np.rint((cb[np.asarray(idx)] * s).astype(F32)), -128, 127).astype(np.int8)
+
+
+def _pack_high_first(q):
+    u = (np.asarray(q, np.int8).astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
+
+
+MUTATIONS = {
+    "fwht_descending_order": ("fwht", lambda v, group=256, dtype=np.float32:
+                              _fwht_generic(v, group, dtype, order="desc")),
+    "fwht_sign_swapped": ("fwht", lambda v, group=256, dtype=np.float32:
+                          _fwht_generic(v, group, dtype, sign_swap=True)),
+    "fwht_missing_normalisation": ("fwht", lambda v, group=256, dtype=np.float32:
+                                   _fwht_generic(v, group, dtype, scale=False)),
+    "quant_truncates": ("_quant_with_scale", _quant_floor),
+    "quant_divides_by_8": ("_quant_with_scale", _quant_qmax8),
+    "act_scale_per_tensor": ("quant_rows", _quant_rows_tensor_scale),
+    "gemm_reversed_k": ("int_gemm", _gemm_reversed_k),
+    "epilogue_drops_weight_scale": ("epilogue", _epilogue_no_sw),
+    "e4m3_wrong_bias": ("e4m3_to_f32", _e4m3_bias8),
+    "w4a8_clamp_128": ("w4a8_decode", _decode_clamp128),
+    "pack_nibble_order": ("pack_int4", _pack_high_first),
+}
+
+PINS = [
+    P.test_hadamard_orthonormal_exact,
+    P.test_fwht_unit_vectors_give_hadamard_rows,
+    P.test_fwht_float64_equals_dense_product,
+    P.test_fwht_float32_within_error_bound,
+    P.test_fwht_stage_order_fixture,
+    P.test_exact_identity_before_quantisation,
+    P.test_one_hot_row_codes,
+    lambda: P.test_constant_row_codes(0.5),
+    P.test_zero_row_and_bias_only_output,
+    P.test_quant_invariants,
+    P.test_pack_roundtrip,
+    P.test_acc_brute_force_python_ints_tiny,
+    P.test_epilogue_exact_for_power_of_two_scales,
+    P.test_end_to_end_close_to_float_linear,
+    P.test_e4m3_decode_matches_torch,
+    P.test_w4a8_decode_hand_cases,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, bad)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:
+            caught.append(getattr(pin, "__name__", "lambda"))
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle
+itself: closed forms, exact identities, hand-derived fixtures, library
+routines (torch's float8 cast), brute-force integer sums, and the figures the
+model cards print.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from oracle import convrot_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _popcount(v: int) -> int:
+    return bin(v).count("1")
+
+
+# ---------------------------------------------------------------------------
+# Hadamard closed form
+# ---------------------------------------------------------------------------
+
+def test_hadamard_orthonormal_exact():
+    H = O.hadamard(256)
+    assert np.array_equal(H @ H.T, np.eye(256))      # exact in float64
+    assert np.array_equal(H, H.T)
+
+
+def test_hadamard_matches_sylvester_recursion():
+    # H_1 = [1]; H_2n = [[H, H], [H, -H]]  (unnormalised), an independent
+    # construction of the same matrix
+    h = np.array([[1.0]])
+    while h.shape[0] < 256:
+        h = np.block([[h, h], [h, -h]])
+    assert np.array_equal(O.hadamard(256) * 16.0, h)
+    for n in (16, 64):
+        g = np.array([[1.0]])
+        while g.shape[0] < n:
+            g = np.block([[g, g], [g, -g]])
+        assert np.allclose(O.hadamard(n) * np.sqrt(n), g, rtol=0, atol=0)
+
+
+def test_fwht_unit_vectors_give_hadamard_rows():
+    eye = np.eye(256, dtype=F32)
+    got = O.fwht(eye)                         # row j = e_j rotated
+    want = np.array([[(-1.0) ** _popcount(i & j) / 16 for j in range(256)] for i in range(256)])
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_fwht_float64_equals_dense_product():
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(5, 1024))
+    got = O.fwht(x, 256, dtype=np.float64)
+    H = O.hadamard(256)
+    want = (x.reshape(5, 4, 256) @ H).reshape(5, 1024)
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+
+
+def test_fwht_float32_within_error_bound():
+    rng = np.random.default_rng(4)
+    x32 = rng.standard_t(3, size=(8, 512)).astype(F32)
+    got = O.fwht(x32).astype(np.float64)
+    H = O.hadamard(256)
+    want = (x32.astype(np.float64).reshape(8, 2, 256) @ H).reshape(8, 512)
+    l1 = np.abs(x32.astype(np.float64)).reshape(8, 2, 256).sum(-1)            # ||x_g||_1
+    bound = 8 * 2.0 ** -24 * l1 / 16 * 1.0001
+    err = np.abs(got - want).reshape(8, 2, 256)
+    assert np.all(err <= bound[:, :, None])
+
+
+def test_fwht_stage_order_fixture():
+    g = _golden("fwht_order_case.json")
+    x = np.zeros((1, 256), dtype=np.uint16)
+    for k, h in g["input_bf16_hex"].items():
+        x[0, int(k)] = int(h, 16)
+    y = O.fwht(O.bf16_to_f32(x))
+    want = np.array([int(h, 16) for h in g["expected_rotated_f32_hex_by_k_mod_4"]], dtype=np.uint32)
+    assert np.array_equal(y.view(np.uint32)[0], np.tile(want, 64))
+    q, s = O.quant_act_w4a4(x)
+    assert np.array_equal(q[0], np.tile(np.array(g["expected_int4_codes_by_k_mod_4"], np.int8), 64))
+    assert s.view(np.uint32)[0] == int(g["expected_scale_f32_hex"], 16)
+
+
+def test_exact_identity_before_quantisation():
+    L = si.tiny()
+    x = O.bf16_to_f32(L.x).astype(np.float64)
+    w = O.bf16_to_f32(L.w).astype(np.float64)
+    xr = O.fwht(x, 256, dtype=np.float64)
+    wr = O.fwht(w, 256, dtype=np.float64)
+    lhs = xr @ wr.T
+    rhs = x @ w.T
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
+
+
+# ---------------------------------------------------------------------------
+# Special cases of the quantiser
+# ---------------------------------------------------------------------------
+
+def test_one_hot_row_codes():
+    K, j, g = 512, 37, 1
+    x = np.zeros((1, K), F32)
+    x[0, 256 * g + j] = 3.0
+    q, s = O.quant_act_w4a4(si.f32_to_bf16_bits(x))
+    sign = np.array([1 if _popcount(j & k) % 2 == 0 else -1 for k in range(256)])
+    assert np.array_equal(q[0, 256 * g:], (7 * sign).astype(np.int8))
+    assert np.all(q[0, :256] == 0)
+    assert s[0] == F32(F32(3.0 / 16) / F32(7))
+    assert list(q[0, 256:264]) == [7, -7, 7, -7, -7, 7, -7, 7]
+
+
+@pytest.mark.parametrize("c", [0.5, -2.0, 1.0])
+def test_constant_row_codes(c):
+    K = 768
+    x = np.full((1, K), c, F32)
+    q, s = O.quant_act_w4a4(si.f32_to_bf16_bits(x))
+    want = np.zeros(K, np.int8)
+    want[0::256] = 7 if c > 0 else -7
+    assert np.array_equal(q[0], want)
+    assert s[0] == F32(F32(16 * abs(c)) / F32(7))
+
+
+def test_zero_row_and_bias_only_output():
+    L = si.random_layer(4, 512, 32, seed=5, bias=True)
+    L.x[2, :] = 0
+    r = O.linear_w4a4(L.x, L.w, L.bias)
+    assert r["sx"][2] == 0 and np.all(r["qx"][2] == 0)
+    assert np.array_equal(r["y"][2], O.bf16_to_f32(L.bias))
+
+
+def test_quant_invariants():
+    L = si.tiny()
+    qx, sx = O.quant_act_w4a4(L.x)
+    xr = O.fwht(O.bf16_to_f32(L.x))
+    assert qx.min() >= -8 and qx.max() <= 7
+    assert np.all(np.max(np.abs(qx), axis=1) == 7)
+    err = np.abs(xr.astype(np.float64) - sx[:, None].astype(np.float64) * qx)
+    assert np.all(err <= sx[:, None] * 0.5 * (1 + 1e-6))
+    qw, sw = O.quant_weight_w4(L.w)
+    assert np.max(np.abs(qw)) == 7 and qw.min() >= -8
+    q8, s8 = O.quant_act_int8(L.x)
+    assert np.all(np.max(np.abs(q8.astype(np.int32)), axis=1) == 127)
+
+
+def test_pack_roundtrip():
+    rng = np.random.default_rng(1)
+    q = rng.integers(-8, 8, size=(7, 64)).astype(np.int8)
+    p = O.pack_int4(q)
+    assert p.shape == (7, 32)
+    assert np.array_equal(O.unpack_int4(p), q)
+    # low nibble = even k, two's complement: codes (-1, 3) -> 0x3F
+    assert O.pack_int4(np.array([[-1, 3]], np.int8))[0, 0] == 0x3F
+    assert O.pack_int4(np.array([[-8, 7]], np.int8))[0, 0] == 0x78
+
+
+# ---------------------------------------------------------------------------
+# Integer accumulation
+# ---------------------------------------------------------------------------
+
+def test_acc_brute_force_python_ints_tiny():
+    L = si.tiny()
+    r = O.linear_w4a4(L.x, L.w)
+    qx, qw, acc = r["qx"], r["qw"], r["acc"]
+    for m in (0, 5, 63):
+        for n in (0, 17, 255):
+            s = 0
+            for k in range(qx.shape[1]):
+                s += int(qx[m, k]) * int(qw[n, k])
+            assert acc[m, n] == s
+    full = (qx[:, None, :].astype(np.int64) * qw[None, :, :].astype(np.int64)).sum(-1)
+    assert np.array_equal(acc.astype(np.int64), full)
+    assert np.max(np.abs(acc)) <= 64 * qx.shape[1]
+
+
+def test_acc_brute_force_int8_k2688():
+    L = si.random_layer(7, 2688, 7, seed=9)
+    r = O.linear_int8tw(L.x, L.w)
+    qx, qw = r["qx"].astype(np.int64), r["qw"].astype(np.int64)
+    for m in range(7):
+        for n in range(7):
+            assert r["acc"][m, n] == sum(int(a) * int(b) for a, b in zip(qx[m], qw[n]))
+
+
+def test_epilogue_exact_for_power_of_two_scales():
+    acc = np.array([[3, -5], [1000, 0]], np.int32)
+    sx = np.array([2.0 ** -3, 2.0 ** 4], F32)
+    sw = F32(2.0 ** -7)
+    bias = si.f32_to_bf16_bits(np.array([0.5, -0.25], F32))
+    y = O.epilogue(acc, sx, sw, bias)
+    want = np.array([[3 / 1024 + 0.5, -5 / 1024 - 0.25], [1000 / 8 + 0.5, -0.25]])
+    assert np.array_equal(y.astype(np.float64), want)
+    y2 = O.epilogue(acc, sx, np.array([2.0 ** -1, 2.0 ** 2], F32), None)
+    assert np.array_equal(y2.astype(np.float64),
+                          np.array([[3 / 16, -5 / 2], [1000 * 8, 0]]))
+
+
+def test_end_to_end_close_to_float_linear():
+    L = si.random_layer(32, 1024, 64, seed=2, bias=True, outlier_count=6)
+    r = O.linear_w4a4(L.x, L.w, L.bias)
+    ref = O.bf16_to_f32(L.x).astype(np.float64) @ O.bf16_to_f32(L.w).astype(np.float64).T \
+        + O.bf16_to_f32(L.bias)
+    rel = np.linalg.norm(r["y"] - ref) / np.linalg.norm(ref)
+    assert 0.02 < rel < 0.35
+    r8 = O.linear_int8tw(L.x, L.w, L.bias)
+    rel8 = np.linalg.norm(r8["y"] - ref) / np.linalg.norm(ref)
+    assert rel8 < 0.1 and rel8 < rel
+
+
+def test_rotation_and_group_size_reduce_error():
+    """[ZIT] 'Where Z-Image sits': a rotation of size N spreads an outlier
+    over N channels, so the error falls as the group grows."""
+    L = si.random_layer(64, 2048, 128, seed=11, outlier_count=10, outlier_scale=40.0)
+    x = O.bf16_to_f32(L.x).astype(np.float64)
+    w = O.bf16_to_f32(L.w).astype(np.float64)
+    ref = x @ w.T
+
+    def err(group):
+        if group is None:
+            qx, sx = O.quant_rows(O.bf16_to_f32(L.x), 7, -8, 7)
+            qw, sw = O.quant_tensor(O.bf16_to_f32(L.w), 7, -8, 7)
+        else:
+            qx, sx = O.quant_act_w4a4(L.x, group)
+            qw, sw = O.quant_weight_w4(L.w, group)
+        y = O.epilogue(O.int_gemm(qx, qw), sx, sw, None)
+        return np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+    e_none, e16, e64, e256 = err(None), err(16), err(64), err(256)
+    assert e256 < e64 < e16 < e_none
+
+
+def test_int8tw_weight_error_near_page_figure():
+    facts = _golden("page_facts.json")
+    L = si.random_layer(1, 3072, 512, seed=6)
+    qw, sw = O.quant_weight_int8tw(L.w)
+    w = O.bf16_to_f32(L.w).astype(np.float64)
+    rel = np.linalg.norm(qw * np.float64(sw) - w) / np.linalg.norm(w)
+    assert 0.3 * facts["int8_tensorwise_weight_error"]["value"] < rel < \
+        3 * facts["int8_tensorwise_weight_error"]["value"]
+
+
+# ---------------------------------------------------------------------------
+# E4M3 and the W4A8 format
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = O.e4m3_to_f32(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.uniform(0, 448, 20000), rng.uniform(0, 0.05, 20000),
+                        -rng.uniform(0, 200, 2000),
+                        O.e4m3_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)])
+    v = v.astype(F32)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.f32_to_e4m3_rne(v)
+    assert np.array_equal(got, want)
+
+
+def test_w4a8_decode_hand_cases():
+    cb = np.linspace(-1.0, 1.0, 16).astype(F32)
+    idx = np.zeros((1, 32), np.uint8)
+    idx[0, :16] = np.arange(16)
+    idx[0, 16:] = 15
+    s_rel = np.array([[0x38, 0x67]], np.uint8)     # 1.0 and 0x67 = 2^5 * 1.875 = 60
+    w8 = O.w4a8_decode(idx, s_rel, cb)
+    assert np.array_equal(w8[0, :16], np.rint(cb).astype(np.int8))
+    assert np.all(w8[0, 16:] == 60)
+    s_big = np.array([[0x78, 0x78]], np.uint8)     # 256: 1.0 * 256 clamps to 127
+    assert np.all(O.w4a8_decode(idx, s_big, cb)[0, 16:] == 127)
+    assert O.w4a8_decode(idx, s_big, cb)[0, 0] == -127
+
+
+def test_w4a8_storage_matches_page_bytes_per_param():
+    facts = _golden("page_facts.json")
+    K = 3840
+    bytes_per_row = K / facts["int4_codes_per_byte"]["value"] + K / facts["w4a8_scale_group"]["value"]
+    assert bytes_per_row / K == pytest.approx(0.5625)
+    assert abs(bytes_per_row / K - facts["w4a8_bytes_per_param"]["value"]) < 0.01
+
+
+def test_lloyd_max_uniform_closed_form():
+    # the optimal 16-level quantiser of U(-1, 1) is uniform: levels (2j+1)/16 - 1
+    rng = np.random.default_rng(0)
+    u = rng.uniform(-1, 1, 400_000)
+    cb, hist = O.lloyd_max_16(u, iters=300)
+    want = (2 * np.arange(16) + 1) / 16 - 1
+    assert np.max(np.abs(cb - want)) < 0.01
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(hist, hist[1:]))
+
+
+def test_lloyd_max_gaussian_textbook_levels():
+    # Max (1960), 16-level minimum-MSE quantiser for N(0,1): positive levels
+    want = np.array([0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6181, 2.0690, 2.7326])
+    rng = np.random.default_rng(1)
+    cb, _ = O.lloyd_max_16(rng.normal(size=1_000_000), iters=500)
+    assert np.all(np.diff(cb) > 0)
+    assert np.max(np.abs(np.sort(np.abs(cb[8:])) - want)) < 0.03
+    assert np.max(np.abs(cb[:8][::-1] + want)) < 0.03
+
+
+def test_w4a8_encode_weight_error_near_page_figure():
+    facts = _golden("page_facts.json")
+    L = si.random_layer(1, 1024, 256, seed=8)
+    enc = O.w4a8_encode(L.w)
+    w8 = O.w4a8_decode(enc["idx"], enc["s_rel"], enc["codebook"])
+    rec = w8.astype(np.float64) * enc["s_channel"][:, None]
+    wr = enc["w_rot"].astype(np.float64)
+    rel = np.linalg.norm(rec - wr) / np.linalg.norm(wr)
+    page = facts["w4a8_weight_rel_l2"]["value"]
+    assert 0.5 * page < rel < 1.7 * page
+    assert np.all(np.diff(enc["codebook"]) > 0)
+    assert np.array_equal(O.unpack_uint4(enc["idx_packed"]), enc["idx"])
+    h = enc["distortion"]
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(h, h[1:]))
+
+
+def test_w4a8_linear_runs_and_is_close():
+    L = si.random_layer(16, 512, 64, seed=12, bias=True)
+    enc = O.w4a8_encode(L.w)
+    r = O.linear_w4a8(L.x, enc["idx_packed"], enc["s_rel"], enc["codebook"], enc["s_channel"], L.bias)
+    ref = O.bf16_to_f32(L.x).astype(np.float64) @ O.bf16_to_f32(L.w).astype(np.float64).T \
+        + O.bf16_to_f32(L.bias)
+    rel = np.linalg.norm(r["y"] - ref) / np.linalg.norm(ref)
+    assert rel < 0.15
+    assert np.max(np.abs(r["w8"].astype(np.int32))) <= 127
+
+
+def test_bf16_rne():
+    v = np.array([1.0, 1.00390625, 1.005859375, -3.0e38, 1e-40], F32)
+    got = O.f32_to_bf16_rne(v)
+    # 1+2^-8 is a tie -> 1.0 (even); 1+3*2^-9 rounds up to 1+2^-7
+    assert got[0] == 0x3F80 and got[1] == 0x3F80 and got[2] == 0x3F81
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    w = (rng.normal(size=10000) * 10).astype(F32)
+    want = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16_rne(w), want)
