@@ -1,0 +1,168 @@
+/*
+ * convrot.h - C ABI of the ConvRot-quantized linear forward on MI355X (gfx950).
+ *
+ * The method (model cards cited by title and section):
+ *   [QIE] "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4 (+ConvRot, mixed int8
+ *         fallback)", intro and "Speed" table: weights stored as packed signed
+ *         INT4, two per byte, rotated offline with a group-256 Hadamard
+ *         (ConvRot); activations rotated online and quantised to INT4
+ *         dynamically inside the kernel; integer MMA with a rank-one rescale.
+ *   [REB] "Rebels_w4a8s", "What's inside a file" and "Mixed formats where the
+ *         kernel demands it": the W4A8 codebook format (int4 codebook indices,
+ *         an fp8 scale per group of 16, a scale per output channel, 16
+ *         Lloyd-Max levels), int8 GEMM; layers whose input width is not a
+ *         multiple of 256 use int8_tensorwise instead.
+ *
+ * Arithmetic (shared by every entry point, float32 unless stated):
+ *   rotation   each contiguous 256-block of K is multiplied by the Sylvester
+ *              Hadamard matrix scaled by 1/16: butterflies with strides
+ *              1,2,...,128 in that order, (a,b)->(a+b,a-b), then x0.0625.
+ *   act quant  per row m: s_x[m] = absmax_k / Q (IEEE division),
+ *              code = clamp(rint(v / s_x[m])) with round-half-even;
+ *              Q = 7, codes [-8,7] (W4A4); Q = 127, codes [-128,127]
+ *              (int8_tensorwise: no rotation; W4A8: rotated).  s = 0 -> 0.
+ *   GEMM       acc[m,n] = sum_k qx[m,k] * qw[n,k], exact int32.
+ *   epilogue   y[m,n] = bf16_rne(fl(fl(float(acc) * s_x[m]) * s_w) + bias[n])
+ *              with s_w the tensor scale (W4A4, int8_tensorwise) or
+ *              s_channel[n] (W4A8).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no memory, keeps no device state and never synchronises.
+ *   - Work is enqueued on `stream` (NULL = the null stream) in order; results
+ *     are valid once the stream reaches that point.
+ *   - bf16 tensors are row-major uint16 bit patterns; x is [M,K], W is [N,K]
+ *     (y = x W^T), y is [M,N], bias is [N] and may be NULL.
+ *   - Pointers must be 16-byte aligned.
+ *   - Argument errors are detected before any launch and nothing is enqueued;
+ *     cr_last_error() (thread-local) then holds a message.  A launch failure
+ *     returns CR_ERR_LAUNCH with the HIP error text.  Nothing aborts or prints.
+ *   - Calls are re-entrant; two calls that share a workspace or an output must
+ *     be ordered by the caller (same stream or events).
+ *   - Packed weight layouts are opaque; sizes come from cr_packed_bytes().
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CR_OK = 0,
+    CR_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    CR_ERR_SHAPE = 2,      /* M < 0, N < 1, K < 1, or a size beyond the limits  */
+    CR_ERR_GROUP = 3,      /* K is not a multiple of 256 (W4A4, W4A8)           */
+    CR_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                  */
+    CR_ERR_WORKSPACE = 5,  /* workspace smaller than cr_workspace_bytes()       */
+    CR_ERR_DEVICE = 6,     /* current device is not gfx950 / no device          */
+    CR_ERR_LAUNCH = 7,     /* a kernel launch failed                            */
+    CR_ERR_KIND = 8        /* unknown format kind                               */
+} cr_status;
+
+/* Format kinds. */
+#define CR_W4A4 0    /* ConvRot W4A4: INT4 weights (tensorwise), INT4 activations */
+#define CR_INT8TW 1  /* int8_tensorwise: int8 weights (tensorwise), int8 activations */
+#define CR_W4A8 2    /* asym W4A8 codebook: 4-bit codebook weights, int8 activations */
+
+/* Limits: 1 <= N, K <= CR_MAX_DIM; 0 <= M <= CR_MAX_DIM. */
+#define CR_MAX_DIM (1 << 20)
+/* Largest K the rotated activation quantiser accepts (W4A4, W4A8). */
+#define CR_MAX_ROT_K 65536
+
+/* Bytes of the packed weight of `kind` for an [N,K] weight (0 on bad args). */
+size_t cr_packed_bytes(int kind, int N, int K);
+
+/* Bytes of workspace cr_linear_* / cr_dbg_linear_acc need for these sizes
+ * (0 on bad args; at least 256 otherwise).  The workspace holds the
+ * quantised activations, their scales and split-K partial sums; its contents
+ * need no initialisation and are meaningless after the call. */
+size_t cr_workspace_bytes(int kind, int M, int N, int K);
+
+/* ---- W4A4 ConvRot ([QIE] intro; "Speed": fused ConvRot + rank-one s4 MMA) */
+
+/* Offline weight preparation: rotate each 256-block of every row of W,
+ * s_w = absmax(rotated W) / 7, codes = clamp(rint(v / s_w), -8, 7), written
+ * in the packed layout.
+ *   w_bf16   [N,K] bf16                     (in)
+ *   w_packed cr_packed_bytes(CR_W4A4,N,K)   (out)
+ *   w_scale  1 float                        (out; also used as scratch)
+ * K must be a multiple of 256 (CR_ERR_GROUP otherwise). */
+cr_status cr_pack_weight_w4(const void* w_bf16, int N, int K, void* w_packed,
+                            float* w_scale, hipStream_t stream);
+
+/* y = W4A4 ConvRot linear of x (rotation, per-row INT4 codes, int32 GEMM
+ * against the packed weight, rank-one epilogue, optional bias).
+ *   x_bf16 [M,K]; w_packed/w_scale from cr_pack_weight_w4 with the same N,K;
+ *   bias_bf16 [N] or NULL; y_bf16 [M,N] (out);
+ *   ws / ws_bytes: workspace of at least cr_workspace_bytes(CR_W4A4,M,N,K).
+ * M = 0 is a no-op.  K % 256 != 0 -> CR_ERR_GROUP (no silent fallback:
+ * such layers use cr_linear_int8tw). */
+cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed,
+                         const float* w_scale, int N, const void* bias_bf16,
+                         void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- int8_tensorwise ([QIE] intro "stock int8_tensorwise"; [REB] "Mixed
+ *      formats": no group constraint) -------------------------------------- */
+
+/* s_w = absmax(W) / 127, codes = clamp(rint(w / s_w), -128, 127); any K. */
+cr_status cr_pack_weight_int8tw(const void* w_bf16, int N, int K, void* w_packed,
+                                float* w_scale, hipStream_t stream);
+
+/* y = int8_tensorwise linear (no rotation; per-row int8 activations). */
+cr_status cr_linear_int8tw(const void* x_bf16, int M, int K, const void* w_packed,
+                           const float* w_scale, int N, const void* bias_bf16,
+                           void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- asym W4A8 codebook ([REB] "What's inside a file", "Why W4A8 instead of
+ *      GGUF": int8 GEMM at ~0.56 B/param) -------------------------------- */
+
+/* Re-lay the stored W4A8 tensors for the GEMM and build the decode table
+ * T[c][i] = clamp(rint(codebook[i] * e4m3(c)), -127, 127) (NaN codes -> 0).
+ *   idx        [N,K/2] uint8, codebook index nibbles, low nibble = even k
+ *   s_rel_e4m3 [N,K/16] uint8, OCP E4M3FN scale per group of 16 along K
+ *   codebook   16 float
+ *   w_packed   cr_packed_bytes(CR_W4A8,N,K) (out)
+ * K must be a multiple of 256. */
+cr_status cr_pack_weight_w4a8(const void* idx, const void* s_rel_e4m3,
+                              const float* codebook, int N, int K, void* w_packed,
+                              hipStream_t stream);
+
+/* y = W4A8 linear: rotated per-row int8 activations (absmax/127) times the
+ * decoded int8 weight w8[n,k] = T[s_rel[n,k/16]][idx[n,k]], int32 accumulation,
+ * epilogue with s_channel[n] (float [N]) in place of s_w. */
+cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed,
+                         const float* s_channel, int N, const void* bias_bf16,
+                         void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- status ----------------------------------------------------------- */
+const char* cr_status_str(cr_status s);
+const char* cr_last_error(void);   /* thread-local detail of the last failure */
+
+/* ---- inspection hooks (canonical layouts, for bit-exact checks) ---------- */
+
+/* Activation codes and scales exactly as the linear of `kind` computes them.
+ *   codes  [M,K] int8 (W4A4 codes in [-8,7], stored one per byte)
+ *   scales [M] float */
+cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K,
+                           void* codes, float* scales, hipStream_t stream);
+
+/* Weight codes from a packed weight, canonical row-major [N,K] int8
+ * (W4A4: [-8,7]; int8_tensorwise: [-128,127]; W4A8: the decoded int8 w8). */
+cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K,
+                               void* codes, hipStream_t stream);
+
+/* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
+ * linear, epilogue replaced by a plain int32 store). */
+cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K,
+                            const void* w_packed, int N, int32_t* acc,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONVROT_H */

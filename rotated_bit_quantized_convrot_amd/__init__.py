@@ -1,0 +1,284 @@
+"""ConvRot-quantized linear forward on MI355X (gfx950).
+
+Thin ctypes binding over ``libconvrot.so`` (C ABI in ``include/convrot.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensors, passes device pointers and the current stream, and uses
+torch as the device-memory allocator.  There is no CPU fallback: if the
+library is missing or the device is not a gfx950, calls raise.
+
+Formats (model cards cited by title and section):
+  * W4A4 ConvRot  - [QIE] "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4
+    (+ConvRot, mixed int8 fallback)", intro: INT4 weights two per byte with a
+    group-256 Hadamard rotation, INT4 activations quantised in the kernel.
+  * int8_tensorwise - same card, intro; [REB] "Rebels_w4a8s", "Mixed formats
+    where the kernel demands it": used for layers whose K is not a multiple
+    of 256.
+  * asym W4A8 codebook - [REB] "What's inside a file".
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "W4A4", "INT8TW", "W4A8", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
+    "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8",
+    "linear_w4a4", "linear_int8tw", "linear_w4a8",
+    "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
+    "PackedWeight", "pack_linear", "linear",
+]
+
+W4A4, INT8TW, W4A8 = 0, 1, 2
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.so")
+_LIB = None
+
+_STATUS = {0: "CR_OK", 1: "CR_ERR_NULL", 2: "CR_ERR_SHAPE", 3: "CR_ERR_GROUP", 4: "CR_ERR_ALIGN",
+           5: "CR_ERR_WORKSPACE", 6: "CR_ERR_DEVICE", 7: "CR_ERR_LAUNCH", 8: "CR_ERR_KIND"}
+
+EXPORTS = [
+    "cr_packed_bytes", "cr_workspace_bytes", "cr_pack_weight_w4", "cr_linear_w4a4",
+    "cr_pack_weight_int8tw", "cr_linear_int8tw", "cr_pack_weight_w4a8", "cr_linear_w4a8",
+    "cr_status_str", "cr_last_error", "cr_dbg_quant_act", "cr_dbg_unpack_weight",
+    "cr_dbg_linear_acc",
+]
+
+
+class ConvRotError(RuntimeError):
+    """A library call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libconvrot.so (built in-tree by ``build_lib``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m rotated_bit_quantized_convrot_amd.build_lib`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "cr_packed_bytes": (sz, [i, i, i]),
+        "cr_workspace_bytes": (sz, [i, i, i, i]),
+        "cr_pack_weight_w4": (i, [vp, i, i, vp, vp, vp]),
+        "cr_pack_weight_int8tw": (i, [vp, i, i, vp, vp, vp]),
+        "cr_pack_weight_w4a8": (i, [vp, vp, vp, i, i, vp, vp]),
+        "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_status_str": (ctypes.c_char_p, [i]),
+        "cr_last_error": (ctypes.c_char_p, []),
+        "cr_dbg_quant_act": (i, [i, vp, i, i, vp, vp, vp]),
+        "cr_dbg_unpack_weight": (i, [i, vp, i, i, vp, vp]),
+        "cr_dbg_linear_acc": (i, [i, vp, i, i, vp, i, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise ConvRotError(status, lib().cr_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def packed_bytes(kind: int, N: int, K: int) -> int:
+    return int(lib().cr_packed_bytes(kind, N, K))
+
+
+def workspace_bytes(kind: int, M: int, N: int, K: int) -> int:
+    return int(lib().cr_workspace_bytes(kind, M, N, K))
+
+
+def _empty_u8(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Weight preparation (offline)
+# ---------------------------------------------------------------------------
+
+def pack_weight_w4(w: torch.Tensor):
+    """bf16 [N,K] -> (packed uint8, scale float32[1]) in the W4A4 format."""
+    _dev(w, "w", torch.bfloat16)
+    N, K = w.shape
+    nb = packed_bytes(W4A4, N, K)
+    if nb == 0:
+        _check(lib().cr_pack_weight_w4(_ptr(w), N, K, None, None, None) or 2)
+    out = _empty_u8(nb, w.device)
+    scale = torch.empty(4, dtype=torch.float32, device=w.device)
+    _check(lib().cr_pack_weight_w4(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
+    return out, scale
+
+
+def pack_weight_int8tw(w: torch.Tensor):
+    """bf16 [N,K] -> (packed uint8, scale float32[1]) in the int8_tensorwise format."""
+    _dev(w, "w", torch.bfloat16)
+    N, K = w.shape
+    nb = packed_bytes(INT8TW, N, K)
+    if nb == 0:
+        _check(lib().cr_pack_weight_int8tw(_ptr(w), N, K, None, None, None) or 2)
+    out = _empty_u8(nb, w.device)
+    scale = torch.empty(4, dtype=torch.float32, device=w.device)
+    _check(lib().cr_pack_weight_int8tw(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
+    return out, scale
+
+
+def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Tensor, N: int, K: int):
+    """Stored W4A8 tensors -> packed uint8 (index nibbles [N,K/2], e4m3 scale
+    codes [N,K/16] as uint8, codebook float32[16])."""
+    _dev(idx, "idx", torch.uint8)
+    _dev(s_rel, "s_rel", torch.uint8)
+    _dev(codebook, "codebook", torch.float32)
+    if idx.numel() != N * K // 2 or s_rel.numel() != N * K // 16 or codebook.numel() != 16:
+        raise ValueError("W4A8 tensor sizes do not match N, K")
+    nb = packed_bytes(W4A8, N, K)
+    if nb == 0:
+        _check(lib().cr_pack_weight_w4a8(_ptr(idx), _ptr(s_rel), _ptr(codebook), N, K, None, None) or 2)
+    out = _empty_u8(nb, idx.device)
+    _check(lib().cr_pack_weight_w4a8(_ptr(idx), _ptr(s_rel), _ptr(codebook), N, K, _ptr(out), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Linears
+# ---------------------------------------------------------------------------
+
+def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace):
+    _dev(x, "x", torch.bfloat16)
+    _dev(packed, "packed", torch.uint8)
+    _dev(scale, "scale", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    need = workspace_bytes(kind, M, N, K)
+    if need == 0:  # invalid shapes: let the library report the reason
+        need = 256
+    if workspace is None:
+        workspace = _empty_u8(need, x.device)
+    else:
+        _dev(workspace, "workspace", torch.uint8)
+    fn = getattr(lib(), fn_name)
+    _check(fn(_ptr(x), M, K, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
+              _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def linear_w4a4(x, packed, scale, N, bias=None, out=None, workspace=None):
+    """y = ConvRot W4A4 linear (x bf16 [M,K], K % 256 == 0)."""
+    return _linear("cr_linear_w4a4", W4A4, x, packed, scale, N, bias, out, workspace)
+
+
+def linear_int8tw(x, packed, scale, N, bias=None, out=None, workspace=None):
+    """y = int8_tensorwise linear (any K)."""
+    return _linear("cr_linear_int8tw", INT8TW, x, packed, scale, N, bias, out, workspace)
+
+
+def linear_w4a8(x, packed, s_channel, N, bias=None, out=None, workspace=None):
+    """y = asym W4A8 codebook linear; s_channel float32 [N]."""
+    return _linear("cr_linear_w4a8", W4A8, x, packed, s_channel, N, bias, out, workspace)
+
+
+# ---------------------------------------------------------------------------
+# Inspection hooks
+# ---------------------------------------------------------------------------
+
+def dbg_quant_act(kind: int, x: torch.Tensor):
+    """Activation codes int8 [M,K] and scales float32 [M] of the linear `kind`."""
+    _dev(x, "x", torch.bfloat16)
+    M, K = x.shape
+    codes = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    scales = torch.empty(max(M, 1), dtype=torch.float32, device=x.device)
+    _check(lib().cr_dbg_quant_act(kind, _ptr(x), M, K, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales[:M]
+
+
+def dbg_unpack_weight(kind: int, packed: torch.Tensor, N: int, K: int):
+    """Canonical int8 weight codes [N,K] held by a packed weight."""
+    _dev(packed, "packed", torch.uint8)
+    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _check(lib().cr_dbg_unpack_weight(kind, _ptr(packed), N, K, _ptr(codes), _stream()))
+    return codes
+
+
+def dbg_linear_acc(kind: int, x: torch.Tensor, packed: torch.Tensor, N: int, workspace=None):
+    """int32 accumulators [M,N] of the linear `kind`."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(packed, "packed", torch.uint8)
+    M, K = x.shape
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    need = max(workspace_bytes(kind, M, N, K), 256)
+    if workspace is None:
+        workspace = _empty_u8(need, x.device)
+    _check(lib().cr_dbg_linear_acc(kind, _ptr(x), M, K, _ptr(packed), N, _ptr(acc),
+                                   _ptr(workspace), workspace.numel(), _stream()))
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# Layer-level convenience
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PackedWeight:
+    """A packed weight and what its linear needs besides x."""
+    kind: int
+    N: int
+    K: int
+    packed: torch.Tensor
+    scale: torch.Tensor              # tensor scale (W4A4, int8tw) or s_channel (W4A8)
+    bias: Optional[torch.Tensor] = None
+
+
+def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None) -> PackedWeight:
+    """Pack a bf16 [N,K] weight: W4A4 ConvRot when K % 256 == 0, otherwise
+    int8_tensorwise ([REB] "Mixed formats where the kernel demands it")."""
+    N, K = w.shape
+    if K % 256 == 0:
+        p, s = pack_weight_w4(w)
+        return PackedWeight(W4A4, N, K, p, s, bias)
+    p, s = pack_weight_int8tw(w)
+    return PackedWeight(INT8TW, N, K, p, s, bias)
+
+
+def linear(x: torch.Tensor, pw: PackedWeight, out=None, workspace=None) -> torch.Tensor:
+    fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8}[pw.kind]
+    return fn(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace)

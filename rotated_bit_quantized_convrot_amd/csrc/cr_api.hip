@@ -1,0 +1,274 @@
+// C ABI of the ConvRot linear library: argument checks, workspace layout and
+// dispatch to the kernels.  Nothing here allocates device memory or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "convrot.h"
+#include "cr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+cr_status fail(cr_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+cr_status ok() {
+    g_err[0] = '\0';
+    return CR_OK;
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other.
+int g_dev_state[64];
+
+cr_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(CR_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 64 && g_dev_state[dev] == 1) return CR_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(CR_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_state[dev] = good ? 1 : 2;
+    if (!good) return fail(CR_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+    return CR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t a256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool rotated(int kind) { return kind == CR_W4A4 || kind == CR_W4A8; }
+
+cr_status check_kind(int kind) {
+    if (kind != CR_W4A4 && kind != CR_INT8TW && kind != CR_W4A8) return fail(CR_ERR_KIND, "unknown kind %d", kind);
+    return CR_OK;
+}
+
+cr_status check_nk(int kind, int N, int K) {
+    if (N < 1 || K < 1 || N > CR_MAX_DIM || K > CR_MAX_DIM)
+        return fail(CR_ERR_SHAPE, "bad shape N=%d K=%d (need 1..%d)", N, K, CR_MAX_DIM);
+    if (rotated(kind)) {
+        if (K % 256 != 0)
+            return fail(CR_ERR_GROUP, "K=%d is not a multiple of the 256-wide rotation group; "
+                        "use the int8_tensorwise format for this layer", K);
+        if (K > CR_MAX_ROT_K) return fail(CR_ERR_SHAPE, "K=%d exceeds %d for rotated formats", K, CR_MAX_ROT_K);
+    }
+    return CR_OK;
+}
+
+size_t packed_bytes(int kind, int N, int K) {
+    switch (kind) {
+        case CR_W4A4: return cr::w4_bytes(N, K);
+        case CR_INT8TW: return cr::i8_bytes(N, K);
+        case CR_W4A8: return cr::w4a8_bytes(N, K);
+        default: return 0;
+    }
+}
+
+int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K; }
+
+struct WsLayout {
+    size_t qx, sx, scratch, total;
+};
+
+WsLayout ws_layout(int kind, int M, int N, int K) {
+    WsLayout l{};
+    const int Kp = kp_of(kind, K);
+    l.qx = 0;
+    l.sx = a256((size_t)M * Kp);
+    l.scratch = l.sx + a256((size_t)M * 4);
+    l.total = l.scratch + cr::gemm_scratch_bytes(M, N, K);
+    if (l.total < 256) l.total = 256;
+    return l;
+}
+
+cr_status launch_err(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(CR_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared body of the three linears and the accumulator hook.
+cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, const float* wscale, int N,
+                     const void* bias, void* y, int32_t* acc, void* ws, size_t ws_bytes,
+                     hipStream_t st) {
+    cr_status s;
+    if ((s = check_kind(kind)) != CR_OK) return s;
+    if (M < 0 || M > CR_MAX_DIM) return fail(CR_ERR_SHAPE, "bad M=%d", M);
+    if ((s = check_nk(kind, N, K)) != CR_OK) return s;
+    if (wp == nullptr) return fail(CR_ERR_NULL, "packed weight is NULL");
+    if (acc == nullptr && wscale == nullptr) return fail(CR_ERR_NULL, "weight scale is NULL");
+    if (!aligned16(wp)) return fail(CR_ERR_ALIGN, "packed weight not 16-byte aligned");
+    if (bias != nullptr && !aligned16(bias)) return fail(CR_ERR_ALIGN, "bias not 16-byte aligned");
+    if (M == 0) return ok();
+    if (x == nullptr || ws == nullptr || (acc == nullptr && y == nullptr))
+        return fail(CR_ERR_NULL, "x, y or workspace is NULL");
+    if (!aligned16(x) || !aligned16(ws) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
+        return fail(CR_ERR_ALIGN, "x, y, accumulator or workspace not 16-byte aligned");
+    const WsLayout l = ws_layout(kind, M, N, K);
+    if (ws_bytes < l.total)
+        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    if ((s = check_device()) != CR_OK) return s;
+
+    char* w = static_cast<char*>(ws);
+    cr::GemmArgs a{};
+    a.kind = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
+    a.qx = reinterpret_cast<int8_t*>(w + l.qx);
+    a.sx = reinterpret_cast<float*>(w + l.sx);
+    a.M = M; a.N = N; a.K = K; a.Kp = kp_of(kind, K); a.Np = cr::round_up(N, 32);
+    a.wp = static_cast<const uint8_t*>(wp);
+    a.wscale = wscale;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.y = static_cast<uint16_t*>(y);
+    a.acc_out = acc;
+    a.scratch = w + l.scratch;
+    a.scratch_bytes = l.total - l.scratch;
+
+    hipError_t e = cr::launch_quant_act(a.kind, static_cast<const uint16_t*>(x), M, K, a.Kp,
+                                        const_cast<int8_t*>(a.qx), const_cast<float*>(a.sx),
+                                        cr::gemm_counters(a), cr::gemm_counter_count(M, N, K), st);
+    if (e != hipSuccess) return launch_err(e, "activation quantisation");
+    return launch_err(cr::launch_gemm(a, st), "integer GEMM");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cr_packed_bytes(int kind, int N, int K) {
+    if (check_kind(kind) != CR_OK || check_nk(kind, N, K) != CR_OK) return 0;
+    return packed_bytes(kind, N, K);
+}
+
+size_t cr_workspace_bytes(int kind, int M, int N, int K) {
+    if (check_kind(kind) != CR_OK || check_nk(kind, N, K) != CR_OK || M < 0 || M > CR_MAX_DIM) return 0;
+    return ws_layout(kind, M, N, K).total;
+}
+
+static cr_status pack_common_checks(int kind, const void* w, int N, int K, void* out, const void* scale) {
+    cr_status s;
+    if ((s = check_nk(kind, N, K)) != CR_OK) return s;
+    if (w == nullptr || out == nullptr || scale == nullptr) return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(w) || !aligned16(out)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    return check_device();
+}
+
+cr_status cr_pack_weight_w4(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
+                            hipStream_t stream) {
+    cr_status s = pack_common_checks(CR_W4A4, w_bf16, N, K, w_packed, w_scale);
+    if (s != CR_OK) return s;
+    return launch_err(cr::launch_pack_w4(static_cast<const uint16_t*>(w_bf16), N, K,
+                                         static_cast<uint8_t*>(w_packed), w_scale, stream),
+                      "W4 weight packing");
+}
+
+cr_status cr_pack_weight_int8tw(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
+                                hipStream_t stream) {
+    cr_status s = pack_common_checks(CR_INT8TW, w_bf16, N, K, w_packed, w_scale);
+    if (s != CR_OK) return s;
+    return launch_err(cr::launch_pack_i8(static_cast<const uint16_t*>(w_bf16), N, K,
+                                         static_cast<uint8_t*>(w_packed), w_scale, stream),
+                      "int8 weight packing");
+}
+
+cr_status cr_pack_weight_w4a8(const void* idx, const void* s_rel_e4m3, const float* codebook, int N,
+                              int K, void* w_packed, hipStream_t stream) {
+    cr_status s;
+    if ((s = check_nk(CR_W4A8, N, K)) != CR_OK) return s;
+    if (idx == nullptr || s_rel_e4m3 == nullptr || codebook == nullptr || w_packed == nullptr)
+        return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(idx) || !aligned16(s_rel_e4m3) || !aligned16(w_packed))
+        return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::launch_pack_w4a8(static_cast<const uint8_t*>(idx),
+                                           static_cast<const uint8_t*>(s_rel_e4m3), codebook, N, K,
+                                           static_cast<uint8_t*>(w_packed), stream),
+                      "W4A8 weight packing");
+}
+
+cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
+                         int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    return run_linear(CR_W4A4, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+cr_status cr_linear_int8tw(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
+                           int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    return run_linear(CR_INT8TW, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed, const float* s_channel,
+                         int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    return run_linear(CR_W4A8, x_bf16, M, K, w_packed, s_channel, N, bias_bf16, y_bf16, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+const char* cr_status_str(cr_status s) {
+    switch (s) {
+        case CR_OK: return "CR_OK";
+        case CR_ERR_NULL: return "CR_ERR_NULL";
+        case CR_ERR_SHAPE: return "CR_ERR_SHAPE";
+        case CR_ERR_GROUP: return "CR_ERR_GROUP";
+        case CR_ERR_ALIGN: return "CR_ERR_ALIGN";
+        case CR_ERR_WORKSPACE: return "CR_ERR_WORKSPACE";
+        case CR_ERR_DEVICE: return "CR_ERR_DEVICE";
+        case CR_ERR_LAUNCH: return "CR_ERR_LAUNCH";
+        case CR_ERR_KIND: return "CR_ERR_KIND";
+        default: return "CR_ERR_UNKNOWN";
+    }
+}
+
+const char* cr_last_error(void) { return g_err; }
+
+cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* codes, float* scales,
+                           hipStream_t stream) {
+    cr_status s;
+    if ((s = check_kind(kind)) != CR_OK) return s;
+    if (M < 0 || M > CR_MAX_DIM) return fail(CR_ERR_SHAPE, "bad M=%d", M);
+    if ((s = check_nk(kind, 1, K)) != CR_OK) return s;
+    if (M == 0) return ok();
+    if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(x_bf16) || !aligned16(codes)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    if ((s = check_device()) != CR_OK) return s;
+    const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
+    return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
+                                           static_cast<int8_t*>(codes), scales, nullptr, 0, stream),
+                      "activation quantisation");
+}
+
+cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K, void* codes,
+                               hipStream_t stream) {
+    cr_status s;
+    if ((s = check_kind(kind)) != CR_OK) return s;
+    if ((s = check_nk(kind, N, K)) != CR_OK) return s;
+    if (w_packed == nullptr || codes == nullptr) return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(w_packed)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    if ((s = check_device()) != CR_OK) return s;
+    const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
+    return launch_err(cr::launch_unpack_weight(wk, static_cast<const uint8_t*>(w_packed), N, K,
+                                               static_cast<int8_t*>(codes), stream),
+                      "weight unpacking");
+}
+
+cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K, const void* w_packed, int N,
+                            int32_t* acc, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (acc == nullptr && M > 0) return fail(CR_ERR_NULL, "accumulator output is NULL");
+    return run_linear(kind, x_bf16, M, K, w_packed, nullptr, N, nullptr, nullptr, acc, ws, ws_bytes,
+                      stream);
+}
+
+}  // extern "C"

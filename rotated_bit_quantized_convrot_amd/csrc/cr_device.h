@@ -1,0 +1,157 @@
+// Device helpers shared by the ConvRot kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+namespace cr {
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bf16, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Lane exchange v <- v[lane ^ MASK] inside each 32-lane half of the wave.
+//   MASK 1, 2 : DPP quad_perm;  MASK 8 : DPP row_ror:8 (a 16-lane row rotated
+//   by 8 is lane ^ 8);  MASK 4, 16 : ds_swizzle in bitmask mode (and 0x1F,
+//   xor MASK), which never leaves the 32-lane half.
+// ---------------------------------------------------------------------------
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float v) {
+    int x = __float_as_int(v);
+    int r;
+    if constexpr (MASK == 1) {
+        r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (MASK == 2) {
+        r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (MASK == 4) {
+        r = __builtin_amdgcn_ds_swizzle(x, 0x101F);                     // xor 4
+    } else if constexpr (MASK == 8) {
+        r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else {
+        static_assert(MASK == 16, "lane_xor mask");
+        r = __builtin_amdgcn_ds_swizzle(x, 0x401F);                     // xor 16
+    }
+    return __int_as_float(r);
+}
+
+// One butterfly stage across lanes: the pair (i, i+h) lives in lanes that
+// differ in bit MASK.  The lane holding i computes a+b, the lane holding i+h
+// computes a-b, with a the value at i and b the value at i+h.
+template <int MASK>
+__device__ __forceinline__ void fwht_cross(float (&v)[8], int lane32) {
+    const bool upper = (lane32 & MASK) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = lane_xor<MASK>(v[i]);
+        v[i] = upper ? (p - v[i]) : (v[i] + p);
+    }
+}
+
+// Rotation of one 256-block held by the 32 lanes of a half-wave, lane j
+// holding elements 8j..8j+7 in v[0..7]: strides 1, 2, 4 inside the lane,
+// then 8, 16, 32, 64, 128 across lanes (lane bits 0..4), then x 1/16.
+// All 32 lanes of the half-wave must be active.
+__device__ __forceinline__ void fwht256(float (&v)[8], int lane32) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+    fwht_cross<1>(v, lane32);
+    fwht_cross<2>(v, lane32);
+    fwht_cross<4>(v, lane32);
+    fwht_cross<8>(v, lane32);
+    fwht_cross<16>(v, lane32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.0625f;
+}
+
+// Symmetric code of v with scale s (IEEE division, round half to even).
+template <int LO, int HI>
+__device__ __forceinline__ int quant_code(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = fminf(fmaxf(r, (float)LO), (float)HI);
+    return (int)r;
+}
+
+// ---------------------------------------------------------------------------
+// Weight fragment producers.
+//
+// A packed 64-k chunk of one weight row is 32 bytes; the 16 bytes at 16*h
+// (h = lane / 32) hold, for MFMA step t = 0, 1, the dwords (t, d) at 8t + 4d.
+// Byte b of dword (t, d): low nibble k = 32t + 16h + 8d + b, high nibble
+// k = 32t + 16h + 8d + 4 + b.  So
+//    (P << 4) & 0xF0F0F0F0  = 16 * codes of k = .. + 8d + 0..3
+//    P & 0xF0F0F0F0         = 16 * codes of k = .. + 8d + 4..7
+// and the four dwords {lo(P0), hi(P0), lo(P1), hi(P1)} are the 16 int8
+// operands of the step in natural k order, each scaled by 16 (exact).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
+    v4i r;
+    r.x = (int)((p0 << 4) & 0xF0F0F0F0u);
+    r.y = (int)(p0 & 0xF0F0F0F0u);
+    r.z = (int)((p1 << 4) & 0xF0F0F0F0u);
+    r.w = (int)(p1 & 0xF0F0F0F0u);
+    return r;
+}
+
+// Four codebook indices (one per byte, 0..15, in `sel`) looked up in a
+// 16-byte table row t0..t3: v_perm picks from the low and the high 8 entries
+// with the index's low 3 bits, a third v_perm picks between them by bit 3.
+__device__ __forceinline__ uint32_t lut16(uint32_t sel, uint32_t t0, uint32_t t1,
+                                          uint32_t t2, uint32_t t3) {
+    const uint32_t s7 = sel & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(t1, t0, s7);
+    const uint32_t hi = __builtin_amdgcn_perm(t3, t2, s7);
+    const uint32_t pick = ((sel >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, pick);
+}
+
+// W4A8: decode the 16 operands of one step from two packed index dwords
+// (same nibble order as above) and the table row of the group's scale code.
+__device__ __forceinline__ v4i decode_w4a8(uint32_t p0, uint32_t p1, uint4 trow) {
+    v4i r;
+    r.x = (int)lut16(p0 & 0x0F0F0F0Fu, trow.x, trow.y, trow.z, trow.w);
+    r.y = (int)lut16((p0 >> 4) & 0x0F0F0F0Fu, trow.x, trow.y, trow.z, trow.w);
+    r.z = (int)lut16(p1 & 0x0F0F0F0Fu, trow.x, trow.y, trow.z, trow.w);
+    r.w = (int)lut16((p1 >> 4) & 0x0F0F0F0Fu, trow.x, trow.y, trow.z, trow.w);
+    return r;
+}
+
+__device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// E4M3FN byte -> float (sign, 4-bit exponent with bias 7, 3-bit mantissa,
+// exponent 0 subnormal, S.1111.111 NaN).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) return __int_as_float(0x7FC00000);
+    if (e == 0u) v = (float)m * 0.001953125f;                 // m/8 * 2^-6 (exact)
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // 2^(e-7) * (1 + m/8)
+    return (c & 0x80u) ? -v : v;
+}
+
+}  // namespace cr

@@ -1,0 +1,75 @@
+// Internal launch interface of the ConvRot library (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cr {
+
+enum WKind { WK_W4 = 0, WK_I8 = 1, WK_W4A8 = 2 };
+
+// Packed-weight geometry.
+//   Np = N rounded up to 32 (rows past N are zero), Kp = K rounded up to 64.
+//   W4 / W4A8 indices: 1 KiB tiles (32 rows x 64 k), tile (nb, kc) at
+//     (nb * Kp/64 + kc) * 1024; row r at r*32; the 16 bytes at 16h hold
+//     k = 32t + 16h + 8d + {0..3 low nibbles, 4..7 high nibbles} of byte
+//     8t + 4d + b.
+//   int8: 2 KiB tiles, row r at r*64, byte 32h + 16t + p holds k = 32t + 16h + p.
+//   W4A8 extra: scale codes, 128-byte tiles, row r at r*4, byte 2t + h is the
+//     code of group (64kc + 32t + 16h)/16; then the 4 KiB decode table
+//     T[c*16 + i] = clamp(rint(codebook[i] * e4m3(c)), -127, 127).
+__host__ __device__ inline int round_up(int v, int a) { return (v + a - 1) / a * a; }
+__host__ __device__ inline size_t w4_bytes(int N, int K) { return (size_t)round_up(N, 32) * (size_t)K / 2; }
+__host__ __device__ inline size_t i8_bytes(int N, int K) { return (size_t)round_up(N, 32) * (size_t)round_up(K, 64); }
+__host__ __device__ inline size_t w4a8_codes_offset(int N, int K) { return w4_bytes(N, K); }
+__host__ __device__ inline size_t w4a8_table_offset(int N, int K) {
+    return w4_bytes(N, K) + (size_t)round_up(N, 32) * (size_t)K / 16;
+}
+__host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_offset(N, K) + 4096; }
+
+// Activation quantisation: codes int8 [M, Kp] (row-major, zero for k >= K)
+// and scales [M].  zero_u32 / zero_count: a region the kernel clears for the
+// GEMM's split-K counters (may be null).
+hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
+                            float* sx, uint32_t* zero_u32, int zero_count, hipStream_t st);
+
+hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                          hipStream_t st);
+hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                          hipStream_t st);
+hipError_t launch_pack_w4a8(const uint8_t* idx, const uint8_t* s_rel, const float* cb, int N,
+                            int K, uint8_t* out, hipStream_t st);
+hipError_t launch_unpack_weight(int kind, const uint8_t* packed, int N, int K, int8_t* out,
+                                hipStream_t st);
+
+struct GemmArgs {
+    int kind;              // WKind
+    const int8_t* qx;      // [M, Kp]
+    const float* sx;       // [M]
+    int M, N, K, Kp, Np;
+    const uint8_t* wp;     // packed weight
+    const float* wscale;   // tensor scale (1 float) or s_channel [N] (W4A8)
+    const uint16_t* bias;  // [N] or null
+    uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
+    int32_t* acc_out;      // [M, N] int32 accumulators instead of y
+    void* scratch;         // split-K partials and counters
+    size_t scratch_bytes;
+};
+
+// Split-K plan of the small-M path; scratch bytes it needs.
+struct SkinnyPlan {
+    bool use;
+    int mf;        // 32-row activation fragments (1..4)
+    int nblk;      // 128-row weight blocks
+    int splits;    // K splits
+    size_t part_bytes;     // int32 partials [splits][M][Np]
+    size_t counter_bytes;  // one uint32 per weight block
+};
+SkinnyPlan plan_skinny(int M, int N, int K);
+size_t gemm_scratch_bytes(int M, int N, int K);
+int gemm_counter_count(int M, int N, int K);
+uint32_t* gemm_counters(const GemmArgs& a);
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace cr

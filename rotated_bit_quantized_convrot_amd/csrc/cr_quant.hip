@@ -1,0 +1,428 @@
+// Activation quantisation and offline weight packing kernels.
+//
+// Rotation + per-row dynamic quantisation of activations, tensorwise weight
+// quantisation and packing ([QIE] model card intro: group-256 Hadamard
+// ConvRot, activations rotated online and quantised to INT4 in the kernel,
+// weights packed signed INT4 two per byte; [REB] "What's inside a file" for
+// the W4A8 tensors).
+#include "cr_device.h"
+#include "cr_internal.h"
+
+namespace cr {
+
+// ---------------------------------------------------------------------------
+// Rows rotated group by group.  One block per row; half-wave h handles groups
+// h, h + NHW, ... (at most GPL of them), each lane 8 consecutive values.
+// ---------------------------------------------------------------------------
+template <int GPL>
+struct RotRow {
+    float v[GPL][8];
+
+    // Loads and rotates the row's groups; returns this lane's absmax.
+    __device__ __forceinline__ float load_rotate(const uint16_t* __restrict__ row, int G, int hw,
+                                                 int nhw, int lane32) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GPL; ++i) {
+            const int g = hw + i * nhw;
+            if (g < G) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(row + (size_t)g * 256 + lane32 * 8);
+                v[i][0] = bf16_lo(raw.x); v[i][1] = bf16_hi(raw.x);
+                v[i][2] = bf16_lo(raw.y); v[i][3] = bf16_hi(raw.y);
+                v[i][4] = bf16_lo(raw.z); v[i][5] = bf16_hi(raw.z);
+                v[i][6] = bf16_lo(raw.w); v[i][7] = bf16_hi(raw.w);
+                fwht256(v[i], lane32);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+            }
+        }
+        return amax;
+    }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Max over the block (blockDim.x <= 1024); every thread gets the result.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const int nw = (blockDim.x + 63) >> 6;
+    float r = 0.0f;
+    for (int i = 0; i < nw; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Rotated activations: codes [M, K] int8 (natural order) and scales [M].
+template <int GPL, int QMAX, int LO, int HI>
+__global__ void __launch_bounds__(512) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
+                                                       int8_t* __restrict__ qx,
+                                                       float* __restrict__ sx,
+                                                       uint32_t* __restrict__ zero_u32,
+                                                       int zero_count) {
+    __shared__ float red[16];
+    const int m = blockIdx.x;
+    if (zero_u32 != nullptr && m == 0) {
+        for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_u32[i] = 0u;
+    }
+    const int G = K >> 8;
+    const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
+    RotRow<GPL> r;
+    const float amax = block_max(r.load_rotate(x + (size_t)m * K, G, hw, nhw, lane32), red);
+    const float s = amax / (float)QMAX;
+    if (threadIdx.x == 0) sx[m] = s;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = hw + i * nhw;
+        if (g < G) {
+            int q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quant_code<LO, HI>(r.v[i][j], s);
+            uint2 o;
+            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+            *reinterpret_cast<uint2*>(qx + (size_t)m * K + (size_t)g * 256 + lane32 * 8) = o;
+        }
+    }
+}
+
+// Unrotated activations (int8_tensorwise): any K; codes [M, Kp] with zeros
+// in [K, Kp).  Two passes over the row (the second one hits the cache).
+__global__ void __launch_bounds__(256) k_quant_act_plain(const uint16_t* __restrict__ x, int M,
+                                                         int K, int Kp, int8_t* __restrict__ qx,
+                                                         float* __restrict__ sx,
+                                                         uint32_t* __restrict__ zero_u32,
+                                                         int zero_count) {
+    __shared__ float red[16];
+    const int m = blockIdx.x;
+    if (zero_u32 != nullptr && m == 0) {
+        for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_u32[i] = 0u;
+    }
+    const uint16_t* row = x + (size_t)m * K;
+    int8_t* out = qx + (size_t)m * Kp;
+    const bool vec = (K % 8) == 0;
+    float amax = 0.0f;
+    if (vec) {
+        for (int k = threadIdx.x * 8; k < K; k += blockDim.x * 8) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(row + k);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(raw.x)), fabsf(bf16_hi(raw.x))),
+                                     fmaxf(fabsf(bf16_lo(raw.y)), fabsf(bf16_hi(raw.y)))));
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(raw.z)), fabsf(bf16_hi(raw.z))),
+                                     fmaxf(fabsf(bf16_lo(raw.w)), fabsf(bf16_hi(raw.w)))));
+        }
+    } else {
+        for (int k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(bf16_to_f32(row[k])));
+    }
+    amax = block_max(amax, red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) sx[m] = s;
+    if (vec) {
+        for (int k = threadIdx.x * 8; k < K; k += blockDim.x * 8) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(row + k);
+            uint2 o;
+            o.x = pack4_i8(quant_code<-128, 127>(bf16_lo(raw.x), s), quant_code<-128, 127>(bf16_hi(raw.x), s),
+                           quant_code<-128, 127>(bf16_lo(raw.y), s), quant_code<-128, 127>(bf16_hi(raw.y), s));
+            o.y = pack4_i8(quant_code<-128, 127>(bf16_lo(raw.z), s), quant_code<-128, 127>(bf16_hi(raw.z), s),
+                           quant_code<-128, 127>(bf16_lo(raw.w), s), quant_code<-128, 127>(bf16_hi(raw.w), s));
+            *reinterpret_cast<uint2*>(out + k) = o;
+        }
+    } else {
+        for (int k = threadIdx.x; k < K; k += blockDim.x)
+            out[k] = (int8_t)quant_code<-128, 127>(bf16_to_f32(row[k]), s);
+    }
+    for (int k = K + threadIdx.x; k < Kp; k += blockDim.x) out[k] = 0;
+}
+
+static int rot_threads(int G, int* gpl) {
+    int nhw = G < 16 ? G : 16;
+    int per = (G + nhw - 1) / nhw;
+    int g = 1;
+    while (g < per) g <<= 1;
+    *gpl = g;
+    int threads = nhw * 32;
+    if (threads < 64) threads = 64;
+    return threads;
+}
+
+template <int QMAX, int LO, int HI>
+static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, uint32_t* z,
+                             int zc, hipStream_t st) {
+    int gpl = 1;
+    const int threads = rot_threads(K >> 8, &gpl);
+    dim3 grid(M), block(threads);
+    switch (gpl) {
+        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        case 8: k_quant_act_rot<8, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        case 16: k_quant_act_rot<16, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
+                            float* sx, uint32_t* zero_u32, int zero_count, hipStream_t st) {
+    if (kind == WK_W4) return launch_rot<7, -8, 7>(x, M, K, qx, sx, zero_u32, zero_count, st);
+    if (kind == WK_W4A8) return launch_rot<127, -128, 127>(x, M, K, qx, sx, zero_u32, zero_count, st);
+    k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx, zero_u32, zero_count);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing (offline).  The tensor absmax is accumulated with atomicMax
+// on the float bit pattern (valid for non-negative floats) in the scale slot,
+// which is then read as the absmax and finally replaced by absmax / Q.
+// ---------------------------------------------------------------------------
+__global__ void k_set_zero(uint32_t* p) { *p = 0u; }
+
+__global__ void k_finalize_scale(float* p, float q) { p[0] = p[0] / q; }
+
+template <int GPL>
+__global__ void __launch_bounds__(512) k_absmax_rot_rows(const uint16_t* __restrict__ w, int K,
+                                                         uint32_t* __restrict__ amax_bits) {
+    __shared__ float red[16];
+    const int n = blockIdx.x;
+    const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
+    RotRow<GPL> r;
+    const float a = block_max(r.load_rotate(w + (size_t)n * K, K >> 8, hw, nhw, lane32), red);
+    if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(a));
+}
+
+// One dword of the W4 layout from 8 codes of k0..k0+7 (k0 % 8 == 0):
+// byte b = code(k0+b) | code(k0+4+b) << 4.
+__device__ __forceinline__ uint32_t w4_dword(const int (&q)[8]) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o |= ((uint32_t)(q[b] & 0xF) | ((uint32_t)(q[b + 4] & 0xF) << 4)) << (8 * b);
+    return o;
+}
+
+// Byte offset of the W4 dword holding k0..k0+7 of row n.
+__device__ __forceinline__ size_t w4_dword_offset(int n, int k0, int K) {
+    const int nb = n >> 5, r = n & 31, kc = k0 >> 6, kk = k0 & 63;
+    const int t = kk >> 5, h = (kk >> 4) & 1, d = (kk >> 3) & 1;
+    return ((size_t)nb * (K >> 6) + kc) * 1024 + r * 32 + 16 * h + 8 * t + 4 * d;
+}
+
+template <int GPL>
+__global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w, int N, int K,
+                                                 const float* __restrict__ amax_slot,
+                                                 uint8_t* __restrict__ out) {
+    const int n = blockIdx.x;
+    const int G = K >> 8;
+    const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
+    if (n >= N) {  // padding rows
+        for (int i = 0; i < GPL; ++i) {
+            const int g = hw + i * nhw;
+            if (g < G) *reinterpret_cast<uint32_t*>(out + w4_dword_offset(n, g * 256 + lane32 * 8, K)) = 0u;
+        }
+        return;
+    }
+    const float s = amax_slot[0] / 7.0f;
+    RotRow<GPL> r;
+    r.load_rotate(w + (size_t)n * K, G, hw, nhw, lane32);
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = hw + i * nhw;
+        if (g < G) {
+            int q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quant_code<-8, 7>(r.v[i][j], s);
+            *reinterpret_cast<uint32_t*>(out + w4_dword_offset(n, g * 256 + lane32 * 8, K)) = w4_dword(q);
+        }
+    }
+}
+
+hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                          hipStream_t st) {
+    const int Np = round_up(N, 32);
+    int gpl = 1;
+    const int threads = rot_threads(K >> 8, &gpl);
+    uint32_t* bits = reinterpret_cast<uint32_t*>(scale);
+    k_set_zero<<<1, 1, 0, st>>>(bits);
+    switch (gpl) {
+#define CR_PACK_CASE(G_)                                                                 \
+    case G_:                                                                             \
+        k_absmax_rot_rows<G_><<<dim3(N), dim3(threads), 0, st>>>(w, K, bits);            \
+        k_pack_w4<G_><<<dim3(Np), dim3(threads), 0, st>>>(w, N, K, scale, out);          \
+        break;
+        CR_PACK_CASE(1) CR_PACK_CASE(2) CR_PACK_CASE(4) CR_PACK_CASE(8) CR_PACK_CASE(16)
+#undef CR_PACK_CASE
+        default: return hipErrorInvalidValue;
+    }
+    k_finalize_scale<<<1, 1, 0, st>>>(scale, 7.0f);
+    return hipGetLastError();
+}
+
+// --- int8_tensorwise ------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_absmax_plain(const uint16_t* __restrict__ w, size_t count,
+                                                      uint32_t* __restrict__ amax_bits) {
+    __shared__ float red[16];
+    float a = 0.0f;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (size_t)gridDim.x * blockDim.x)
+        a = fmaxf(a, fabsf(bf16_to_f32(w[i])));
+    a = block_max(a, red);
+    if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(a));
+}
+
+// One thread per 16-byte segment (row n, 64-chunk kc, half h, step t).
+__global__ void __launch_bounds__(256) k_pack_i8(const uint16_t* __restrict__ w, int N, int K,
+                                                 int Kp, const float* __restrict__ amax_slot,
+                                                 uint8_t* __restrict__ out, size_t nseg) {
+    const size_t seg = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (seg >= nseg) return;
+    const float s = amax_slot[0] / 127.0f;
+    const size_t tile = seg >> 7;            // 128 segments of 16 B per 2 KiB tile
+    const int within = (int)(seg & 127);
+    const int r = within >> 2, h = (within >> 1) & 1, t = within & 1;
+    const int nkc = Kp >> 6;
+    const int nb = (int)(tile / nkc), kc = (int)(tile % nkc);
+    const int n = nb * 32 + r;
+    const int k0 = kc * 64 + 32 * t + 16 * h;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (n < N) {
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int k = k0 + p;
+            const int q = (k < K) ? quant_code<-128, 127>(bf16_to_f32(w[(size_t)n * K + k]), s) : 0;
+            o[p >> 2] |= (uint32_t)(q & 0xFF) << (8 * (p & 3));
+        }
+    }
+    *reinterpret_cast<uint4*>(out + tile * 2048 + r * 64 + 32 * h + 16 * t) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                          hipStream_t st) {
+    const int Np = round_up(N, 32), Kp = round_up(K, 64);
+    uint32_t* bits = reinterpret_cast<uint32_t*>(scale);
+    k_set_zero<<<1, 1, 0, st>>>(bits);
+    const size_t count = (size_t)N * K;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    k_absmax_plain<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, count, bits);
+    const size_t nseg = (size_t)Np * Kp / 16;
+    k_pack_i8<<<dim3((unsigned)((nseg + 255) / 256)), dim3(256), 0, st>>>(w, N, K, Kp, scale, out, nseg);
+    k_finalize_scale<<<1, 1, 0, st>>>(scale, 127.0f);
+    return hipGetLastError();
+}
+
+// --- W4A8 -----------------------------------------------------------------
+
+// One thread per W4-layout dword: re-orders the canonical index nibbles
+// (low nibble = even k) of k0..k0+7 into the GEMM's nibble order.
+__global__ void __launch_bounds__(256) k_pack_w4a8_idx(const uint8_t* __restrict__ idx, int N,
+                                                       int K, uint8_t* __restrict__ out,
+                                                       size_t ndw) {
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= ndw) return;
+    const size_t tile = id >> 8;
+    const int within = (int)(id & 255);
+    const int r = within >> 3, rem = within & 7;
+    const int h = rem >> 2, t = (rem >> 1) & 1, d = rem & 1;
+    const int nkc = K >> 6;
+    const int nb = (int)(tile / nkc), kc = (int)(tile % nkc);
+    const int n = nb * 32 + r;
+    const int k0 = kc * 64 + 32 * t + 16 * h + 8 * d;
+    uint32_t o = 0u;
+    if (n < N) {
+        const uint32_t c = *reinterpret_cast<const uint32_t*>(idx + (size_t)n * (K / 2) + k0 / 2);
+        int nib[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) nib[j] = (c >> (4 * j)) & 0xF;   // nibble j = k0 + j
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o |= ((uint32_t)nib[b] | ((uint32_t)nib[b + 4] << 4)) << (8 * b);
+    }
+    *reinterpret_cast<uint32_t*>(out + tile * 1024 + r * 32 + 16 * h + 8 * t + 4 * d) = o;
+}
+
+// One thread per (row, 64-chunk): the four group codes, natural group order.
+__global__ void __launch_bounds__(256) k_pack_w4a8_codes(const uint8_t* __restrict__ s_rel, int N,
+                                                         int K, uint8_t* __restrict__ out,
+                                                         size_t nitems) {
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= nitems) return;
+    const int nkc = K >> 6;
+    const size_t tile = id >> 5;
+    const int r = (int)(id & 31);
+    const int nb = (int)(tile / nkc), kc = (int)(tile % nkc);
+    const int n = nb * 32 + r;
+    uint32_t c = 0u;
+    if (n < N) c = *reinterpret_cast<const uint32_t*>(s_rel + (size_t)n * (K / 16) + kc * 4);
+    *reinterpret_cast<uint32_t*>(out + tile * 128 + r * 4) = c;
+}
+
+__global__ void __launch_bounds__(256) k_w4a8_table(const float* __restrict__ cb,
+                                                    int8_t* __restrict__ table) {
+    const int id = blockIdx.x * blockDim.x + threadIdx.x;   // 4096 entries
+    const int c = id >> 4, i = id & 15;
+    const float v = cb[i] * e4m3_decode((uint32_t)c);
+    int q = 0;
+    if (!__builtin_isnan(v)) q = (int)fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+    table[id] = (int8_t)q;
+}
+
+hipError_t launch_pack_w4a8(const uint8_t* idx, const uint8_t* s_rel, const float* cb, int N,
+                            int K, uint8_t* out, hipStream_t st) {
+    const int Np = round_up(N, 32);
+    const size_t ndw = (size_t)Np * K / 8;
+    k_pack_w4a8_idx<<<dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, st>>>(idx, N, K, out, ndw);
+    const size_t nitems = (size_t)Np * (K / 64);
+    k_pack_w4a8_codes<<<dim3((unsigned)((nitems + 255) / 256)), dim3(256), 0, st>>>(
+        s_rel, N, K, out + w4a8_codes_offset(N, K), nitems);
+    k_w4a8_table<<<dim3(16), dim3(256), 0, st>>>(cb, reinterpret_cast<int8_t*>(out + w4a8_table_offset(N, K)));
+    return hipGetLastError();
+}
+
+// --- canonical weight codes (inspection) ---------------------------------
+
+__global__ void __launch_bounds__(256) k_unpack_weight(int kind, const uint8_t* __restrict__ p, int N,
+                                                       int K, int Kp, size_t codes_off,
+                                                       size_t table_off, int8_t* __restrict__ out) {
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= (size_t)N * K) return;
+    const int n = (int)(id / K), k = (int)(id % K);
+    const int nb = n >> 5, r = n & 31, kc = k >> 6, kk = k & 63;
+    const int t = kk >> 5, h = (kk >> 4) & 1, pp = kk & 15;
+    const size_t tile = (size_t)nb * (Kp >> 6) + kc;
+    int v;
+    if (kind == WK_I8) {
+        v = (int8_t)p[tile * 2048 + r * 64 + 32 * h + 16 * t + pp];
+    } else {
+        const int d = pp >> 3, b = pp & 3, hi = (pp >> 2) & 1;
+        const uint8_t byte = p[tile * 1024 + r * 32 + 16 * h + 8 * t + 4 * d + b];
+        const int nib = hi ? (byte >> 4) : (byte & 0xF);
+        if (kind == WK_W4) {
+            v = nib >= 8 ? nib - 16 : nib;
+        } else {
+            const uint8_t code = p[codes_off + tile * 128 + r * 4 + 2 * t + h];
+            v = (int8_t)p[table_off + (size_t)code * 16 + nib];
+        }
+    }
+    out[id] = (int8_t)v;
+}
+
+hipError_t launch_unpack_weight(int kind, const uint8_t* packed, int N, int K, int8_t* out,
+                                hipStream_t st) {
+    const size_t count = (size_t)N * K;
+    const int Kp = round_up(K, 64);
+    size_t co = 0, to = 0;
+    if (kind == WK_W4A8) { co = w4a8_codes_offset(N, K); to = w4a8_table_offset(N, K); }
+    k_unpack_weight<<<dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st>>>(kind, packed, N, K, Kp, co, to, out);
+    return hipGetLastError();
+}
+
+}  // namespace cr

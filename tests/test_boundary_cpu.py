@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments before any launch (no GPU needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+LIBPATH = os.path.join(ROOT, "rotated_bit_quantized_convrot_amd", "libconvrot.so")
+
+CR = dict(OK=0, NULL=1, SHAPE=2, GROUP=3, ALIGN=4, WORKSPACE=5, DEVICE=6, LAUNCH=7, KIND=8)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cr_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBPATH):
+        pytest.fail("libconvrot.so is not built (run __graft_entry__.build())")
+    import rotated_bit_quantized_convrot_amd as crp
+    return crp.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("cr_pack_weight_w4", "cr_linear_w4a4", "cr_linear_int8tw", "cr_linear_w4a8"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    import rotated_bit_quantized_convrot_amd as crp
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(crp.EXPORTS) == _declared()
+
+
+def test_sizes(L):
+    # W4A4: N rounded to 32 rows, two codes per byte
+    assert L.cr_packed_bytes(0, 12288, 3072) == 12288 * 3072 // 2
+    assert L.cr_packed_bytes(0, 100, 512) == 128 * 256
+    # int8tw: rows to 32, K to 64
+    assert L.cr_packed_bytes(1, 2688, 2688) == 2688 * 2688
+    assert L.cr_packed_bytes(1, 7, 100) == 32 * 128
+    # W4A8: codes + one e4m3 byte per 16 + 4 KiB table (0.5625 B/param + table)
+    assert L.cr_packed_bytes(2, 10240, 3840) == 10240 * 3840 // 2 + 10240 * 3840 // 16 + 4096
+    # bad shapes / group
+    assert L.cr_packed_bytes(0, 256, 2688) == 0
+    assert L.cr_packed_bytes(0, 0, 256) == 0
+    assert L.cr_packed_bytes(7, 256, 256) == 0
+    assert L.cr_workspace_bytes(0, 76, 9728, 2560) >= 76 * 2560 + 76 * 4
+    assert L.cr_workspace_bytes(1, -1, 16, 16) == 0
+
+
+def _err(L):
+    return L.cr_last_error().decode()
+
+
+def test_group_error_is_clear(L):
+    vp = ctypes.c_void_p(16)  # never dereferenced: rejected before launch
+    st = L.cr_linear_w4a4(vp, 8, 2688, vp, vp, 2688, None, vp, vp, 1 << 20, None)
+    assert st == CR["GROUP"]
+    assert "2688" in _err(L) and "int8_tensorwise" in _err(L)
+    assert L.cr_linear_w4a8(vp, 8, 300, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]
+    assert L.cr_pack_weight_w4(vp, 64, 2688, vp, vp, None) == CR["GROUP"]
+    assert L.cr_status_str(CR["GROUP"]) == b"CR_ERR_GROUP"
+
+
+def test_argument_errors(L):
+    vp = ctypes.c_void_p(16)
+    odd = ctypes.c_void_p(24)
+    assert L.cr_linear_int8tw(vp, -1, 64, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["SHAPE"]
+    assert L.cr_linear_int8tw(vp, 4, 64, None, vp, 64, None, vp, vp, 1 << 20, None) == CR["NULL"]
+    assert L.cr_linear_int8tw(vp, 4, 64, vp, None, 64, None, vp, vp, 1 << 20, None) == CR["NULL"]
+    assert L.cr_linear_int8tw(vp, 4, 64, vp, vp, 64, None, None, vp, 1 << 20, None) == CR["NULL"]
+    assert L.cr_linear_int8tw(odd, 4, 64, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["ALIGN"]
+    assert L.cr_linear_int8tw(vp, 4, 64, vp, vp, 64, odd, vp, vp, 1 << 20, None) == CR["ALIGN"]
+    assert L.cr_linear_int8tw(vp, 4, 64, vp, vp, 64, None, vp, vp, 16, None) == CR["WORKSPACE"]
+    assert L.cr_dbg_quant_act(9, vp, 4, 256, vp, vp, None) == CR["KIND"]
+    assert L.cr_linear_w4a4(vp, 4, 1 << 21, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["SHAPE"]
+
+
+def test_m_zero_is_a_noop(L):
+    vp = ctypes.c_void_p(16)
+    assert L.cr_linear_w4a4(None, 0, 256, vp, vp, 64, None, None, None, 0, None) == CR["OK"]
+    assert L.cr_linear_int8tw(None, 0, 100, vp, vp, 64, None, None, None, 0, None) == CR["OK"]
+
+
+def test_no_device_is_reported_not_faked(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    vp = ctypes.c_void_p(16)
+    need = L.cr_workspace_bytes(0, 4, 64, 256)
+    st = L.cr_linear_w4a4(vp, 4, 256, vp, vp, 64, None, vp, vp, need, None)
+    assert st == CR["DEVICE"]
+
+
+def test_binding_fails_loudly_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    import rotated_bit_quantized_convrot_amd as crp
+    with pytest.raises((ValueError, RuntimeError)):
+        crp.pack_weight_w4(torch.zeros(64, 256, dtype=torch.bfloat16))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "rotated_bit_quantized_convrot_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("the oracle", ""), f

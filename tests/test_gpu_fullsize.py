@@ -1,0 +1,103 @@
+"""Full-size parity for every workload, in the launch configuration the
+benchmark times: the GPU computes the whole layer, the oracle recomputes a
+sample of rows (rows are independent given the weight), compared bit-exact on
+the int32 accumulators and within 1e-2 on the bf16 outputs."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from oracle import convrot_oracle as O
+from tests._util import TOL, bf16_dev_to_f32, max_rel_err, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def crp():
+    import rotated_bit_quantized_convrot_amd as m
+    m.lib()
+    return m
+
+
+def _rows(M, n=24, seed=0):
+    if M <= 96:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, M // 2, M - 2, M - 1]
+    rest = rng.choice(np.setdiff1d(np.arange(M), fixed), n - len(fixed), replace=False)
+    return np.sort(np.concatenate([fixed, rest]))
+
+
+def _check(y, acc, rows, ref_acc, ref_y):
+    idx = torch.from_numpy(rows).cuda()
+    a = acc.index_select(0, idx).cpu().numpy()
+    assert np.array_equal(a, ref_acc)
+    yd = bf16_dev_to_f32(y.index_select(0, idx))
+    assert max_rel_err(yd, ref_y) <= TOL
+
+
+W4A4_LAYERS = {
+    "dit_w1": lambda: si.dit_w1(),
+    "dit_w2": lambda: si.dit_w2(),
+    "te_gate_up_M76": lambda: si.te_gate_up(76),
+    "te_down_M76": lambda: si.te_down(76),
+    "te_gate_up_M1220": lambda: si.te_gate_up(1220),
+    "te_down_M1220": lambda: si.te_down(1220),
+}
+
+
+@pytest.mark.parametrize("name", list(W4A4_LAYERS))
+def test_w4a4_full_size(crp, name):
+    print(f"[fullsize] {name}", flush=True)
+    L = W4A4_LAYERS[name]()
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    bias = to_dev_bf16(L.bias) if L.bias is not None else None
+    ws = torch.empty(crp.workspace_bytes(0, L.M, L.N, L.K), dtype=torch.uint8, device="cuda")
+    y = crp.linear_w4a4(x, p, s, L.N, bias, workspace=ws)
+    acc = crp.dbg_linear_acc(0, x, p, L.N, workspace=ws)
+    torch.cuda.synchronize()
+    rows = _rows(L.M)
+    qw, sw = O.quant_weight_w4(L.w)
+    assert s.cpu().numpy()[:1].view(np.uint32)[0] == np.float32(sw).view(np.uint32)
+    qx, sx = O.quant_act_w4a4(L.x[rows])
+    ref_acc = O.int_gemm(qx, qw)
+    _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, sw, L.bias))
+
+
+INT8_LAYERS = {"int8tw_vo": lambda: si.int8tw_vo(), "int8tw_k2688": lambda: si.int8tw_k2688()}
+
+
+@pytest.mark.parametrize("name", list(INT8_LAYERS))
+def test_int8tw_full_size(crp, name):
+    print(f"[fullsize] {name}", flush=True)
+    L = INT8_LAYERS[name]()
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_int8tw(to_dev_bf16(L.w))
+    y = crp.linear_int8tw(x, p, s, L.N)
+    acc = crp.dbg_linear_acc(1, x, p, L.N)
+    torch.cuda.synchronize()
+    rows = _rows(L.M)
+    qw, sw = O.quant_weight_int8tw(L.w)
+    qx, sx = O.quant_act_int8(L.x[rows])
+    ref_acc = O.int_gemm(qx, qw)
+    _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, sw, None))
+
+
+def test_w4a8_full_size(crp):
+    print("[fullsize] w4a8", flush=True)
+    L = si.w4a8_layer()
+    enc = O.w4a8_encode(L.w)
+    x = to_dev_bf16(L.x)
+    p = crp.pack_weight_w4a8(to_dev(enc["idx_packed"]), to_dev(enc["s_rel"]),
+                             to_dev(enc["codebook"]), L.N, L.K)
+    sch = to_dev(enc["s_channel"])
+    y = crp.linear_w4a8(x, p, sch, L.N)
+    acc = crp.dbg_linear_acc(2, x, p, L.N)
+    torch.cuda.synchronize()
+    rows = _rows(L.M)
+    w8 = O.w4a8_decode(enc["idx"], enc["s_rel"], enc["codebook"])
+    qx, sx = O.quant_act_w4a8(L.x[rows])
+    ref_acc = O.int_gemm(qx, w8)
+    _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, enc["s_channel"], None))

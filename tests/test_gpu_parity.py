@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: activation codes and scales, weight codes and scales, int32
+accumulators.  bf16 outputs: within max relative error 1e-2 of the oracle's
+float32 epilogue (they are expected to equal its bf16 rounding)."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from oracle import convrot_oracle as O
+from tests._util import TOL, bf16_dev_to_f32, max_rel_err, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def crp():
+    import rotated_bit_quantized_convrot_amd as m
+    m.lib()
+    return m
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+KIND_ORACLE_ACT = {
+    0: O.quant_act_w4a4,
+    1: O.quant_act_int8,
+    2: O.quant_act_w4a8,
+}
+
+
+# ---------------------------------------------------------------------------
+# Activation quantisation
+# ---------------------------------------------------------------------------
+
+ACT_CASES = [
+    (0, 64, 512), (0, 76, 2560), (0, 33, 9728), (0, 3, 256), (0, 5, 12288), (0, 2, 65536),
+    (1, 64, 2688), (1, 9, 100), (1, 17, 3072), (1, 1, 7),
+    (2, 40, 3840), (2, 3, 256),
+]
+
+
+@pytest.mark.parametrize("kind,M,K", ACT_CASES)
+def test_quant_act_bitexact(crp, kind, M, K):
+    L = si.random_layer(M, K, 1, seed=100 + M + K, outlier_count=min(8, K), outlier_scale=40.0)
+    x = L.x.copy()
+    if M >= 3:
+        x[1, :] = 0                                  # zero row
+        x[2, :] = si.f32_to_bf16_bits(np.full(K, 0.75, np.float32))   # constant row
+    q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
+    _sync()
+    q_ref, s_ref = KIND_ORACLE_ACT[kind](x)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_act_stage_order_fixture(crp):
+    """The hand-derived stage-order case: codes and scale bits."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fwht_order_case.json")))
+    x = np.zeros((1, 256), np.uint16)
+    for k, h in g["input_bf16_hex"].items():
+        x[0, int(k)] = int(h, 16)
+    q, s = crp.dbg_quant_act(0, to_dev_bf16(x))
+    _sync()
+    assert np.array_equal(q.cpu().numpy()[0], np.tile(np.array(g["expected_int4_codes_by_k_mod_4"], np.int8), 64))
+    assert s.cpu().numpy().view(np.uint32)[0] == int(g["expected_scale_f32_hex"], 16)
+
+
+# ---------------------------------------------------------------------------
+# Weight packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(256, 512), (100, 512), (33, 256), (64, 2560)])
+def test_pack_w4_bitexact(crp, N, K):
+    L = si.random_layer(1, K, N, seed=N * 7 + K)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    codes = crp.dbg_unpack_weight(0, p, N, K)
+    _sync()
+    q_ref, s_ref = O.quant_weight_w4(L.w)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert s.cpu().numpy()[:1].view(np.uint32)[0] == np.float32(s_ref).view(np.uint32)
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (7, 100), (64, 2688), (40, 3072)])
+def test_pack_int8tw_bitexact(crp, N, K):
+    L = si.random_layer(1, K, N, seed=N * 5 + K)
+    p, s = crp.pack_weight_int8tw(to_dev_bf16(L.w))
+    codes = crp.dbg_unpack_weight(1, p, N, K)
+    _sync()
+    q_ref, s_ref = O.quant_weight_int8tw(L.w)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert s.cpu().numpy()[:1].view(np.uint32)[0] == np.float32(s_ref).view(np.uint32)
+
+
+def _w4a8_dev(crp, idx_packed, s_rel, cb, N, K):
+    return crp.pack_weight_w4a8(to_dev(idx_packed), to_dev(s_rel), to_dev(cb.astype(np.float32)), N, K)
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (50, 768)])
+def test_pack_w4a8_decode_bitexact(crp, N, K):
+    L = si.random_layer(1, K, N, seed=N + K)
+    enc = O.w4a8_encode(L.w)
+    p = _w4a8_dev(crp, enc["idx_packed"], enc["s_rel"], enc["codebook"], N, K)
+    codes = crp.dbg_unpack_weight(2, p, N, K)
+    _sync()
+    assert np.array_equal(codes.cpu().numpy(), O.w4a8_decode(enc["idx"], enc["s_rel"], enc["codebook"]))
+
+
+def test_pack_w4a8_random_format_bitexact(crp):
+    """Random stored tensors, including scale codes that saturate at 127."""
+    N, K = 96, 512
+    idx, s_rel, cb, _ = si.random_w4a8_format(N, K, seed=3)
+    s_rel[0, :] = 0x78                                  # 256: every |cb| >= 0.5 saturates
+    s_rel[1, :4] = np.array([0x00, 0x01, 0x7F, 0xFF], np.uint8)   # zero, subnormal, NaN codes
+    p = _w4a8_dev(crp, idx, s_rel, cb, N, K)
+    codes = crp.dbg_unpack_weight(2, p, N, K)
+    _sync()
+    assert np.array_equal(codes.cpu().numpy(), O.w4a8_decode(O.unpack_uint4(idx), s_rel, cb))
+
+
+# ---------------------------------------------------------------------------
+# Accumulators and outputs
+# ---------------------------------------------------------------------------
+
+def _run_w4a4(crp, L, acc=True):
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    bias = to_dev_bf16(L.bias) if L.bias is not None else None
+    y = crp.linear_w4a4(x, p, s, L.N, bias)
+    a = crp.dbg_linear_acc(0, x, p, L.N) if acc else None
+    _sync()
+    return y, a
+
+
+SHAPES = [
+    (64, 512, 256), (1, 256, 64), (33, 512, 100), (76, 2560, 512), (128, 1024, 256),
+    (129, 512, 256), (300, 768, 384), (257, 256, 96), (96, 2048, 2560), (2, 9728, 64),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w4a4_acc_and_output(crp, M, K, N):
+    L = si.random_layer(M, K, N, seed=M * 3 + K + N, bias=(M % 2 == 1), outlier_count=6)
+    y, a = _run_w4a4(crp, L)
+    r = O.linear_w4a4(L.x, L.w, L.bias)
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    yd = bf16_dev_to_f32(y)
+    assert max_rel_err(yd, r["y"]) <= TOL
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(r["y"]))
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 2688, 256), (7, 2688, 7), (130, 100, 40), (76, 3072, 384),
+                                   (5, 7, 9), (200, 192, 64)])
+def test_int8tw_acc_and_output(crp, M, K, N):
+    L = si.random_layer(M, K, N, seed=M + K * 3 + N, bias=True)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_int8tw(to_dev_bf16(L.w))
+    y = crp.linear_int8tw(x, p, s, N, to_dev_bf16(L.bias))
+    a = crp.dbg_linear_acc(1, x, p, N)
+    _sync()
+    r = O.linear_int8tw(L.x, L.w, L.bias)
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 512, 256), (76, 768, 96), (200, 512, 160), (3, 256, 33)])
+def test_w4a8_acc_and_output(crp, M, K, N):
+    L = si.random_layer(M, K, N, seed=M + K + N * 11, bias=True)
+    enc = O.w4a8_encode(L.w)
+    x = to_dev_bf16(L.x)
+    p = _w4a8_dev(crp, enc["idx_packed"], enc["s_rel"], enc["codebook"], N, K)
+    sch = to_dev(enc["s_channel"])
+    y = crp.linear_w4a8(x, p, sch, N, to_dev_bf16(L.bias))
+    a = crp.dbg_linear_acc(2, x, p, N)
+    _sync()
+    r = O.linear_w4a8(L.x, enc["idx_packed"], enc["s_rel"], enc["codebook"], enc["s_channel"], L.bias)
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
+
+
+def test_tiny_config_end_to_end(crp):
+    L = si.tiny()
+    y, a = _run_w4a4(crp, L)
+    r = O.linear_w4a4(L.x, L.w)
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def test_zero_rows_give_bias(crp):
+    L = si.random_layer(40, 512, 64, seed=1, bias=True)
+    L.x[[0, 17, 39], :] = 0
+    y, a = _run_w4a4(crp, L)
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    for m in (0, 17, 39):
+        assert np.array_equal(yb[m], L.bias)
+        assert np.all(a.cpu().numpy()[m] == 0)
+
+
+def test_m_zero_noop(crp):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    p, s = crp.pack_weight_w4(to_dev_bf16(si.random_layer(1, 256, 32, seed=0).w))
+    y = crp.linear_w4a4(x, p, s, 32)
+    _sync()
+    assert tuple(y.shape) == (0, 32)
+
+
+def test_group_error_raises(crp):
+    w = to_dev_bf16(si.random_layer(1, 2688, 64, seed=0).w)
+    with pytest.raises(crp.ConvRotError) as e:
+        crp.pack_weight_w4(w)
+    assert e.value.status == 3
+    pw = crp.pack_linear(w)        # routed to int8_tensorwise
+    assert pw.kind == crp.INT8TW
+
+
+def test_short_workspace_raises(crp):
+    L = si.random_layer(8, 512, 64, seed=2)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(crp.ConvRotError) as e:
+        crp.linear_w4a4(to_dev_bf16(L.x), p, s, 64, workspace=ws)
+    assert e.value.status == 5
+
+
+def test_repeat_runs_identical_and_workspace_reuse(crp):
+    L = si.random_layer(76, 2560, 1024, seed=4)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    ws = torch.empty(crp.workspace_bytes(0, 76, 1024, 2560), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)
+    y1 = crp.linear_w4a4(x, p, s, 1024, workspace=ws).clone()
+    y2 = crp.linear_w4a4(x, p, s, 1024, workspace=ws).clone()
+    _sync()
+    assert torch.equal(y1, y2)
+
+
+def test_no_dequantized_weight_buffer(crp):
+    """The quantised path never materialises a dequantised weight: its
+    workspace holds the activation codes and small partial sums only."""
+    M, N, K = 76, 9728, 2560
+    assert crp.workspace_bytes(0, M, N, K) < N * K   # far below a bf16 N*K copy
