@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the ConvRot-quantized linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--rows all|none|name,name] [--repeat R]
+
+Headline ("step"): one W4A4 ConvRot linear of the DiT image-token MLP (W1,
+x bf16 [4096,3072], W [12288,3072], bias) - activation rotation +
+quantisation kernel, then the int-MFMA GEMM with the rank-one epilogue - on
+inputs resident in HBM, weights packed beforehand (offline).  value = int
+TOPS (2*M*N*K / step time).
+
+Also measured in the same run, each by replaying a HIP graph of repeated
+calls and timing it with HIP events on the launch stream:
+  * the GEMM kernel alone (roofline: int8 MFMA peak 5.0 POPS dense) and the
+    activation kernel alone (roofline: HBM 8 TB/s);
+  * every other row of the hot path: DiT W2, text-encoder gate/up and down
+    at M=76 (weight-stream GB/s with cold weights cycled through 48 copies,
+    more than twice the 256 MB last-level cache) and M=1220, the
+    int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer.
+The CPU oracle (NumPy) is timed on a row sample of the headline layer.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POPS
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+COLD_COPIES = 48
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rotated_bit_quantized_convrot_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Rows of the hot path
+# ---------------------------------------------------------------------------
+
+def row_specs():
+    import synthetic_inputs as si
+    return {
+        "dit_w1": dict(kind=0, gen=lambda: si.dit_w1(), cold=False),
+        "dit_w2": dict(kind=0, gen=lambda: si.dit_w2(), cold=False),
+        "te_gate_up_M76": dict(kind=0, gen=lambda: si.te_gate_up(76), cold=True),
+        "te_down_M76": dict(kind=0, gen=lambda: si.te_down(76), cold=True),
+        "te_gate_up_M1220": dict(kind=0, gen=lambda: si.te_gate_up(1220), cold=False),
+        "te_down_M1220": dict(kind=0, gen=lambda: si.te_down(1220), cold=False),
+        "int8tw_vo": dict(kind=1, gen=lambda: si.int8tw_vo(), cold=False),
+        "int8tw_k2688": dict(kind=1, gen=lambda: si.int8tw_k2688(), cold=False),
+        "w4a8": dict(kind=2, gen=lambda: si.w4a8_layer(), cold=False),
+    }
+
+
+class Layer:
+    """A layer's device buffers: x, packed weight(s), scale, bias, y, workspace."""
+
+    def __init__(self, crp, torch, L, kind, copies=1):
+        import synthetic_inputs as si
+        dev = "cuda"
+        self.crp, self.torch, self.kind = crp, torch, kind
+        self.M, self.K, self.N = L.M, L.K, L.N
+        self.x = torch.from_numpy(L.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.bias = None
+        if L.bias is not None:
+            self.bias = torch.from_numpy(L.bias.view(np.int16)).view(torch.bfloat16).to(dev)
+        if kind == 2:
+            idx, s_rel, cb, s_ch = si.random_w4a8_format(L.N, L.K, seed=0)
+            p = crp.pack_weight_w4a8(torch.from_numpy(idx).to(dev), torch.from_numpy(s_rel).to(dev),
+                                     torch.from_numpy(cb).to(dev), L.N, L.K)
+            s = torch.from_numpy(s_ch).to(dev)
+        else:
+            w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
+            p, s = (crp.pack_weight_w4 if kind == 0 else crp.pack_weight_int8tw)(w)
+            del w
+        self.packed = [p] + [p.clone() for _ in range(copies - 1)]
+        self.scale = s
+        self.y = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(crp.workspace_bytes(kind, L.M, L.N, L.K), dtype=torch.uint8, device=dev)
+        self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8}[kind]
+
+    def linear(self, i=0):
+        return self.fn(self.x, self.packed[i], self.scale, self.N, self.bias, self.y, self.ws)
+
+    def quant(self):
+        self.crp.quantize_activations(self.kind, self.x, self.ws)
+
+    def gemm(self, i=0):
+        self.crp.gemm_quantized(self.kind, self.M, self.K, self.packed[i], self.scale, self.N, self.ws,
+                                self.bias, self.y)
+
+    # algorithmic quantities
+    def ops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def weight_bytes(self):
+        if self.kind == 0:
+            return self.N * self.K / 2
+        if self.kind == 1:
+            return self.N * self.K
+        return self.N * self.K / 2 + self.N * self.K / 16 + 4 * self.N
+
+    def gemm_bytes(self):
+        qx = self.M * self.K
+        y = self.M * self.N * 2
+        b = self.N * 2 if self.bias is not None else 0
+        return qx + self.weight_bytes() + y + b + 4 * self.M
+
+    def quant_bytes(self):
+        return self.M * self.K * 2 + self.M * self.K + 4 * self.M
+
+    def linear_bytes(self):
+        return self.M * self.K * 2 + self.weight_bytes() + self.M * self.N * 2 + \
+            (self.N * 2 if self.bias is not None else 0)
+
+
+def graph_time_us(torch, fn_list, iters):
+    """Average time per call of the calls in fn_list, replayed as one HIP graph."""
+    for f in fn_list:          # eager warm-up (first-call checks happen outside capture)
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fn_list:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (iters * len(fn_list))
+    del g
+    return us
+
+
+def measure_row(torch, lay: Layer, cold: bool, reps: int):
+    n = len(lay.packed)
+    calls = max(reps, n)
+    out = {}
+    out["linear_us"] = graph_time_us(torch, [lambda i=i: lay.linear(i % n) for i in range(calls)], 5)
+    lay.quant()
+    out["gemm_us"] = graph_time_us(torch, [lambda i=i: lay.gemm(i % n) for i in range(calls)], 5)
+    out["quant_us"] = graph_time_us(torch, [lay.quant for _ in range(reps)], 5)
+    out["linear_tops"] = lay.ops() / (out["linear_us"] * 1e-6) / 1e12
+    out["gemm_tops"] = lay.ops() / (out["gemm_us"] * 1e-6) / 1e12
+    out["gemm_frac_int8_peak"] = out["gemm_tops"] / PEAK_INT8_TOPS
+    out["weight_gbs"] = lay.weight_bytes() / (out["gemm_us"] * 1e-6) / 1e9
+    out["gemm_alg_gbs"] = lay.gemm_bytes() / (out["gemm_us"] * 1e-6) / 1e9
+    out["linear_alg_gbs"] = lay.linear_bytes() / (out["linear_us"] * 1e-6) / 1e9
+    out["quant_gbs"] = lay.quant_bytes() / (out["quant_us"] * 1e-6) / 1e9
+    out["cold_weights"] = bool(cold)
+    out["shape"] = {"M": lay.M, "K": lay.K, "N": lay.N}
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a row sample of the headline layer
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(L, rows: int):
+    from oracle import convrot_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    qw, sw = O.quant_weight_w4(L.w)           # offline weight preparation: not timed
+    xs = L.x[:rows]
+    bias = L.bias
+    t0 = time.perf_counter()
+    qx, sx = O.quant_act_w4a4(xs)
+    acc = O.int_gemm(qx, qw)
+    O.epilogue(acc, sx, sw, bias)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * L.N * L.K
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"DiT W1 W4A4 linear, first {rows} of {L.M} rows (K={L.K}, N={L.N}); "
+                      "rotation+quantisation of x, exact integer GEMM (float64 BLAS), epilogue; "
+                      "weight preparation excluded (offline on both sides)"}
+
+
+def load_traffic(kernel_hash: str):
+    """HBM traffic per GEMM launch from committed rocprofv3 --pmc runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "gemm_w4a4_dit_w1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_sources_hash") != kernel_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeat", type=int, default=20, help="calls per captured graph")
+    ap.add_argument("--rows", default="all", help="all | none | comma-separated row names")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the linear would shard by rows with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rotated_bit_quantized_convrot_amd as crp
+    crp.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    khash = kernel_sources_hash()
+
+    specs = row_specs()
+    _log("generating DiT W1 inputs")
+    Lh = specs["dit_w1"]["gen"]()
+    head = Layer(crp, torch, Lh, 0)
+
+    # --- headline: K timed steps of the whole linear -----------------------
+    for _ in range(args.warmup):
+        head.linear()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        head.linear()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    value = head.ops() / (ms_per_step * 1e-3) / 1e12
+    _log(f"headline: {ms_per_step * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events")
+
+    # --- kernels of the headline step: GEMM and activation kernel -----------
+    hrow = measure_row(torch, head, False, args.repeat)
+    _log(f"dit_w1 gemm {hrow['gemm_us']:.1f} us = {hrow['gemm_tops']:.0f} TOPS; "
+         f"quant {hrow['quant_us']:.1f} us")
+
+    rows = {"dit_w1": hrow}
+    wanted = [] if args.rows == "none" else (
+        [r for r in specs if r != "dit_w1"] if args.rows == "all" else
+        [r for r in args.rows.split(",") if r != "dit_w1"])
+    for name in wanted:
+        sp = specs[name]
+        _log(f"row {name}")
+        lay = Layer(crp, torch, sp["gen"](), sp["kind"], COLD_COPIES if sp["cold"] else 1)
+        rows[name] = measure_row(torch, lay, sp["cold"], args.repeat)
+        r = rows[name]
+        _log(f"  linear {r['linear_us']:.2f} us ({r['linear_tops']:.0f} TOPS), gemm {r['gemm_us']:.2f} us "
+             f"({r['gemm_tops']:.0f} TOPS, weights {r['weight_gbs']:.0f} GB/s), quant {r['quant_us']:.2f} us")
+        del lay
+        torch.cuda.empty_cache()
+
+    gemm_us = hrow["gemm_us"]
+    roofline = {
+        "bound": "mfma",
+        "kernel": "k_gemm_big<W4> (DiT W1, M=4096 K=3072 N=12288)",
+        "achieved": round(hrow["gemm_tops"], 2),
+        "peak": PEAK_INT8_TOPS,
+        "unit": "TFLOP/s",
+        "frac": round(hrow["gemm_tops"] / PEAK_INT8_TOPS, 4),
+        "traffic": load_traffic(khash),
+        "algorithmic_bytes": head.gemm_bytes(),
+        "avg_launch_us": round(gemm_us, 3),
+        "note": "int8 MFMA ops (2*M*N*K per launch) / average GEMM launch duration (HIP events over a "
+                "replayed graph of back-to-back launches on the launch stream); unit is int TOPS",
+    }
+    small = rows.get("te_gate_up_M76")
+    small_m = None
+    if small is not None:
+        small_m = {
+            "workload": "text-encoder gate/up W4A4, M=76 K=2560 N=9728, cold weights",
+            "bound": "hbm",
+            "weight_gbs": round(small["weight_gbs"], 1),
+            "gemm_alg_gbs": round(small["gemm_alg_gbs"], 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(small["weight_gbs"] / PEAK_HBM_GBS, 4),
+            "gemm_us": round(small["gemm_us"], 3),
+            "linear_us": round(small["linear_us"], 3),
+        }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log(f"cpu baseline on {args.cpu_rows} rows")
+        cpu = cpu_baseline(Lh, args.cpu_rows)
+
+    out = {
+        "metric": "fused ConvRot W4A4 linear TOPS (% int8 MFMA peak) + small-M HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; shapes and distributions of the DiT image-token MLP W1)",
+        "config": {
+            "workload": "DiT image-token MLP W1, W4A4 ConvRot linear: x bf16 [4096,3072] Student-t(3) "
+                        "with 1% outlier channels x50, W [12288,3072] N(0,0.02), bias, group 256",
+            "M": head.M, "K": head.K, "N": head.N, "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "small_m": small_m,
+        "cpu_baseline": cpu,
+        "step_events_us": round(ev_ms * 1e3, 3),
+        "rows": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                 for k, v in rows.items()},
+        "kernel_sources_hash": khash,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

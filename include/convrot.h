@@ -139,6 +139,31 @@ cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed,
                          const float* s_channel, int N, const void* bias_bf16,
                          void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- two-phase form of the linears ------------------------------------
+ * cr_linear_<kind>(x, ...) == cr_quantize_activations(kind, x, ...) followed
+ * by cr_gemm_quantized(kind, ...) on the same workspace and stream; results
+ * are bit-identical.  One quantisation may feed GEMMs against several
+ * weights with the same K (e.g. the gate and up projections of an MLP,
+ * which read the same x); the workspace must then be sized with
+ * cr_workspace_bytes() for the largest N, and GEMMs sharing it must run in
+ * stream order.  The [QIE] card describes the rotation and quantisation of
+ * the activations as part of the same fused kernel as the MMA; here they are
+ * two kernels on one stream (rotation + quantisation need the whole row for
+ * its scale before any code can be used). */
+
+/* Rotation (W4A4, W4A8) and per-row quantisation of x [M,K] into `ws`.
+ * ws_bytes >= cr_workspace_bytes(kind, M, 1, K). */
+cr_status cr_quantize_activations(int kind, const void* x_bf16, int M, int K, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* GEMM + rank-one epilogue from a workspace filled by
+ * cr_quantize_activations(kind, x, M, K, ...).  w_scale is the tensor scale
+ * (W4A4, int8_tensorwise) or s_channel [N] (W4A8).
+ * ws_bytes >= cr_workspace_bytes(kind, M, N, K). */
+cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const float* w_scale,
+                            int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* ---- status ----------------------------------------------------------- */
 const char* cr_status_str(cr_status s);
 const char* cr_last_error(void);   /* thread-local detail of the last failure */

@@ -29,6 +29,7 @@ __all__ = [
     "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8",
     "linear_w4a4", "linear_int8tw", "linear_w4a8",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
+    "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
 ]
 
@@ -43,7 +44,7 @@ EXPORTS = [
     "cr_packed_bytes", "cr_workspace_bytes", "cr_pack_weight_w4", "cr_linear_w4a4",
     "cr_pack_weight_int8tw", "cr_linear_int8tw", "cr_pack_weight_w4a8", "cr_linear_w4a8",
     "cr_status_str", "cr_last_error", "cr_dbg_quant_act", "cr_dbg_unpack_weight",
-    "cr_dbg_linear_acc",
+    "cr_dbg_linear_acc", "cr_quantize_activations", "cr_gemm_quantized",
 ]
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         "cr_dbg_quant_act": (i, [i, vp, i, i, vp, vp, vp]),
         "cr_dbg_unpack_weight": (i, [i, vp, i, i, vp, vp]),
         "cr_dbg_linear_acc": (i, [i, vp, i, i, vp, i, vp, vp, sz, vp]),
+        "cr_quantize_activations": (i, [i, vp, i, i, vp, sz, vp]),
+        "cr_gemm_quantized": (i, [i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -215,6 +218,35 @@ def linear_int8tw(x, packed, scale, N, bias=None, out=None, workspace=None):
 def linear_w4a8(x, packed, s_channel, N, bias=None, out=None, workspace=None):
     """y = asym W4A8 codebook linear; s_channel float32 [N]."""
     return _linear("cr_linear_w4a8", W4A8, x, packed, s_channel, N, bias, out, workspace)
+
+
+# ---------------------------------------------------------------------------
+# Two-phase form: quantise x once, run GEMMs against one or more weights
+# ---------------------------------------------------------------------------
+
+def quantize_activations(kind: int, x: torch.Tensor, workspace: torch.Tensor):
+    """Rotate (W4A4, W4A8) and quantise x [M,K] into ``workspace``."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(workspace, "workspace", torch.uint8)
+    M, K = x.shape
+    _check(lib().cr_quantize_activations(kind, _ptr(x), M, K, _ptr(workspace), workspace.numel(),
+                                         _stream()))
+
+
+def gemm_quantized(kind: int, M: int, K: int, packed, scale, N: int, workspace, bias=None, out=None):
+    """GEMM + epilogue from a workspace filled by :func:`quantize_activations`."""
+    _dev(packed, "packed", torch.uint8)
+    _dev(scale, "scale", torch.float32)
+    _dev(workspace, "workspace", torch.uint8)
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=packed.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+    _check(lib().cr_gemm_quantized(kind, M, K, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream()))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -78,8 +78,12 @@ size_t packed_bytes(int kind, int N, int K) {
 
 int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K; }
 
+// Workspace: [codes M x Kp][scales M][split-K counters][split-K partials].
+// Everything but the partials is independent of N, so one quantisation can
+// feed GEMMs against several weights (with the workspace sized for the
+// largest N).
 struct WsLayout {
-    size_t qx, sx, scratch, total;
+    size_t qx, sx, counters, part, quant_end, total;
 };
 
 WsLayout ws_layout(int kind, int M, int N, int K) {
@@ -87,9 +91,14 @@ WsLayout ws_layout(int kind, int M, int N, int K) {
     const int Kp = kp_of(kind, K);
     l.qx = 0;
     l.sx = a256((size_t)M * Kp);
-    l.scratch = l.sx + a256((size_t)M * 4);
-    l.total = l.scratch + cr::gemm_scratch_bytes(M, N, K);
+    l.counters = l.sx + a256((size_t)M * 4);
+    const bool skinny = M > 0 && M <= cr::kSkinnyMaxM;
+    l.part = l.counters + (skinny ? a256((size_t)cr::kMaxCounters * 4) : 0);
+    l.quant_end = l.part;
+    const cr::SkinnyPlan sp = cr::plan_skinny(M, N, K);
+    l.total = l.part + a256(sp.use ? sp.part_bytes : 0);
     if (l.total < 256) l.total = 256;
+    if (l.quant_end < 256) l.quant_end = 256;
     return l;
 }
 
@@ -98,47 +107,82 @@ cr_status launch_err(hipError_t e, const char* what) {
     return fail(CR_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Shared body of the three linears and the accumulator hook.
-cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, const float* wscale, int N,
-                     const void* bias, void* y, int32_t* acc, void* ws, size_t ws_bytes,
-                     hipStream_t st) {
-    cr_status s;
-    if ((s = check_kind(kind)) != CR_OK) return s;
+int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8); }
+
+cr_status check_m(int M) {
     if (M < 0 || M > CR_MAX_DIM) return fail(CR_ERR_SHAPE, "bad M=%d", M);
-    if ((s = check_nk(kind, N, K)) != CR_OK) return s;
-    if (wp == nullptr) return fail(CR_ERR_NULL, "packed weight is NULL");
-    if (acc == nullptr && wscale == nullptr) return fail(CR_ERR_NULL, "weight scale is NULL");
-    if (!aligned16(wp)) return fail(CR_ERR_ALIGN, "packed weight not 16-byte aligned");
-    if (bias != nullptr && !aligned16(bias)) return fail(CR_ERR_ALIGN, "bias not 16-byte aligned");
-    if (M == 0) return ok();
-    if (x == nullptr || ws == nullptr || (acc == nullptr && y == nullptr))
-        return fail(CR_ERR_NULL, "x, y or workspace is NULL");
-    if (!aligned16(x) || !aligned16(ws) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
-        return fail(CR_ERR_ALIGN, "x, y, accumulator or workspace not 16-byte aligned");
+    return CR_OK;
+}
+
+// Phase 1: codes and scales of x into the workspace (and clear the counters).
+cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t ws_bytes, hipStream_t st) {
+    const WsLayout l = ws_layout(kind, M, 1, K);
+    if (ws_bytes < l.quant_end)
+        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.quant_end);
+    char* w = static_cast<char*>(ws);
+    const bool skinny = M <= cr::kSkinnyMaxM;
+    hipError_t e = cr::launch_quant_act(wkind(kind), static_cast<const uint16_t*>(x), M, K, kp_of(kind, K),
+                                        reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
+                                        skinny ? reinterpret_cast<uint32_t*>(w + l.counters) : nullptr,
+                                        skinny ? cr::kMaxCounters : 0, st);
+    return launch_err(e, "activation quantisation");
+}
+
+// Phase 2: GEMM + epilogue from the workspace.
+cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale, int N, const void* bias,
+                     void* y, int32_t* acc, void* ws, size_t ws_bytes, hipStream_t st) {
     const WsLayout l = ws_layout(kind, M, N, K);
     if (ws_bytes < l.total)
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
-    if ((s = check_device()) != CR_OK) return s;
-
     char* w = static_cast<char*>(ws);
     cr::GemmArgs a{};
-    a.kind = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
-    a.qx = reinterpret_cast<int8_t*>(w + l.qx);
-    a.sx = reinterpret_cast<float*>(w + l.sx);
+    a.kind = wkind(kind);
+    a.qx = reinterpret_cast<const int8_t*>(w + l.qx);
+    a.sx = reinterpret_cast<const float*>(w + l.sx);
     a.M = M; a.N = N; a.K = K; a.Kp = kp_of(kind, K); a.Np = cr::round_up(N, 32);
     a.wp = static_cast<const uint8_t*>(wp);
     a.wscale = wscale;
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.acc_out = acc;
-    a.scratch = w + l.scratch;
-    a.scratch_bytes = l.total - l.scratch;
-
-    hipError_t e = cr::launch_quant_act(a.kind, static_cast<const uint16_t*>(x), M, K, a.Kp,
-                                        const_cast<int8_t*>(a.qx), const_cast<float*>(a.sx),
-                                        cr::gemm_counters(a), cr::gemm_counter_count(M, N, K), st);
-    if (e != hipSuccess) return launch_err(e, "activation quantisation");
+    a.counters = reinterpret_cast<uint32_t*>(w + l.counters);
+    a.part = reinterpret_cast<int32_t*>(w + l.part);
     return launch_err(cr::launch_gemm(a, st), "integer GEMM");
+}
+
+// Checks shared by the linears and the GEMM phase.
+cr_status check_linear_args(int kind, int M, int K, const void* wp, const float* wscale, int N,
+                            const void* bias, const void* y, const int32_t* acc, const void* ws) {
+    cr_status s;
+    if ((s = check_kind(kind)) != CR_OK) return s;
+    if ((s = check_m(M)) != CR_OK) return s;
+    if ((s = check_nk(kind, N, K)) != CR_OK) return s;
+    if (wp == nullptr) return fail(CR_ERR_NULL, "packed weight is NULL");
+    if (acc == nullptr && wscale == nullptr) return fail(CR_ERR_NULL, "weight scale is NULL");
+    if (!aligned16(wp)) return fail(CR_ERR_ALIGN, "packed weight not 16-byte aligned");
+    if (bias != nullptr && !aligned16(bias)) return fail(CR_ERR_ALIGN, "bias not 16-byte aligned");
+    if (M == 0) return CR_OK;
+    if (ws == nullptr || (acc == nullptr && y == nullptr)) return fail(CR_ERR_NULL, "y or workspace is NULL");
+    if (!aligned16(ws) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
+        return fail(CR_ERR_ALIGN, "y, accumulator or workspace not 16-byte aligned");
+    return CR_OK;
+}
+
+// Shared body of the three linears and the accumulator hook.
+cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, const float* wscale, int N,
+                     const void* bias, void* y, int32_t* acc, void* ws, size_t ws_bytes,
+                     hipStream_t st) {
+    cr_status s = check_linear_args(kind, M, K, wp, wscale, N, bias, y, acc, ws);
+    if (s != CR_OK) return s;
+    if (M == 0) return ok();
+    if (x == nullptr) return fail(CR_ERR_NULL, "x is NULL");
+    if (!aligned16(x)) return fail(CR_ERR_ALIGN, "x not 16-byte aligned");
+    const WsLayout l = ws_layout(kind, M, N, K);
+    if (ws_bytes < l.total)
+        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    if ((s = check_device()) != CR_OK) return s;
+    if ((s = quantize_phase(kind, x, M, K, ws, ws_bytes, st)) != CR_OK) return s;
+    return gemm_phase(kind, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
 }
 
 }  // namespace
@@ -215,6 +259,29 @@ cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed,
                          hipStream_t stream) {
     return run_linear(CR_W4A8, x_bf16, M, K, w_packed, s_channel, N, bias_bf16, y_bf16, nullptr, ws,
                       ws_bytes, stream);
+}
+
+cr_status cr_quantize_activations(int kind, const void* x_bf16, int M, int K, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    cr_status s;
+    if ((s = check_kind(kind)) != CR_OK) return s;
+    if ((s = check_m(M)) != CR_OK) return s;
+    if ((s = check_nk(kind, 1, K)) != CR_OK) return s;
+    if (M == 0) return ok();
+    if (x_bf16 == nullptr || ws == nullptr) return fail(CR_ERR_NULL, "x or workspace is NULL");
+    if (!aligned16(x_bf16) || !aligned16(ws)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    if ((s = check_device()) != CR_OK) return s;
+    return quantize_phase(kind, x_bf16, M, K, ws, ws_bytes, stream);
+}
+
+cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const float* w_scale, int N,
+                            const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    cr_status s = check_linear_args(kind, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws);
+    if (s != CR_OK) return s;
+    if (M == 0) return ok();
+    if ((s = check_device()) != CR_OK) return s;
+    return gemm_phase(kind, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, ws_bytes, stream);
 }
 
 const char* cr_status_str(cr_status s) {

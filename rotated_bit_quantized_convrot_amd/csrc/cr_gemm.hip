@@ -391,6 +391,7 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int
     __syncthreads();
     if (!s_last) return;
     __threadfence();
+    if (tid == 0) counters[bx] = 0u;   // every slice has arrived: ready for the next call
 
     // Last block of this column: sum the slices in order, then the epilogue.
     const int ncols = min(128, Np - bx * 128);
@@ -415,7 +416,7 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int
 // ---------------------------------------------------------------------------
 SkinnyPlan plan_skinny(int M, int N, int K) {
     SkinnyPlan sp{};
-    sp.use = M > 0 && M <= 128;
+    sp.use = M > 0 && M <= kSkinnyMaxM;
     if (!sp.use) return sp;
     const int Np = round_up(N, 32), Kp = round_up(K, 64);
     const int nkc = Kp / 64;
@@ -423,39 +424,17 @@ SkinnyPlan plan_skinny(int M, int N, int K) {
     sp.nblk = (Np + 127) / 128;
     sp.splits = (nkc + KSLMAX - 1) / KSLMAX;
     sp.part_bytes = sp.splits > 1 ? (size_t)sp.splits * M * Np * 4 : 0;
-    sp.counter_bytes = (size_t)sp.nblk * 4;
     return sp;
-}
-
-static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
-
-size_t gemm_scratch_bytes(int M, int N, int K) {
-    const SkinnyPlan sp = plan_skinny(M, N, K);
-    if (!sp.use) return 0;
-    return align256(sp.part_bytes) + align256(sp.counter_bytes);
-}
-
-int gemm_counter_count(int M, int N, int K) {
-    const SkinnyPlan sp = plan_skinny(M, N, K);
-    return sp.use ? sp.nblk : 0;
-}
-
-uint32_t* gemm_counters(const GemmArgs& a) {
-    const SkinnyPlan sp = plan_skinny(a.M, a.N, a.K);
-    if (!sp.use || a.scratch == nullptr) return nullptr;
-    return reinterpret_cast<uint32_t*>(static_cast<char*>(a.scratch) + align256(sp.part_bytes));
 }
 
 template <int WK, bool ACC>
 static hipError_t launch_skinny_t(const GemmArgs& a, const SkinnyPlan& sp, hipStream_t st) {
-    int32_t* part = sp.splits > 1 ? static_cast<int32_t*>(a.scratch) : nullptr;
-    uint32_t* cnt = gemm_counters(a);
     dim3 grid(sp.nblk, sp.splits), block(256);
     switch (sp.mf) {
-        case 1: k_gemm_skinny<WK, 1, ACC><<<grid, block, 0, st>>>(a, sp.splits, part, cnt); break;
-        case 2: k_gemm_skinny<WK, 2, ACC><<<grid, block, 0, st>>>(a, sp.splits, part, cnt); break;
-        case 3: k_gemm_skinny<WK, 3, ACC><<<grid, block, 0, st>>>(a, sp.splits, part, cnt); break;
-        case 4: k_gemm_skinny<WK, 4, ACC><<<grid, block, 0, st>>>(a, sp.splits, part, cnt); break;
+        case 1: k_gemm_skinny<WK, 1, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
+        case 2: k_gemm_skinny<WK, 2, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
+        case 3: k_gemm_skinny<WK, 3, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
+        case 4: k_gemm_skinny<WK, 4, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -28,8 +28,8 @@ __host__ __device__ inline size_t w4a8_table_offset(int N, int K) {
 __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_offset(N, K) + 4096; }
 
 // Activation quantisation: codes int8 [M, Kp] (row-major, zero for k >= K)
-// and scales [M].  zero_u32 / zero_count: a region the kernel clears for the
-// GEMM's split-K counters (may be null).
+// and scales [M].  zero_u32 / zero_count: a region the kernel clears (the
+// split-K counters; may be null).
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
                             float* sx, uint32_t* zero_u32, int zero_count, hipStream_t st);
 
@@ -52,23 +52,24 @@ struct GemmArgs {
     const uint16_t* bias;  // [N] or null
     uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
     int32_t* acc_out;      // [M, N] int32 accumulators instead of y
-    void* scratch;         // split-K partials and counters
-    size_t scratch_bytes;
+    int32_t* part;         // split-K partial sums (small-M path)
+    uint32_t* counters;    // split-K arrival counters, zero between calls
 };
 
-// Split-K plan of the small-M path; scratch bytes it needs.
+// Small-M (split-K) path: used for M <= kSkinnyMaxM.  Its arrival counters
+// live at a fixed place in the workspace (kMaxCounters of them, enough for
+// any N <= 2^20), are cleared by the activation quantiser and reset by the
+// block that consumes them, so one quantisation can feed several GEMMs.
+constexpr int kSkinnyMaxM = 128;
+constexpr int kMaxCounters = 8192;
 struct SkinnyPlan {
     bool use;
     int mf;        // 32-row activation fragments (1..4)
     int nblk;      // 128-row weight blocks
     int splits;    // K splits
     size_t part_bytes;     // int32 partials [splits][M][Np]
-    size_t counter_bytes;  // one uint32 per weight block
 };
 SkinnyPlan plan_skinny(int M, int N, int K);
-size_t gemm_scratch_bytes(int M, int N, int K);
-int gemm_counter_count(int M, int N, int K);
-uint32_t* gemm_counters(const GemmArgs& a);
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 

@@ -248,3 +248,42 @@ def test_no_dequantized_weight_buffer(crp):
     workspace holds the activation codes and small partial sums only."""
     M, N, K = 76, 9728, 2560
     assert crp.workspace_bytes(0, M, N, K) < N * K   # far below a bf16 N*K copy
+
+
+def test_two_phase_matches_linear_and_reuses_quantisation(crp):
+    """One quantisation feeding GEMMs against two weights (different N, split
+    K on the small-M path), each repeated: identical to the one-call linear."""
+    M, K = 76, 2560
+    A = si.random_layer(M, K, 640, seed=21, bias=True)
+    B = si.random_layer(M, K, 1152, seed=22)
+    x = to_dev_bf16(A.x)
+    pa, sa = crp.pack_weight_w4(to_dev_bf16(A.w))
+    pb, sb = crp.pack_weight_w4(to_dev_bf16(B.w))
+    ba = to_dev_bf16(A.bias)
+    ya = crp.linear_w4a4(x, pa, sa, 640, ba)
+    yb = crp.linear_w4a4(x, pb, sb, 1152)
+    ws = torch.empty(crp.workspace_bytes(0, M, 1152, K), dtype=torch.uint8, device="cuda")
+    crp.quantize_activations(0, x, ws)
+    outs = []
+    for _ in range(2):
+        outs.append(crp.gemm_quantized(0, M, K, pa, sa, 640, ws, bias=ba))
+        outs.append(crp.gemm_quantized(0, M, K, pb, sb, 1152, ws))
+    _sync()
+    for i in (0, 2):
+        assert torch.equal(outs[i], ya)
+        assert torch.equal(outs[i + 1], yb)
+    r = O.linear_w4a4(A.x, A.w, A.bias)
+    assert max_rel_err(bf16_dev_to_f32(ya), r["y"]) <= TOL
+
+
+def test_two_phase_large_m(crp):
+    M, K, N = 300, 1024, 512
+    L = si.random_layer(M, K, N, seed=23)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_int8tw(to_dev_bf16(L.w))
+    y = crp.linear_int8tw(x, p, s, N)
+    ws = torch.empty(crp.workspace_bytes(1, M, N, K), dtype=torch.uint8, device="cuda")
+    crp.quantize_activations(1, x, ws)
+    y2 = crp.gemm_quantized(1, M, K, p, s, N, ws)
+    _sync()
+    assert torch.equal(y, y2)
