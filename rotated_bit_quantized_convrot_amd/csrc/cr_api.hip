@@ -78,12 +78,11 @@ size_t packed_bytes(int kind, int N, int K) {
 
 int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K; }
 
-// Workspace: [codes M x Kp][scales M][split-K counters][split-K partials].
-// Everything but the partials is independent of N, so one quantisation can
-// feed GEMMs against several weights (with the workspace sized for the
-// largest N).
+// Workspace: [codes M x Kp][scales M][split-K partials].  The codes and
+// scales do not depend on N, so one quantisation can feed GEMMs against
+// several weights (with the workspace sized for the largest N).
 struct WsLayout {
-    size_t qx, sx, counters, part, quant_end, total;
+    size_t qx, sx, part, quant_end, total;
 };
 
 WsLayout ws_layout(int kind, int M, int N, int K) {
@@ -91,9 +90,7 @@ WsLayout ws_layout(int kind, int M, int N, int K) {
     const int Kp = kp_of(kind, K);
     l.qx = 0;
     l.sx = a256((size_t)M * Kp);
-    l.counters = l.sx + a256((size_t)M * 4);
-    const bool skinny = M > 0 && M <= cr::kSkinnyMaxM;
-    l.part = l.counters + (skinny ? a256((size_t)cr::kMaxCounters * 4) : 0);
+    l.part = l.sx + a256((size_t)M * 4);
     l.quant_end = l.part;
     const cr::SkinnyPlan sp = cr::plan_skinny(M, N, K);
     l.total = l.part + a256(sp.use ? sp.part_bytes : 0);
@@ -114,17 +111,14 @@ cr_status check_m(int M) {
     return CR_OK;
 }
 
-// Phase 1: codes and scales of x into the workspace (and clear the counters).
+// Phase 1: codes and scales of x into the workspace.
 cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t ws_bytes, hipStream_t st) {
     const WsLayout l = ws_layout(kind, M, 1, K);
     if (ws_bytes < l.quant_end)
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.quant_end);
     char* w = static_cast<char*>(ws);
-    const bool skinny = M <= cr::kSkinnyMaxM;
     hipError_t e = cr::launch_quant_act(wkind(kind), static_cast<const uint16_t*>(x), M, K, kp_of(kind, K),
-                                        reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
-                                        skinny ? reinterpret_cast<uint32_t*>(w + l.counters) : nullptr,
-                                        skinny ? cr::kMaxCounters : 0, st);
+                                        reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx), st);
     return launch_err(e, "activation quantisation");
 }
 
@@ -145,7 +139,6 @@ cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale
     a.bias = static_cast<const uint16_t*>(bias);
     a.y = static_cast<uint16_t*>(y);
     a.acc_out = acc;
-    a.counters = reinterpret_cast<uint32_t*>(w + l.counters);
     a.part = reinterpret_cast<int32_t*>(w + l.part);
     return launch_err(cr::launch_gemm(a, st), "integer GEMM");
 }
@@ -313,7 +306,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if ((s = check_device()) != CR_OK) return s;
     const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
     return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
-                                           static_cast<int8_t*>(codes), scales, nullptr, 0, stream),
+                                           static_cast<int8_t*>(codes), scales, stream),
                       "activation quantisation");
 }
 

@@ -268,19 +268,19 @@ __global__ void __launch_bounds__(64 * WM * WN, 2) k_gemm_big(GemmArgs p, int ti
 // tile per wave) and one K slice of at most KSLMAX 64-chunks; the slice of the
 // activations (all rows) is staged in LDS once and shared by the 4 waves.
 // Each wave issues all of its weight loads up front.  With several K slices
-// the int32 partial sums go to the workspace and the last block of a column
-// (device-scope counter) adds them in slice order and runs the epilogue.
+// each block stores its int32 partial sums in accumulator-register order
+// (fully coalesced) and k_splitk_reduce, the next kernel on the stream, adds
+// the slices in order and runs the epilogue: no atomics and no device-scope
+// fences (both cost far more than a second launch here).
 // ---------------------------------------------------------------------------
 constexpr int KSLMAX = 8;
 
 template <int WK, int MF, bool ACC>
-__global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int32_t* part,
-                                                     uint32_t* counters) {
+__global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits) {
     constexpr int MR = MF * 32;
     constexpr int CAMAX = MR * KSLMAX * 4 / 256;
     __shared__ __attribute__((aligned(16))) int8_t sA[MR * (KSLMAX * 64 + 16)];
     __shared__ uint4 sT[WK == WK_W4A8 ? 256 : 1];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int bx = blockIdx.x, s = blockIdx.y;
@@ -294,16 +294,21 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int
     const bool active = nb < (p.Np >> 5);
     const size_t codes_off = w4a8_codes_offset(p.N, p.K);
 
-    // 1. activation slice -> registers (indices past the slice re-read its
-    //    last chunk; those registers are not stored)
+    // 1. activation slice -> registers.  Thread chunk idx covers row
+    //    idx / (4*KSLMAX), 16-byte column idx % (4*KSLMAX); columns past the
+    //    slice re-read (and later re-store) the slice's last column, rows
+    //    past M re-read row M-1.  Issued before the weight loads so that the
+    //    wait for them does not wait for the weights.
     uint4 ra[CAMAX];
-    const int nch = MR * ksl * 4;
+    int aoff[CAMAX];
 #pragma unroll
     for (int c = 0; c < CAMAX; ++c) {
-        const int idx = min(tid + c * 256, nch - 1);
-        const int row = idx / (ksl * 4), col = idx - row * (ksl * 4);
+        const int idx = tid + c * 256;
+        const int row = idx / (4 * KSLMAX);
+        const int col = min(idx % (4 * KSLMAX), ksl * 4 - 1);
         const int m = min(row, M - 1);
         ra[c] = *reinterpret_cast<const uint4*>(p.qx + (size_t)m * Kp + (size_t)kc0 * 64 + col * 16);
+        aoff[c] = row * lrow + col * 16;
     }
     // 2. all weight loads of this wave (chunks past the slice re-read its
     //    last chunk and are not used; idle waves read tile 0)
@@ -311,15 +316,9 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int
     const int nbl = active ? nb : 0;
 #pragma unroll
     for (int j = 0; j < KSLMAX; ++j) load_wraw<WK>(wr[j], p.wp, codes_off, nbl, nkc, kc0 + min(j, ksl - 1), lane);
-    // 3. activations -> LDS
+    // 3. activations -> LDS (duplicate chunks store identical bytes)
 #pragma unroll
-    for (int c = 0; c < CAMAX; ++c) {
-        const int idx = tid + c * 256;
-        if (idx < nch) {
-            const int row = idx / (ksl * 4), col = idx - row * (ksl * 4);
-            *reinterpret_cast<uint4*>(sA + row * lrow + col * 16) = ra[c];
-        }
-    }
+    for (int c = 0; c < CAMAX; ++c) *reinterpret_cast<uint4*>(sA + aoff[c]) = ra[c];
     if constexpr (WK == WK_W4A8) {
         const uint4* tg = reinterpret_cast<const uint4*>(p.wp + w4a8_table_offset(p.N, p.K));
         for (int i = tid; i < 256; i += 256) sT[i] = tg[i];
@@ -370,45 +369,53 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits, int
         return;
     }
 
-    // Split K: publish this slice's partial sums (raw MFMA sums, int32).
-    const int Np = p.Np;
-    if (active) {
+    // Split K: this slice's raw MFMA sums, in register order.
+    if (!active) return;
+    int4* dst = reinterpret_cast<int4*>(p.part) + ((((size_t)s * gridDim.x + bx) * 4 + wave) * MF) * 4 * 64 + lane;
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            const int m = i * 32 + (lane & 31);
-            if (m < M) {
-                int32_t* dst = part + ((size_t)s * M + m) * Np + nb * 32 + 4 * h;
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<int4*>(dst + 8 * q) =
-                        make_int4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
-            }
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counters[bx], 1u) == (uint32_t)(splits - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid == 0) counters[bx] = 0u;   // every slice has arrived: ready for the next call
+        for (int q = 0; q < 4; ++q)
+            dst[(i * 4 + q) * 64] = make_int4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
+}
 
-    // Last block of this column: sum the slices in order, then the epilogue.
-    const int ncols = min(128, Np - bx * 128);
-    const int quads = ncols >> 2;
-    for (int item = tid; item < M * quads; item += 256) {
-        const int m = item / quads;
-        const int n = bx * 128 + (item - m * quads) * 4;
-        int4 t = make_int4(0, 0, 0, 0);
-        for (int k = 0; k < splits; ++k) {
-            const int4 v = *reinterpret_cast<const int4*>(part + ((size_t)k * M + m) * Np + n);
-            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
-        }
-        if (n < N) {
-            const float sxm = ACC ? 0.0f : p.sx[m];
-            store4<WK, ACC>(epi, m, n, sxm, fix_acc<WK>(t.x), fix_acc<WK>(t.y), fix_acc<WK>(t.z), fix_acc<WK>(t.w));
-        }
+// Sum of the K slices' partials (in slice order) + epilogue.  One thread per
+// (column block, wave, fragment, register quad, lane) of k_gemm_skinny.
+template <int WK, int MF, bool ACC>
+__global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs p, int splits, int nblk) {
+    const size_t items = (size_t)nblk * 4 * MF * 4 * 64;
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= items) return;
+    const int lane = (int)(id & 63);
+    size_t t = id >> 6;
+    const int q = (int)(t % 4); t /= 4;
+    const int i = (int)(t % MF); t /= MF;
+    const int wave = (int)(t % 4);
+    const int bx = (int)(t / 4);
+    const int nb = bx * 4 + wave;
+    if (nb >= (p.Np >> 5)) return;
+    const int m = i * 32 + (lane & 31);
+    const int n = nb * 32 + 8 * q + 4 * (lane >> 5);
+    if (m >= p.M || n >= p.N) return;
+    const int4* src = reinterpret_cast<const int4*>(p.part) + id;
+    const size_t stride = items;
+    int4 a = make_int4(0, 0, 0, 0);
+    int k = 0;
+    for (; k + 4 <= splits; k += 4) {
+        const int4 v0 = src[(k + 0) * stride], v1 = src[(k + 1) * stride];
+        const int4 v2 = src[(k + 2) * stride], v3 = src[(k + 3) * stride];
+        a.x += v0.x; a.y += v0.y; a.z += v0.z; a.w += v0.w;
+        a.x += v1.x; a.y += v1.y; a.z += v1.z; a.w += v1.w;
+        a.x += v2.x; a.y += v2.y; a.z += v2.z; a.w += v2.w;
+        a.x += v3.x; a.y += v3.y; a.z += v3.z; a.w += v3.w;
     }
+    for (; k < splits; ++k) {
+        const int4 v = src[k * stride];
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    const Epi epi = make_epi(p);
+    const float sxm = ACC ? 0.0f : p.sx[m];
+    store4<WK, ACC>(epi, m, n, sxm, fix_acc<WK>(a.x), fix_acc<WK>(a.y), fix_acc<WK>(a.z), fix_acc<WK>(a.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -423,21 +430,29 @@ SkinnyPlan plan_skinny(int M, int N, int K) {
     sp.mf = (M + 31) / 32;
     sp.nblk = (Np + 127) / 128;
     sp.splits = (nkc + KSLMAX - 1) / KSLMAX;
-    sp.part_bytes = sp.splits > 1 ? (size_t)sp.splits * M * Np * 4 : 0;
+    sp.part_bytes = sp.splits > 1 ? (size_t)sp.splits * sp.nblk * 4 * sp.mf * 4 * 64 * 16 : 0;
     return sp;
+}
+
+template <int WK, int MF, bool ACC>
+static hipError_t launch_skinny_mf(const GemmArgs& a, const SkinnyPlan& sp, hipStream_t st) {
+    k_gemm_skinny<WK, MF, ACC><<<dim3(sp.nblk, sp.splits), dim3(256), 0, st>>>(a, sp.splits);
+    if (sp.splits > 1) {
+        const size_t items = (size_t)sp.nblk * 4 * MF * 4 * 64;
+        k_splitk_reduce<WK, MF, ACC><<<dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st>>>(a, sp.splits, sp.nblk);
+    }
+    return hipGetLastError();
 }
 
 template <int WK, bool ACC>
 static hipError_t launch_skinny_t(const GemmArgs& a, const SkinnyPlan& sp, hipStream_t st) {
-    dim3 grid(sp.nblk, sp.splits), block(256);
     switch (sp.mf) {
-        case 1: k_gemm_skinny<WK, 1, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
-        case 2: k_gemm_skinny<WK, 2, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
-        case 3: k_gemm_skinny<WK, 3, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
-        case 4: k_gemm_skinny<WK, 4, ACC><<<grid, block, 0, st>>>(a, sp.splits, a.part, a.counters); break;
+        case 1: return launch_skinny_mf<WK, 1, ACC>(a, sp, st);
+        case 2: return launch_skinny_mf<WK, 2, ACC>(a, sp, st);
+        case 3: return launch_skinny_mf<WK, 3, ACC>(a, sp, st);
+        case 4: return launch_skinny_mf<WK, 4, ACC>(a, sp, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int WK, bool ACC>

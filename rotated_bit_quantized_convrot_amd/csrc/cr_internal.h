@@ -28,10 +28,9 @@ __host__ __device__ inline size_t w4a8_table_offset(int N, int K) {
 __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_offset(N, K) + 4096; }
 
 // Activation quantisation: codes int8 [M, Kp] (row-major, zero for k >= K)
-// and scales [M].  zero_u32 / zero_count: a region the kernel clears (the
-// split-K counters; may be null).
+// and scales [M].
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, uint32_t* zero_u32, int zero_count, hipStream_t st);
+                            float* sx, hipStream_t st);
 
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
                           hipStream_t st);
@@ -53,21 +52,18 @@ struct GemmArgs {
     uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
     int32_t* acc_out;      // [M, N] int32 accumulators instead of y
     int32_t* part;         // split-K partial sums (small-M path)
-    uint32_t* counters;    // split-K arrival counters, zero between calls
 };
 
-// Small-M (split-K) path: used for M <= kSkinnyMaxM.  Its arrival counters
-// live at a fixed place in the workspace (kMaxCounters of them, enough for
-// any N <= 2^20), are cleared by the activation quantiser and reset by the
-// block that consumes them, so one quantisation can feed several GEMMs.
+// Small-M (split-K) path, used for M <= kSkinnyMaxM: a GEMM kernel that
+// writes each K slice's int32 partials to the workspace and a reduction
+// kernel that adds them and runs the epilogue.
 constexpr int kSkinnyMaxM = 128;
-constexpr int kMaxCounters = 8192;
 struct SkinnyPlan {
     bool use;
     int mf;        // 32-row activation fragments (1..4)
     int nblk;      // 128-row weight blocks
     int splits;    // K splits
-    size_t part_bytes;     // int32 partials [splits][M][Np]
+    size_t part_bytes;     // int32 partials, [splits][nblk][4 waves][mf][4][64 lanes] x int4
 };
 SkinnyPlan plan_skinny(int M, int N, int K);
 

@@ -68,14 +68,9 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 template <int GPL, int QMAX, int LO, int HI>
 __global__ void __launch_bounds__(512) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
                                                        int8_t* __restrict__ qx,
-                                                       float* __restrict__ sx,
-                                                       uint32_t* __restrict__ zero_u32,
-                                                       int zero_count) {
+                                                       float* __restrict__ sx) {
     __shared__ float red[16];
     const int m = blockIdx.x;
-    if (zero_u32 != nullptr && m == 0) {
-        for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_u32[i] = 0u;
-    }
     const int G = K >> 8;
     const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
     RotRow<GPL> r;
@@ -101,14 +96,9 @@ __global__ void __launch_bounds__(512) k_quant_act_rot(const uint16_t* __restric
 // in [K, Kp).  Two passes over the row (the second one hits the cache).
 __global__ void __launch_bounds__(256) k_quant_act_plain(const uint16_t* __restrict__ x, int M,
                                                          int K, int Kp, int8_t* __restrict__ qx,
-                                                         float* __restrict__ sx,
-                                                         uint32_t* __restrict__ zero_u32,
-                                                         int zero_count) {
+                                                         float* __restrict__ sx) {
     __shared__ float red[16];
     const int m = blockIdx.x;
-    if (zero_u32 != nullptr && m == 0) {
-        for (int i = threadIdx.x; i < zero_count; i += blockDim.x) zero_u32[i] = 0u;
-    }
     const uint16_t* row = x + (size_t)m * K;
     int8_t* out = qx + (size_t)m * Kp;
     const bool vec = (K % 8) == 0;
@@ -156,27 +146,26 @@ static int rot_threads(int G, int* gpl) {
 }
 
 template <int QMAX, int LO, int HI>
-static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, uint32_t* z,
-                             int zc, hipStream_t st) {
+static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, hipStream_t st) {
     int gpl = 1;
     const int threads = rot_threads(K >> 8, &gpl);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
-        case 8: k_quant_act_rot<8, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
-        case 16: k_quant_act_rot<16, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx, z, zc); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
+        case 8: k_quant_act_rot<8, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
+        case 16: k_quant_act_rot<16, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, uint32_t* zero_u32, int zero_count, hipStream_t st) {
-    if (kind == WK_W4) return launch_rot<7, -8, 7>(x, M, K, qx, sx, zero_u32, zero_count, st);
-    if (kind == WK_W4A8) return launch_rot<127, -128, 127>(x, M, K, qx, sx, zero_u32, zero_count, st);
-    k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx, zero_u32, zero_count);
+                            float* sx, hipStream_t st) {
+    if (kind == WK_W4) return launch_rot<7, -8, 7>(x, M, K, qx, sx, st);
+    if (kind == WK_W4A8) return launch_rot<127, -128, 127>(x, M, K, qx, sx, st);
+    k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
 }
 
