@@ -83,13 +83,15 @@ __device__ __forceinline__ Epi make_epi(const GemmArgs& p) {
 }
 
 // Writes 4 consecutive outputs n..n+3 of row m (n % 4 == 0, n < N).
+// sw0: the tensor scale (unused for W4A8, which reads s_channel[n]).
 template <int WK, bool ACC>
-__device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, int a0, int a1,
-                                       int a2, int a3) {
+__device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, float sw0, int a0,
+                                       int a1, int a2, int a3) {
     const int N = e.N;
+    const bool full = (N & 3) == 0;          // n + 3 < N then, rows 8-byte aligned
     if constexpr (ACC) {
         int32_t* dst = e.acc_out + (size_t)m * N + n;
-        if ((N & 3) == 0) {
+        if (full) {
             *reinterpret_cast<int4*>(dst) = make_int4(a0, a1, a2, a3);
         } else {
             dst[0] = a0;
@@ -97,60 +99,132 @@ __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, in
             if (n + 2 < N) dst[2] = a2;
             if (n + 3 < N) dst[3] = a3;
         }
+    } else if (full) {
+        float sw[4] = {sw0, sw0, sw0, sw0};
+        if constexpr (WK == WK_W4A8) {
+            const float4 c = *reinterpret_cast<const float4*>(e.wscale + n);
+            sw[0] = c.x; sw[1] = c.y; sw[2] = c.z; sw[3] = c.w;
+        }
+        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const bool has_bias = e.bias != nullptr;
+        if (has_bias) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(e.bias + n);
+            b[0] = bf16_lo(bb.x); b[1] = bf16_hi(bb.x); b[2] = bf16_lo(bb.y); b[3] = bf16_hi(bb.y);
+        }
+        const int a[4] = {a0, a1, a2, a3};
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = (float)a[j] * sxm;
+            v[j] = v[j] * sw[j];
+            if (has_bias) v[j] = v[j] + b[j];
+        }
+        *reinterpret_cast<uint2*>(e.y + (size_t)m * N + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     } else {
-        const float sw0 = (WK == WK_W4A8) ? 0.0f : e.wscale[0];
-        auto one = [&](int a, int nn) -> uint32_t {
-            nn = nn < N ? nn : N - 1;
-            float v = (float)a * sxm;
-            v = v * ((WK == WK_W4A8) ? e.wscale[nn] : sw0);
-            if (e.bias != nullptr) v = v + bf16_to_f32(e.bias[nn]);
-            return f32_to_bf16_rne(v);
-        };
-        const uint32_t h0 = one(a0, n), h1 = one(a1, n + 1), h2 = one(a2, n + 2), h3 = one(a3, n + 3);
-        uint16_t* dst = e.y + (size_t)m * N + n;
-        if ((N & 3) == 0) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        } else {
-            dst[0] = (uint16_t)h0;
-            if (n + 1 < N) dst[1] = (uint16_t)h1;
-            if (n + 2 < N) dst[2] = (uint16_t)h2;
-            if (n + 3 < N) dst[3] = (uint16_t)h3;
+        const int a[4] = {a0, a1, a2, a3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int nn = n + j;
+            if (nn < N) {
+                float v = (float)a[j] * sxm;
+                v = v * ((WK == WK_W4A8) ? e.wscale[nn] : sw0);
+                if (e.bias != nullptr) v = v + bf16_to_f32(e.bias[nn]);
+                e.y[(size_t)m * N + nn] = (uint16_t)f32_to_bf16_rne(v);
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Large-M kernel.  Block tile BM (activations) x BN (weights), 64-k stages.
-// Activation tiles go through double-buffered LDS; each wave streams its
-// weight tiles straight from global memory into registers (the packed layout
-// gives every lane its operand bytes in one 16-byte load) one stage ahead.
+// Large-M kernel.  Block tile 256 activation rows x 256 weight rows, 8 waves
+// (2 along m x 4 along n, 128 x 64 each), 64-k stages in a 4-deep LDS ring.
+// Stages are filled with direct-to-LDS loads (global_load_lds_dwordx4: lane i
+// of a wave writes its 16 bytes at base + 16 i), issued three stages ahead,
+// so no registers hold data in flight.  LDS layouts are XOR-swizzled so the
+// MFMA operand reads (ds_read_b128, 16 consecutive lanes = 16 rows) hit 16
+// distinct 16-byte bank groups:
+//   activations / int8 weights: row r (64 B) at r*64, 16-byte chunk c at
+//     slot c ^ ((r >> 2) & 3);
+//   packed 4-bit weights: 1 KiB tile of 32 rows, row r half h at slot
+//     2r + (h ^ ((r >> 3) & 1)).
 // ---------------------------------------------------------------------------
-template <int WK, int BM, int BN, int WM, int WN, bool ACC>
-__global__ void __launch_bounds__(64 * WM * WN, 2) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n) {
-    constexpr int NT = 64 * WM * WN;
-    constexpr int FM = BM / WM / 32, FN = BN / WN / 32;
-    constexpr int CA = BM * 4 / NT;
-    static_assert(CA * NT == BM * 4, "activation tile split");
-    __shared__ __attribute__((aligned(16))) int8_t sA[2 * BM * LDA];
-    __shared__ uint4 sT[WK == WK_W4A8 ? 256 : 1];
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WM, wn = wave / WM;
+// global_load_lds_dwordx4 issued from inline asm: the compiler does not see
+// it as an LDS write, so it inserts no vmcnt(0) before later LDS reads (the
+// stage ring makes them independent); completion is tracked with explicit
+// wait_vmcnt<> before the barrier that publishes a stage.  The instruction
+// has no register result; M0 (the wave's LDS base) is set in the same block.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(l), "v"(g) : "m0");
+}
 
-    // Block -> tile: blocks are dealt to the 8 XCDs round-robin; give each XCD
-    // a contiguous run of tiles, ordered in bands of 8 tile-rows.
-    const int total = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, per = total >> 3, rem = total & 7;
-    const int lid = xcd * per + (xcd < rem ? xcd : rem) + (bid >> 3);
-    constexpr int GM = 8;
-    const int band = lid / (GM * tiles_n);
-    const int first_m = band * GM;
-    const int gm = min(tiles_m - first_m, GM);
-    const int in_band = lid - band * GM * tiles_n;
-    const int tm = first_m + in_band % gm;
-    const int tn = in_band / gm;
-    const int m0 = tm * BM, n0 = tn * BN;
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero without touching memory.  Word 3 selects 32-bit untyped data.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    v4i r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes at offset voff + soff of the
+// resource go to LDS address lds + 16 i (same inline-asm reasoning as
+// lds_dma16).
+__device__ __forceinline__ void buf_lds16(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 : : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+template <int V> struct IntC { static constexpr int value = V; };
+
+// Workgroup barrier without the memory fence of __syncthreads(): LDS data
+// written by this workgroup's direct-to-LDS loads is published by waiting
+// for them (wait_vmcnt) before the barrier.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N) (N < 64), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+constexpr int BIG_BM = 256;
+
+// NW waves (2 along m x NW/2 along n, 128 x 64 each), block tile 256 x 32*NW,
+// NS-stage LDS ring.
+template <int WK, int NW, int NS>
+struct BigCfg {
+    static constexpr int BN = 32 * NW;
+    static constexpr int A_BYTES = BIG_BM * 64;                       // activations per stage
+    static constexpr int B_BYTES = WK == WK_I8 ? BN * 64 : BN * 32;
+    static constexpr int C_BYTES = WK == WK_W4A8 ? BN * 4 : 0;        // W4A8 scale codes
+    static constexpr int STAGE = A_BYTES + B_BYTES + C_BYTES;
+    static constexpr int LA = 16 / NW;                                 // activation loads per wave
+    // direct-to-LDS loads per wave per stage
+    static constexpr int LPS = LA + (WK == WK_I8 ? 2 : 1) + (WK == WK_W4A8 ? 1 : 0);
+    static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0);
+};
+
+template <int WK, int NW, int NS, bool ACC>
+__global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n) {
+    using C = BigCfg<WK, NW, NS>;
+    constexpr int BN = C::BN;
+    constexpr int FM = 4, FN = 2;
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+    int8_t* ring = smem;
+    uint4* sT = reinterpret_cast<uint4*>(smem + NS * C::STAGE);   // W4A8 decode table
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    const int wm = wave & 1, wn = wave >> 1;
+    const int h = lane >> 5, l32 = lane & 31;
 
     const int M = p.M, Kp = p.Kp;
     const int nkc = Kp >> 6;
@@ -158,32 +232,100 @@ __global__ void __launch_bounds__(64 * WM * WN, 2) k_gemm_big(GemmArgs p, int ti
     const size_t codes_off = w4a8_codes_offset(p.N, p.K);
     if constexpr (WK == WK_W4A8) {
         const uint4* tg = reinterpret_cast<const uint4*>(p.wp + w4a8_table_offset(p.N, p.K));
-        for (int i = tid; i < 256; i += NT) sT[i] = tg[i];
+        for (int i = tid; i < 256; i += 64 * NW) sT[i] = tg[i];
+        __syncthreads();
     }
 
-    int nbs[FN];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) nbs[f] = min((n0 >> 5) + wn * FN + f, nbmax);
+    // Persistent blocks: block b handles tiles b, b + G, b + 2G, ...  Blocks
+    // are dealt to the 8 XCDs round-robin, so within each round the blocks
+    // of one XCD take a contiguous run of tile ids (bands of 8 tile-rows),
+    // which keeps the operands they share in that XCD's L2.
+    const int total = tiles_m * tiles_n;
+    const int G = gridDim.x, bid = blockIdx.x;
+    // slot: a permutation of 0..G-1; tile id j*G + slot for round j, so every
+    // tile id below `total` belongs to exactly one (block, round)
+    const int slot = (G & 7) == 0 ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
+    const int my_tiles = (total - slot + G - 1) / G;
+    const int total_stages = my_tiles * nkc;
+    auto tile_origin = [&](int j, int& m0, int& n0) {
+        int lid = j * G + slot;
+        if (lid >= total) lid = total - 1;           // only for the clamped tail re-reads
+        constexpr int GM = 8;
+        const int band = lid / (GM * tiles_n);
+        const int first_m = band * GM;
+        const int gm = min(tiles_m - first_m, GM);
+        const int in_band = lid - band * GM * tiles_n;
+        m0 = (first_m + in_band % gm) * BIG_BM;
+        n0 = (in_band / gm) * BN;
+    };
 
-    uint4 ra[CA];
-    const int8_t* arow[CA];
-    int aoff[CA];
+    // --- stage loads: buffer loads straight to LDS --------------------------
+    // Per tile, one buffer resource per operand starts at the tile's first
+    // row; per lane the offset inside a stage is fixed, and the stage's k
+    // offset goes in the scalar offset.  Rows past M (activations) and tiles
+    // past Np (weights) are outside the resource and load as zero.
+    //   activations: rows 16*(LA*wave + j) + lane/4, chunk (lane%4) ^ swizzle
+    //   weights: tile n0/32 + wave, this lane's row and half (swizzled)
+    constexpr int BSTEP = WK == WK_I8 ? 2048 : 1024;
+    uint32_t a_voff[C::LA];
 #pragma unroll
-    for (int c = 0; c < CA; ++c) {
-        const int idx = tid + c * NT;
-        const int row = idx >> 2, ch = idx & 3;
-        const int m = min(m0 + row, M - 1);
-        arow[c] = p.qx + (size_t)m * Kp + ch * 16;
-        aoff[c] = row * LDA + ch * 16;
+    for (int j = 0; j < C::LA; ++j) {
+        const int row = 16 * (C::LA * wave + j) + (lane >> 2);
+        a_voff[j] = (uint32_t)(row * Kp + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
     }
-
-    WRaw<WK> wr[FN];
+    uint32_t b_voff0, b_voff1;
+    if constexpr (WK == WK_I8) {
+        const int row0 = lane >> 2, row1 = row0 + 16;
+        b_voff0 = (uint32_t)(wave * nkc * BSTEP + row0 * 64 + (((lane & 3) ^ ((row0 >> 2) & 3)) * 16));
+        b_voff1 = (uint32_t)(wave * nkc * BSTEP + row1 * 64 + (((lane & 3) ^ ((row1 >> 2) & 3)) * 16));
+    } else {
+        b_voff0 = (uint32_t)(wave * nkc * BSTEP + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
+        b_voff1 = b_voff0;
+    }
+    const uint32_t c_voff = (uint32_t)(wave * nkc * 128 + (lane & 7) * 16);
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
+    v4i rs_a, rs_b, rs_c;
+    uint32_t soff_a = 0, soff_b = 0, soff_c = 0;
+    int is_tile = 0, is_kc = 0;   // issue cursor
+    auto aim = [&](int j) {       // resources of tile j, stage 0
+        int m0, n0;
+        tile_origin(j, m0, n0);
+        rs_a = make_rsrc(p.qx + (size_t)m0 * Kp, (uint32_t)((size_t)(M - m0) * Kp));
+        const int nb0 = n0 >> 5;
+        const size_t tiles_left = (size_t)(nbmax + 1 - nb0);
+        rs_b = make_rsrc(p.wp + (size_t)nb0 * nkc * BSTEP, (uint32_t)(tiles_left * nkc * BSTEP));
+        if constexpr (WK == WK_W4A8)
+            rs_c = make_rsrc(p.wp + codes_off + (size_t)nb0 * nkc * 128, (uint32_t)(tiles_left * nkc * 128));
+        soff_a = 0; soff_b = 0; soff_c = 0;
+    };
+    aim(0);
+    auto issue_stage = [&](auto BUF) {
+        constexpr int buf = decltype(BUF)::value;
+        const uint32_t st = ring_lds + buf * C::STAGE;
 #pragma unroll
-    for (int c = 0; c < CA; ++c) ra[c] = *reinterpret_cast<const uint4*>(arow[c]);
-#pragma unroll
-    for (int f = 0; f < FN; ++f) load_wraw<WK>(wr[f], p.wp, codes_off, nbs[f], nkc, 0, lane);
-#pragma unroll
-    for (int c = 0; c < CA; ++c) *reinterpret_cast<uint4*>(sA + aoff[c]) = ra[c];
+        for (int j = 0; j < C::LA; ++j) buf_lds16(rs_a, a_voff[j], soff_a, st + 16 * (C::LA * wave + j) * 64);
+        const uint32_t sb = st + C::A_BYTES;
+        if constexpr (WK == WK_I8) {
+            buf_lds16(rs_b, b_voff0, soff_b, sb + wave * 2048);
+            buf_lds16(rs_b, b_voff1, soff_b, sb + wave * 2048 + 1024);
+        } else {
+            buf_lds16(rs_b, b_voff0, soff_b, sb + wave * 1024);
+        }
+        if constexpr (WK == WK_W4A8) {
+            if (lane < 8) buf_lds16(rs_c, c_voff, soff_c, st + C::A_BYTES + C::B_BYTES + wave * 128);
+        }
+        // advance (past the last stage the offsets stay put: the tail
+        // re-reads it into a buffer that is never consumed)
+        if (++is_kc < nkc) {
+            soff_a += 64; soff_b += BSTEP; soff_c += 128;
+        } else if (is_tile + 1 < my_tiles) {
+            ++is_tile;
+            is_kc = 0;
+            aim(is_tile);
+        } else {
+            is_kc = nkc;
+        }
+    };
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -192,75 +334,192 @@ __global__ void __launch_bounds__(64 * WM * WN, 2) k_gemm_big(GemmArgs p, int ti
         for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
-    __syncthreads();
 
-    const int h = lane >> 5;
-    const int arow_lds = (wm * FM * 32 + (lane & 31)) * LDA + 16 * h;
-    for (int kc = 0; kc < nkc; ++kc) {
-        const int cur = kc & 1;
-        WRaw<WK> wc[FN];
+    // per-lane LDS read offsets
+    const int swz = (l32 >> 2) & 3;                 // activation row swizzle (row % 32 == l32)
+    int aoff[2];
 #pragma unroll
-        for (int f = 0; f < FN; ++f) wc[f] = wr[f];
-        // Prefetch the next stage (the last iteration re-reads its own
-        // stage; that copy is written to the idle buffer and never read).
-        const int kn = min(kc + 1, nkc - 1);
+    for (int t = 0; t < 2; ++t) aoff[t] = (wm * 128 + l32) * 64 + (((2 * t + h) ^ swz) * 16);
+    int boff[FN];
 #pragma unroll
-        for (int c = 0; c < CA; ++c) ra[c] = *reinterpret_cast<const uint4*>(arow[c] + kn * 64);
-#pragma unroll
-        for (int f = 0; f < FN; ++f) load_wraw<WK>(wr[f], p.wp, codes_off, nbs[f], nkc, kn, lane);
-        const int8_t* sa = sA + cur * BM * LDA + arow_lds;
-        {
-            v4i bf[FN];
-#pragma unroll
-            for (int f = 0; f < FN; ++f) bf[f] = wfrag<WK, 0>(wc[f], sT, h);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const v4i af = *reinterpret_cast<const v4i*>(sa + i * 32 * LDA);
-#pragma unroll
-                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bf[f], af, acc[i][f]);
-            }
-        }
-        {
-            v4i bf[FN];
-#pragma unroll
-            for (int f = 0; f < FN; ++f) bf[f] = wfrag<WK, 1>(wc[f], sT, h);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const v4i af = *reinterpret_cast<const v4i*>(sa + i * 32 * LDA + 32);
-#pragma unroll
-                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bf[f], af, acc[i][f]);
-            }
-        }
-        {
-            int8_t* dst = sA + (cur ^ 1) * BM * LDA;
-#pragma unroll
-            for (int c = 0; c < CA; ++c) *reinterpret_cast<uint4*>(dst + aoff[c]) = ra[c];
-        }
-        __syncthreads();
+    for (int f = 0; f < FN; ++f) {
+        const int tile = wn * FN + f;
+        if constexpr (WK == WK_I8) boff[f] = tile * 2048 + l32 * 64;
+        else boff[f] = tile * 1024 + (2 * l32 + (h ^ ((l32 >> 3) & 1))) * 16;
     }
 
-    // Epilogue.
+    // Weight operand bytes of one stage (both MFMA steps) and their decode.
+    struct WStage { uint4 a, b; uint32_t codes; };
+    auto read_w = [&](const int8_t* st, int f) -> WStage {
+        WStage w;
+        const int8_t* sb = st + C::A_BYTES;
+        if constexpr (WK == WK_I8) {
+            w.a = *reinterpret_cast<const uint4*>(sb + boff[f] + (((2 * h + 0) ^ swz) * 16));
+            w.b = *reinterpret_cast<const uint4*>(sb + boff[f] + (((2 * h + 1) ^ swz) * 16));
+        } else {
+            w.a = *reinterpret_cast<const uint4*>(sb + boff[f]);
+        }
+        if constexpr (WK == WK_W4A8)
+            w.codes = *reinterpret_cast<const uint32_t*>(st + C::A_BYTES + C::B_BYTES + (wn * FN + f) * 128 + l32 * 4);
+        return w;
+    };
+    auto wop = [&](const WStage& w, int t) -> v4i {
+        if constexpr (WK == WK_I8) {
+            const uint4 v = t == 0 ? w.a : w.b;
+            v4i r;
+            r.x = (int)v.x; r.y = (int)v.y; r.z = (int)v.z; r.w = (int)v.w;
+            return r;
+        } else if constexpr (WK == WK_W4) {
+            return t == 0 ? unpack_w4x16(w.a.x, w.a.y) : unpack_w4x16(w.a.z, w.a.w);
+        } else {
+            const uint4 tr = sT[(w.codes >> (8 * (2 * t + h))) & 0xFF];
+            return t == 0 ? decode_w4a8(w.a.x, w.a.y, tr) : decode_w4a8(w.a.z, w.a.w, tr);
+        }
+    };
+    auto read_a = [&](const int8_t* st, int t, v4i (&af)[FM]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const v4i*>(st + aoff[t] + i * 32 * 64);
+    };
+
     const Epi epi = make_epi(p);
+    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
+
+    // Pipeline over the block's whole stage stream (its tiles back to back):
+    // stage s lives in ring buffer s % NS and is loaded NS-1 stages ahead.
+    // Inside a stage the fragments of the second MFMA step are read while the
+    // first step's MFMAs run, and the next stage's first-step fragments while
+    // the second step's MFMAs run; a buffer is refilled only after the
+    // barrier that follows the last read of it by every wave.
+    static_assert(NS == 4, "the stage loop is unrolled for a 4-deep ring");
+    issue_stage(IntC<0>{});
+    issue_stage(IntC<1>{});
+    issue_stage(IntC<2>{});
+    wait_vmcnt<(NS - 2) * C::LPS>();
+    lds_barrier();
+    v4i a0[FM], a1[FM];
+    WStage wcur[FN];
+    read_a(ring, 0, a0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * FM * 32 + i * 32 + (lane & 31);
-        if (m < M) {
-            const float sxm = ACC ? 0.0f : p.sx[m];
+    for (int f = 0; f < FN; ++f) wcur[f] = read_w(ring, f);
+
+    int cur_tile = 0, kc = 0;
+    // One stage: buffer B, next stage in (B+1)%4, refill (B+3)%4.
+    auto step = [&](auto BUF) {
+        constexpr int B = decltype(BUF)::value;
+        const int8_t* st = ring + B * C::STAGE;
+        read_a(st, 1, a1);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs they overlap
+        {
+            v4i b0[FN];
 #pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                const int nbase = n0 + (wn * FN + f) * 32 + 4 * h;
+            for (int f = 0; f < FN; ++f) b0[f] = wop(wcur[f], 0);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = nbase + 8 * q;
-                    if (n < p.N)
-                        store4<WK, ACC>(epi, m, n, sxm, fix_acc<WK>(acc[i][f][4 * q + 0]),
-                                        fix_acc<WK>(acc[i][f][4 * q + 1]),
-                                        fix_acc<WK>(acc[i][f][4 * q + 2]),
-                                        fix_acc<WK>(acc[i][f][4 * q + 3]));
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(b0[f], a0[i], acc[i][f]);
+        }
+        v4i b1[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) b1[f] = wop(wcur[f], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // publish the next stage and refill the buffer of the previous one
+        wait_vmcnt<(NS - 3) * C::LPS>();
+        lds_barrier();
+        issue_stage(IntC<(B + 3) % 4>{});
+        const int8_t* sn = ring + ((B + 1) % 4) * C::STAGE;
+        read_a(sn, 0, a0);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) wcur[f] = read_w(sn, f);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(b1[f], a1[i], acc[i][f]);
+
+        if (++kc == nkc) {
+            // Tile done: epilogue while the next tile's stages are in flight.
+            int m0, n0;
+            tile_origin(cur_tile, m0, n0);
+            const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 3) == 0;
+            if (full && !ACC) {
+                // All epilogue operands are loaded up front (one wait), then
+                // every output quad is converted and stored without checks.
+                float sxv[FM];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * 128 + i * 32 + l32];
+#pragma unroll
+                for (int f = 0; f < FN; ++f) {
+                    uint2 bv[4];
+                    float4 cv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
+                        bv[q] = p.bias != nullptr ? *reinterpret_cast<const uint2*>(p.bias + n) : make_uint2(0u, 0u);
+                        if constexpr (WK == WK_W4A8) cv[q] = *reinterpret_cast<const float4*>(p.wscale + n);
+                        else cv[q] = make_float4(sw0, sw0, sw0, sw0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int m = m0 + wm * 128 + i * 32 + l32;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
+                            const float c[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
+                            const float b[4] = {bf16_lo(bv[q].x), bf16_hi(bv[q].x), bf16_lo(bv[q].y), bf16_hi(bv[q].y)};
+                            float v[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                v[j] = (float)fix_acc<WK>(acc[i][f][4 * q + j]) * sxv[i];
+                                v[j] = v[j] * c[j];
+                                if (p.bias != nullptr) v[j] = v[j] + b[j];
+                            }
+                            *reinterpret_cast<uint2*>(p.y + (size_t)m * p.N + n) =
+                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int m = m0 + wm * 128 + i * 32 + l32;
+                    if (m < M) {
+                        const float sxm = ACC ? 0.0f : p.sx[m];
+#pragma unroll
+                        for (int f = 0; f < FN; ++f) {
+                            const int nbase = n0 + (wn * FN + f) * 32 + 4 * h;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int n = nbase + 8 * q;
+                                if (n < p.N)
+                                    store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(acc[i][f][4 * q + 0]),
+                                                    fix_acc<WK>(acc[i][f][4 * q + 1]),
+                                                    fix_acc<WK>(acc[i][f][4 * q + 2]),
+                                                    fix_acc<WK>(acc[i][f][4 * q + 3]));
+                            }
+                        }
+                    }
                 }
             }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int f = 0; f < FN; ++f)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
+            kc = 0;
+            ++cur_tile;
         }
+    };
+    for (int gs = 0; gs < total_stages; gs += 4) {
+        step(IntC<0>{});
+        if (gs + 1 >= total_stages) break;
+        step(IntC<1>{});
+        if (gs + 2 >= total_stages) break;
+        step(IntC<2>{});
+        if (gs + 3 >= total_stages) break;
+        step(IntC<3>{});
     }
+    wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -350,6 +609,7 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits) {
     }
 
     const Epi epi = make_epi(p);
+    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
     if (splits == 1) {
         if (!active) return;
 #pragma unroll
@@ -361,7 +621,7 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits) {
                 for (int q = 0; q < 4; ++q) {
                     const int n = nb * 32 + 8 * q + 4 * h;
                     if (n < N)
-                        store4<WK, ACC>(epi, m, n, sxm, fix_acc<WK>(acc[i][4 * q]), fix_acc<WK>(acc[i][4 * q + 1]),
+                        store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(acc[i][4 * q]), fix_acc<WK>(acc[i][4 * q + 1]),
                                         fix_acc<WK>(acc[i][4 * q + 2]), fix_acc<WK>(acc[i][4 * q + 3]));
                 }
             }
@@ -414,8 +674,9 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs p, int splits, i
         a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
     }
     const Epi epi = make_epi(p);
+    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
     const float sxm = ACC ? 0.0f : p.sx[m];
-    store4<WK, ACC>(epi, m, n, sxm, fix_acc<WK>(a.x), fix_acc<WK>(a.y), fix_acc<WK>(a.z), fix_acc<WK>(a.w));
+    store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(a.x), fix_acc<WK>(a.y), fix_acc<WK>(a.z), fix_acc<WK>(a.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -455,11 +716,36 @@ static hipError_t launch_skinny_t(const GemmArgs& a, const SkinnyPlan& sp, hipSt
     }
 }
 
+// Large-M configuration: 8 waves (block tile 256 x 256), 4-stage ring (96 KiB
+// of LDS; int8 weights 128 KiB): one persistent block per CU.
+constexpr int BIG_NW = 8, BIG_STAGES = 4;
+
+// Compute units of the current device (cached per device).
+static int num_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <int WK, bool ACC>
 static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
-    constexpr int BM = 256, BN = 128, WM = 2, WN = 2;
-    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    k_gemm_big<WK, BM, BN, WM, WN, ACC><<<dim3(tiles_m * tiles_n), dim3(64 * WM * WN), 0, st>>>(a, tiles_m, tiles_n);
+    using C = BigCfg<WK, BIG_NW, BIG_STAGES>;
+    const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + C::BN - 1) / C::BN;
+    static bool attr_set = false;   // opt in to more than 64 KiB of dynamic LDS (once per process)
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, BIG_STAGES, ACC>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = min(tiles_m * tiles_n, num_cus());
+    k_gemm_big<WK, BIG_NW, BIG_STAGES, ACC><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
