@@ -196,19 +196,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 constexpr int BIG_BM = 256;
+constexpr int BIG_WM = 2;   // waves along m in the large-M kernel (wave tile 128 x 64)
 
-// NW waves (2 along m x NW/2 along n, 128 x 64 each), block tile 256 x 32*NW,
-// NS-stage LDS ring.
+// NW waves (2 along m x NW/2 along n; wave tile 128 x 512/NW), block tile
+// 256 x 256, NS-stage LDS ring.
 template <int WK, int NW, int NS>
 struct BigCfg {
-    static constexpr int BN = 32 * NW;
+    static constexpr int BN = 256;
+    static constexpr int TPW = 8 / NW;                                 // 32-row weight tiles loaded per wave
     static constexpr int A_BYTES = BIG_BM * 64;                       // activations per stage
     static constexpr int B_BYTES = WK == WK_I8 ? BN * 64 : BN * 32;
     static constexpr int C_BYTES = WK == WK_W4A8 ? BN * 4 : 0;        // W4A8 scale codes
     static constexpr int STAGE = A_BYTES + B_BYTES + C_BYTES;
     static constexpr int LA = 16 / NW;                                 // activation loads per wave
     // direct-to-LDS loads per wave per stage
-    static constexpr int LPS = LA + (WK == WK_I8 ? 2 : 1) + (WK == WK_W4A8 ? 1 : 0);
+    static constexpr int LPS = LA + TPW * (WK == WK_I8 ? 2 : 1) + (WK == WK_W4A8 ? 1 : 0);
     static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0);
 };
 
@@ -216,14 +218,17 @@ template <int WK, int NW, int NS, bool ACC>
 __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n) {
     using C = BigCfg<WK, NW, NS>;
     constexpr int BN = C::BN;
-    constexpr int FM = 4, FN = 2;
+    // WM waves along m, NW/WM along n; wave tile (256/WM) x (256*WM/NW)
+    constexpr int WM = BIG_WM, WNW = NW / WM;
+    constexpr int WROWS = BIG_BM / WM;
+    constexpr int FM = WROWS / 32, FN = 8 / WNW;
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
     int8_t* ring = smem;
     uint4* sT = reinterpret_cast<uint4*>(smem + NS * C::STAGE);   // W4A8 decode table
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int h = lane >> 5, l32 = lane & 31;
 
     const int M = p.M, Kp = p.Kp;
@@ -273,16 +278,20 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         const int row = 16 * (C::LA * wave + j) + (lane >> 2);
         a_voff[j] = (uint32_t)(row * Kp + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
     }
-    uint32_t b_voff0, b_voff1;
-    if constexpr (WK == WK_I8) {
-        const int row0 = lane >> 2, row1 = row0 + 16;
-        b_voff0 = (uint32_t)(wave * nkc * BSTEP + row0 * 64 + (((lane & 3) ^ ((row0 >> 2) & 3)) * 16));
-        b_voff1 = (uint32_t)(wave * nkc * BSTEP + row1 * 64 + (((lane & 3) ^ ((row1 >> 2) & 3)) * 16));
-    } else {
-        b_voff0 = (uint32_t)(wave * nkc * BSTEP + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
-        b_voff1 = b_voff0;
+    uint32_t b_voff[C::TPW][2];
+#pragma unroll
+    for (int t = 0; t < C::TPW; ++t) {
+        const uint32_t tb = (uint32_t)((wave * C::TPW + t) * nkc * BSTEP);
+        if constexpr (WK == WK_I8) {
+            const int row0 = lane >> 2, row1 = row0 + 16;
+            b_voff[t][0] = tb + row0 * 64 + (((lane & 3) ^ ((row0 >> 2) & 3)) * 16);
+            b_voff[t][1] = tb + row1 * 64 + (((lane & 3) ^ ((row1 >> 2) & 3)) * 16);
+        } else {
+            b_voff[t][0] = tb + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16);
+            b_voff[t][1] = b_voff[t][0];
+        }
     }
-    const uint32_t c_voff = (uint32_t)(wave * nkc * 128 + (lane & 7) * 16);
+    const uint32_t c_voff = (uint32_t)((wave * C::TPW + (lane >> 3)) * nkc * 128 + (lane & 7) * 16);
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
     v4i rs_a, rs_b, rs_c;
     uint32_t soff_a = 0, soff_b = 0, soff_c = 0;
@@ -305,14 +314,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
         for (int j = 0; j < C::LA; ++j) buf_lds16(rs_a, a_voff[j], soff_a, st + 16 * (C::LA * wave + j) * 64);
         const uint32_t sb = st + C::A_BYTES;
-        if constexpr (WK == WK_I8) {
-            buf_lds16(rs_b, b_voff0, soff_b, sb + wave * 2048);
-            buf_lds16(rs_b, b_voff1, soff_b, sb + wave * 2048 + 1024);
-        } else {
-            buf_lds16(rs_b, b_voff0, soff_b, sb + wave * 1024);
+#pragma unroll
+        for (int t = 0; t < C::TPW; ++t) {
+            const uint32_t dst = sb + (wave * C::TPW + t) * BSTEP;
+            buf_lds16(rs_b, b_voff[t][0], soff_b, dst);
+            if constexpr (WK == WK_I8) buf_lds16(rs_b, b_voff[t][1], soff_b, dst + 1024);
         }
         if constexpr (WK == WK_W4A8) {
-            if (lane < 8) buf_lds16(rs_c, c_voff, soff_c, st + C::A_BYTES + C::B_BYTES + wave * 128);
+            if (lane < 8 * C::TPW) buf_lds16(rs_c, c_voff, soff_c, st + C::A_BYTES + C::B_BYTES + wave * C::TPW * 128);
         }
         // advance (past the last stage the offsets stay put: the tail
         // re-reads it into a buffer that is never consumed)
@@ -339,7 +348,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     const int swz = (l32 >> 2) & 3;                 // activation row swizzle (row % 32 == l32)
     int aoff[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) aoff[t] = (wm * 128 + l32) * 64 + (((2 * t + h) ^ swz) * 16);
+    for (int t = 0; t < 2; ++t) aoff[t] = (wm * WROWS + l32) * 64 + (((2 * t + h) ^ swz) * 16);
     int boff[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
@@ -390,51 +399,49 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     // first step's MFMAs run, and the next stage's first-step fragments while
     // the second step's MFMAs run; a buffer is refilled only after the
     // barrier that follows the last read of it by every wave.
-    static_assert(NS == 4, "the stage loop is unrolled for a 4-deep ring");
+    static_assert(NS == 4 || NS == 6, "ring depth (even: register sets alternate per stage)");
+    // Fragments of one stage: activation operands of both MFMA steps and the
+    // weight bytes.  Two sets alternate: while the MFMAs of stage s run from
+    // one set, the reads of stage s+1 land in the other.
+    struct Frags { v4i a[2][FM]; WStage w[FN]; };
+    auto read_frags = [&](const int8_t* st, Frags& F) {
+        read_a(st, 0, F.a[0]);
+        read_a(st, 1, F.a[1]);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) F.w[f] = read_w(st, f);
+    };
     issue_stage(IntC<0>{});
     issue_stage(IntC<1>{});
     issue_stage(IntC<2>{});
+    if constexpr (NS > 4) { issue_stage(IntC<3>{}); issue_stage(IntC<4>{}); }
     wait_vmcnt<(NS - 2) * C::LPS>();
     lds_barrier();
-    v4i a0[FM], a1[FM];
-    WStage wcur[FN];
-    read_a(ring, 0, a0);
-#pragma unroll
-    for (int f = 0; f < FN; ++f) wcur[f] = read_w(ring, f);
+    Frags F0, F1;
+    read_frags(ring, F0);
 
     int cur_tile = 0, kc = 0;
-    // One stage: buffer B, next stage in (B+1)%4, refill (B+3)%4.
+    // One stage in buffer B: publish stage B+1 (and free the buffer of the
+    // previous stage), refill it, read the next stage's fragments into the
+    // other register set, then run this stage's 16 MFMAs back to back.
     auto step = [&](auto BUF) {
         constexpr int B = decltype(BUF)::value;
-        const int8_t* st = ring + B * C::STAGE;
-        read_a(st, 1, a1);
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs they overlap
-        {
-            v4i b0[FN];
+        Frags& cur = (B & 1) ? F1 : F0;
+        Frags& nxt = (B & 1) ? F0 : F1;
+        wait_vmcnt<(NS - 3) * C::LPS>();
+        lds_barrier();
+        issue_stage(IntC<(B + NS - 1) % NS>{});
+        read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
+        __builtin_amdgcn_sched_barrier(0);   // the next stage's reads go out before the MFMAs
 #pragma unroll
-            for (int f = 0; f < FN; ++f) b0[f] = wop(wcur[f], 0);
+        for (int t = 0; t < 2; ++t) {
+            v4i bt[FN];
+#pragma unroll
+            for (int f = 0; f < FN; ++f) bt[f] = wop(cur.w[f], t);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(b0[f], a0[i], acc[i][f]);
+                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bt[f], cur.a[t][i], acc[i][f]);
         }
-        v4i b1[FN];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) b1[f] = wop(wcur[f], 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // publish the next stage and refill the buffer of the previous one
-        wait_vmcnt<(NS - 3) * C::LPS>();
-        lds_barrier();
-        issue_stage(IntC<(B + 3) % 4>{});
-        const int8_t* sn = ring + ((B + 1) % 4) * C::STAGE;
-        read_a(sn, 0, a0);
-#pragma unroll
-        for (int f = 0; f < FN; ++f) wcur[f] = read_w(sn, f);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(b1[f], a1[i], acc[i][f]);
 
         if (++kc == nkc) {
             // Tile done: epilogue while the next tile's stages are in flight.
@@ -446,7 +453,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 // every output quad is converted and stored without checks.
                 float sxv[FM];
 #pragma unroll
-                for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * 128 + i * 32 + l32];
+                for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * WROWS + i * 32 + l32];
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     uint2 bv[4];
@@ -460,7 +467,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                     }
 #pragma unroll
                     for (int i = 0; i < FM; ++i) {
-                        const int m = m0 + wm * 128 + i * 32 + l32;
+                        const int m = m0 + wm * WROWS + i * 32 + l32;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
@@ -481,7 +488,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             } else {
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
-                    const int m = m0 + wm * 128 + i * 32 + l32;
+                    const int m = m0 + wm * WROWS + i * 32 + l32;
                     if (m < M) {
                         const float sxm = ACC ? 0.0f : p.sx[m];
 #pragma unroll
@@ -510,7 +517,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             ++cur_tile;
         }
     };
-    for (int gs = 0; gs < total_stages; gs += 4) {
+    for (int gs = 0; gs < total_stages; gs += NS) {
         step(IntC<0>{});
         if (gs + 1 >= total_stages) break;
         step(IntC<1>{});
@@ -518,6 +525,12 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         step(IntC<2>{});
         if (gs + 3 >= total_stages) break;
         step(IntC<3>{});
+        if constexpr (NS > 4) {
+            if (gs + 4 >= total_stages) break;
+            step(IntC<4 % NS>{});
+            if (gs + 5 >= total_stages) break;
+            step(IntC<5 % NS>{});
+        }
     }
     wait_vmcnt<0>();
 }
@@ -716,9 +729,11 @@ static hipError_t launch_skinny_t(const GemmArgs& a, const SkinnyPlan& sp, hipSt
     }
 }
 
-// Large-M configuration: 8 waves (block tile 256 x 256), 4-stage ring (96 KiB
-// of LDS; int8 weights 128 KiB): one persistent block per CU.
-constexpr int BIG_NW = 8, BIG_STAGES = 4;
+// Large-M configuration: 8 waves (block tile 256 x 256), one persistent block
+// per CU; ring depth 6 for 4-bit weights (144 KiB of LDS; W4A8 154 KiB with
+// its table), 4 for int8 weights (128 KiB).
+constexpr int BIG_NW = 8;
+template <int WK> constexpr int big_stages() { return WK == WK_I8 ? 4 : 6; }
 
 // Compute units of the current device (cached per device).
 static int num_cus() {
@@ -735,17 +750,18 @@ static int num_cus() {
 
 template <int WK, bool ACC>
 static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
-    using C = BigCfg<WK, BIG_NW, BIG_STAGES>;
+    constexpr int NS = big_stages<WK>();
+    using C = BigCfg<WK, BIG_NW, NS>;
     const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + C::BN - 1) / C::BN;
     static bool attr_set = false;   // opt in to more than 64 KiB of dynamic LDS (once per process)
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, BIG_STAGES, ACC>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int grid = min(tiles_m * tiles_n, num_cus());
-    k_gemm_big<WK, BIG_NW, BIG_STAGES, ACC><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n);
+    k_gemm_big<WK, BIG_NW, NS, ACC><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
