@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POPS
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 COLD_COPIES = 48
+COPY_BYTES = 512 << 20         # plain device copy used to calibrate the HBM byte counters
 
 
 def _log(msg):
@@ -134,8 +135,11 @@ class Layer:
             (self.N * 2 if self.bias is not None else 0)
 
 
-def graph_time_us(torch, fn_list, iters):
-    """Average time per call of the calls in fn_list, replayed as one HIP graph."""
+def graph_time_us(torch, fn_list, min_us=4000.0):
+    """Average time per call of the calls in fn_list, replayed as one HIP graph.
+
+    The graph is replayed until at least min_us of GPU time is timed, so that
+    short kernels are measured over a long enough window."""
     for f in fn_list:          # eager warm-up (first-call checks happen outside capture)
         f()
     torch.cuda.synchronize()
@@ -143,10 +147,16 @@ def graph_time_us(torch, fn_list, iters):
     with torch.cuda.graph(g):
         for f in fn_list:
             f()
-    g.replay()
-    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        g.replay()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    iters = int(min(2000, max(5, min_us // one + 1)))
     e0.record()
     for _ in range(iters):
         g.replay()
@@ -161,10 +171,10 @@ def measure_row(torch, lay: Layer, cold: bool, reps: int):
     n = len(lay.packed)
     calls = max(reps, n)
     out = {}
-    out["linear_us"] = graph_time_us(torch, [lambda i=i: lay.linear(i % n) for i in range(calls)], 5)
+    out["linear_us"] = graph_time_us(torch, [lambda i=i: lay.linear(i % n) for i in range(calls)])
     lay.quant()
-    out["gemm_us"] = graph_time_us(torch, [lambda i=i: lay.gemm(i % n) for i in range(calls)], 5)
-    out["quant_us"] = graph_time_us(torch, [lay.quant for _ in range(reps)], 5)
+    out["gemm_us"] = graph_time_us(torch, [lambda i=i: lay.gemm(i % n) for i in range(calls)])
+    out["quant_us"] = graph_time_us(torch, [lay.quant for _ in range(reps)])
     out["linear_tops"] = lay.ops() / (out["linear_us"] * 1e-6) / 1e12
     out["gemm_tops"] = lay.ops() / (out["gemm_us"] * 1e-6) / 1e12
     out["gemm_frac_int8_peak"] = out["gemm_tops"] / PEAK_INT8_TOPS
@@ -181,7 +191,9 @@ def measure_row(torch, lay: Layer, cold: bool, reps: int):
 # CPU baseline: the oracle on a row sample of the headline layer
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(L, rows: int):
+def cpu_baseline(L, rows: int, min_seconds: float = 10.0):
+    """The oracle on blocks of `rows` rows of the headline layer, taken in turn
+    (wrapping around) until at least min_seconds of CPU time have been spent."""
     from oracle import convrot_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -189,19 +201,28 @@ def cpu_baseline(L, rows: int):
     except Exception:
         threads = os.cpu_count() or 1
     qw, sw = O.quant_weight_w4(L.w)           # offline weight preparation: not timed
-    xs = L.x[:rows]
     bias = L.bias
+    done_rows = 0
+    blocks = 0
     t0 = time.perf_counter()
-    qx, sx = O.quant_act_w4a4(xs)
-    acc = O.int_gemm(qx, qw)
-    O.epilogue(acc, sx, sw, bias)
-    dt = time.perf_counter() - t0
-    ops = 2.0 * rows * L.N * L.K
+    while True:
+        r0 = (blocks * rows) % L.M
+        xs = L.x[r0:r0 + rows]
+        qx, sx = O.quant_act_w4a4(xs)
+        acc = O.int_gemm(qx, qw)
+        O.epilogue(acc, sx, sw, bias)
+        done_rows += xs.shape[0]
+        blocks += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt > 30.0:
+            break
+    ops = 2.0 * done_rows * L.N * L.K
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"DiT W1 W4A4 linear, first {rows} of {L.M} rows (K={L.K}, N={L.N}); "
-                      "rotation+quantisation of x, exact integer GEMM (float64 BLAS), epilogue; "
-                      "weight preparation excluded (offline on both sides)"}
+            "seconds": round(dt, 3),
+            "sample": f"DiT W1 W4A4 linear (K={L.K}, N={L.N}), {blocks} blocks of {rows} rows "
+                      f"({done_rows} rows, the {L.M}-row input taken in turn); rotation+quantisation of x, "
+                      "exact integer GEMM (float64 BLAS), epilogue; weight preparation excluded "
+                      "(offline on both sides)"}
 
 
 def load_traffic(kernel_hash: str):
@@ -225,6 +246,9 @@ def main():
     ap.add_argument("--rows", default="all", help="all | none | comma-separated row names")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the headline GEMM 5 times and a 512 MiB device copy 5 times "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -246,6 +270,21 @@ def main():
     _log("generating DiT W1 inputs")
     Lh = specs["dit_w1"]["gen"]()
     head = Layer(crp, torch, Lh, 0)
+
+    if args.traffic_probe:
+        head.quant()
+        for _ in range(5):
+            head.gemm()
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "gemm_launches": 5, "copy_launches": 5,
+                          "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                          "gemm_algorithmic_bytes": head.gemm_bytes()}), flush=True)
+        return
 
     # --- headline: K timed steps of the whole linear -----------------------
     for _ in range(args.warmup):

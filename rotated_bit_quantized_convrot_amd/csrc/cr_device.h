@@ -96,6 +96,89 @@ __device__ __forceinline__ void fwht256(float (&v)[8], int lane32) {
     for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.0625f;
 }
 
+// Rotation of one 256-block held by 16 lanes, lane j holding elements
+// 16j..16j+15 in v[0..15]: strides 1, 2, 4, 8 inside the lane, then 16, 32,
+// 64, 128 across lanes (lane bits 0..3), with no final 1/16 (the caller
+// folds it into the scale).
+//
+// Cross-lane stages keep a per-lane sign: a lane holds sigma * (true value)
+// with sigma = (-1)^(number of cross stages in which it was the upper lane).
+// Before the stage on lane bit b both partners have the same sigma, so with
+// own value w and partner value p every lane computes fma(p, c, w), c = +1 in
+// the lower lane (sigma (a + b)) and -1 in the upper lane (sigma (b - a) =
+// -sigma (a - b)): one instruction per value and stage, and since rounding
+// is symmetric the magnitudes are bitwise those of the plain butterflies
+// (a zero may carry the other sign, which no later add can tell apart).
+// On return sigma = (-1)^popcount(lane & 15).  All 16 lanes of each row
+// must be active.
+#define CR_FMAC_DPP16(CTRL)                                                                   \
+    asm("s_nop 1\n\t"                                                                           \
+        "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
+        "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+        "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+        "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+        "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+        "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                  \
+        "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf"                      \
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),    \
+          "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]),            \
+          "+v"(v[13]), "+v"(v[14]), "+v"(v[15])                                                  \
+        : "v"(c))
+
+// One cross-lane stage: v[i] = v[i] + c * v[i] of lane ^ MASK.  Masks 1, 2
+// and 8 are one v_fmac_f32_dpp per value (quad_perm / row_ror:8, all source
+// lanes inside the 16-lane row); the leading s_nop gives the two wait states
+// a DPP read needs after a VALU write of its source, and inside the block
+// each source was written 16 instructions earlier.  Mask 4 goes through
+// ds_swizzle.
+template <int MASK>
+__device__ __forceinline__ void fwht_cross16(float (&v)[16], int lane) {
+    const float c = (lane & MASK) ? -1.0f : 1.0f;
+    if constexpr (MASK == 1) {
+        CR_FMAC_DPP16("quad_perm:[1,0,3,2]");
+    } else if constexpr (MASK == 2) {
+        CR_FMAC_DPP16("quad_perm:[2,3,0,1]");
+    } else if constexpr (MASK == 8) {
+        CR_FMAC_DPP16("row_ror:8");
+    } else {
+        static_assert(MASK == 4, "fwht_cross16 mask");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(lane_xor<4>(v[i]), c, v[i]);
+    }
+}
+
+__device__ __forceinline__ void fwht256_x16_signed(float (&v)[16], int lane) {
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+    fwht_cross16<1>(v, lane);
+    fwht_cross16<2>(v, lane);
+    fwht_cross16<4>(v, lane);
+    fwht_cross16<8>(v, lane);
+}
+
+// The sign sigma that fwht256_x16_signed leaves in a lane.
+__device__ __forceinline__ float fwht_x16_sign(int lane) {
+    return (__builtin_popcount(lane & 15) & 1) ? -1.0f : 1.0f;
+}
+
 // Symmetric code of v with scale s (IEEE division, round half to even).
 template <int LO, int HI>
 __device__ __forceinline__ int quant_code(float v, float s) {

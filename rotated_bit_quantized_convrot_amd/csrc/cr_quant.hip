@@ -64,30 +64,129 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xFF) << 24);
 }
 
+// Max over the `seg` lanes (16, 32 or 64; aligned) of each lane's segment.
+__device__ __forceinline__ float seg_max(float a, int seg) {
+    a = fmaxf(a, lane_xor<1>(a));
+    a = fmaxf(a, lane_xor<2>(a));
+    a = fmaxf(a, lane_xor<4>(a));
+    a = fmaxf(a, lane_xor<8>(a));
+    if (seg >= 32) a = fmaxf(a, lane_xor<16>(a));
+    if (seg >= 64) a = fmaxf(a, __shfl_xor(a, 32, 64));
+    return a;
+}
+
+// Four codes (int, -128..127) -> one dword, first code in the low byte.
+__device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
+    const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
 // Rotated activations: codes [M, K] int8 (natural order) and scales [M].
+//
+// Each row is handled by a segment of lanes: 16 lanes per 256-group, each
+// lane 16 consecutive values.  seg_log2 >= 0: segments of 2^seg_log2 <= 64
+// lanes, 256 / 2^seg_log2 rows per block; seg_log2 < 0: one row per block
+// (GPL groups per lane, strided by the block's group count).
+//
+// The butterflies run on the unscaled values (sign-tracked, see
+// fwht256_x16_signed); the 1/16 of the rotation is folded into the scale.
+// With amax_u the row's max |value| before the 1/16, the stored scale is
+// s = fl(fl(amax_u / 16) / QMAX), and for 2^-100 <= amax_u <= 2^100 the code
+// fl(v/16 / s) equals fl(v / s_u), s_u = fl(amax_u / QMAX): scaling by 2^-4
+// commutes with rounding away from the subnormal range, and values too small
+// for that have code 0 either way.  That quotient is taken as v * fl(1/s_u):
+// the product is within QMAX * 2^-22.9 of v / s_u and the correctly rounded
+// quotient within half an ulp (< QMAX * 2^-23), so both round to the same
+// integer unless v / s_u lies within QMAX * 2^-20 of a half-integer; a lane
+// whose 16 products come that close redoes them with the division.  |v/s_u|
+// <= QMAX (1 + 2^-23) keeps the fast codes inside [LO, HI].  Rows outside
+// the range take the literal path.
 template <int GPL, int QMAX, int LO, int HI>
-__global__ void __launch_bounds__(512) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
-                                                       int8_t* __restrict__ qx,
-                                                       float* __restrict__ sx) {
+__global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
+                                                        int seg_log2, int8_t* __restrict__ qx,
+                                                        float* __restrict__ sx) {
     __shared__ float red[16];
-    const int m = blockIdx.x;
-    const int G = K >> 8;
-    const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
-    RotRow<GPL> r;
-    const float amax = block_max(r.load_rotate(x + (size_t)m * K, G, hw, nhw, lane32), red);
-    const float s = amax / (float)QMAX;
-    if (threadIdx.x == 0) sx[m] = s;
+    const int tid = threadIdx.x;
+    int m, l, seg;
+    if (seg_log2 >= 0) {
+        seg = 1 << seg_log2;
+        m = blockIdx.x * (blockDim.x >> seg_log2) + (tid >> seg_log2);
+        l = tid & (seg - 1);
+    } else {
+        seg = blockDim.x;
+        m = blockIdx.x;
+        l = tid;
+    }
+    const int G = K >> 8, gslot = l >> 4, gstride = seg >> 4, j = l & 15;
+    const bool row_ok = m < M;
+
+    float v[GPL][16];
+    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-        const int g = hw + i * nhw;
-        if (g < G) {
-            int q[8];
+        const int g = gslot + i * gstride;
+        if (row_ok && g < G) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)g * 256 + j * 16);
+            const uint4 r0 = src[0], r1 = src[1];
+            const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = quant_code<LO, HI>(r.v[i][j], s);
-            uint2 o;
-            o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-            o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-            *reinterpret_cast<uint2*>(qx + (size_t)m * K + (size_t)g * 256 + lane32 * 8) = o;
+            for (int t = 0; t < 8; ++t) {
+                v[i][2 * t] = bf16_lo(w[t]);
+                v[i][2 * t + 1] = bf16_hi(w[t]);
+            }
+            fwht256_x16_signed(v[i], l);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
+        }
+    }
+    amax = seg_max(amax, seg < 64 ? seg : 64);
+    if (seg > 64) {                      // one row per block: across waves
+        const int wave = tid >> 6, nw = blockDim.x >> 6;
+        if ((tid & 63) == 0) red[wave] = amax;
+        __syncthreads();
+        amax = 0.0f;
+        for (int i = 0; i < nw; ++i) amax = fmaxf(amax, red[i]);
+    }
+    if (!row_ok) return;
+
+    const float s = (amax * 0.0625f) / (float)QMAX;
+    if (l == 0) sx[m] = s;
+    const float sigma = fwht_x16_sign(l);
+    const bool fast = amax >= 0x1p-100f && amax <= 0x1p100f;
+    const float s_u = amax / (float)QMAX;
+    const float rinv = sigma * (1.0f / s_u);          // undoes the lane's sign too
+
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = gslot + i * gstride;
+        if (g < G) {
+            float r[16];
+            if (fast) {
+                float dmax = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const float q = v[i][t] * rinv;
+                    r[t] = __builtin_rintf(q);
+                    dmax = fmaxf(dmax, fabsf(q - r[t]));
+                }
+                if (dmax > 0.5f - (float)QMAX * 9.5367431640625e-07f) {   // within QMAX * 2^-20 of a tie
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        const float q = __builtin_rintf((sigma * v[i][t]) / s_u);
+                        r[t] = fminf(fmaxf(q, (float)LO), (float)HI);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[i][t]) * 0.0625f, s);
+            }
+            uint4 o;
+            o.x = pack4_codes((int)r[0], (int)r[1], (int)r[2], (int)r[3]);
+            o.y = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
+            o.z = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
+            o.w = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
+            *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
         }
     }
 }
@@ -147,15 +246,22 @@ static int rot_threads(int G, int* gpl) {
 
 template <int QMAX, int LO, int HI>
 static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, hipStream_t st) {
+    const int T = K / 16;              // lanes per row
+    if (T <= 64) {
+        int lg = 4;
+        while ((1 << lg) < T) ++lg;
+        const int rows = 256 >> lg;
+        k_quant_act_rot<1, QMAX, LO, HI><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx);
+        return hipGetLastError();
+    }
     int gpl = 1;
-    const int threads = rot_threads(K >> 8, &gpl);
+    while ((T + gpl - 1) / gpl > 1024) gpl <<= 1;
+    const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
-        case 8: k_quant_act_rot<8, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
-        case 16: k_quant_act_rot<16, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, qx, sx); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -39,6 +39,7 @@ KIND_ORACLE_ACT = {
 
 ACT_CASES = [
     (0, 64, 512), (0, 76, 2560), (0, 33, 9728), (0, 3, 256), (0, 5, 12288), (0, 2, 65536),
+    (0, 33, 512), (0, 17, 768), (0, 9, 1024), (0, 7, 1280), (0, 3, 32768), (0, 300, 3072),
     (1, 64, 2688), (1, 9, 100), (1, 17, 3072), (1, 1, 7),
     (2, 40, 3840), (2, 3, 256),
 ]
@@ -51,6 +52,62 @@ def test_quant_act_bitexact(crp, kind, M, K):
     if M >= 3:
         x[1, :] = 0                                  # zero row
         x[2, :] = si.f32_to_bf16_bits(np.full(K, 0.75, np.float32))   # constant row
+    q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
+    _sync()
+    q_ref, s_ref = KIND_ORACLE_ACT[kind](x)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def _rows_from_rotated(y_rows):
+    """bf16 rows x with rotate(x) == y exactly: x = H y per 256-group (the
+    normalised Sylvester Hadamard is symmetric and its own inverse); asserts
+    that every x is exactly a bf16 value."""
+    H = O.hadamard(256)
+    y = np.asarray(y_rows, np.float64)
+    R, K = y.shape
+    x = (y.reshape(R, K // 256, 256) @ H.T).reshape(R, K)
+    x32 = x.astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), x)
+    bits = si.f32_to_bf16_bits(x32)
+    assert np.array_equal(si.bf16_bits_to_f32(bits).astype(np.float64), x)
+    return bits
+
+
+@pytest.mark.parametrize("kind", [0, 2])
+def test_quant_act_exact_ties(crp, kind):
+    """Rotated values exactly on half-integer multiples of the scale (round
+    half to even decides) next to the row maximum."""
+    qmax = 7 if kind == 0 else 127
+    K = 256 * 8
+    rows = []
+    for e in (-3, 0, 5):
+        y = np.zeros(K)
+        for g in range(8):
+            y[g * 256] = qmax * 2.0 ** e                  # the row maximum: scale 2^e
+            if kind == 0:
+                k = g % 7
+                y[g * 256 + 1 + g] = (-1) ** g * (k + 0.5) * 2.0 ** e
+            else:
+                y[g * 256 + 1 + g] = (-1) ** g * 0.5 * 2.0 ** e
+        rows.append(y)
+    x = _rows_from_rotated(rows)
+    q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
+    _sync()
+    q_ref, s_ref = KIND_ORACLE_ACT[kind](x)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", [0, 2])
+def test_quant_act_extreme_magnitudes(crp, kind):
+    """Rows whose max lies outside [2^-100, 2^100] before the 1/16 (tiny,
+    huge, subnormal bf16) next to ordinary rows."""
+    rng = np.random.default_rng(7)
+    K = 512
+    base = rng.standard_normal((6, K)).astype(np.float32)
+    scales = [1.0, 1e-33, 1e33, 1e-39, 3e-38, 1.0]
+    x = si.f32_to_bf16_bits(base * np.array(scales, np.float32)[:, None])
     q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
     _sync()
     q_ref, s_ref = KIND_ORACLE_ACT[kind](x)
