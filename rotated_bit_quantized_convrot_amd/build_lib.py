@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libconvrot.so")
-SOURCES = ["cr_api.hip", "cr_quant.hip", "cr_gemm.hip"]
+SOURCES = ["cr_api.hip", "cr_quant.hip", "cr_gemm.hip", "cr_gemm_small.hip"]
 ARCH = "gfx950"
 
 

@@ -78,21 +78,24 @@ size_t packed_bytes(int kind, int N, int K) {
 
 int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K; }
 
-// Workspace: [codes M x Kp][scales M][split-K partials].  The codes and
-// scales do not depend on N, so one quantisation can feed GEMMs against
-// several weights (with the workspace sized for the largest N).
+int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8); }
+
+// Workspace: [codes][scales M][split-K partials].  Codes are int8 [M, Kp],
+// or 4-bit packed (round_up(M, 32) x K/2 bytes) for W4A4 at small M.  The
+// codes and scales do not depend on N, so one quantisation can feed GEMMs
+// against several weights (with the workspace sized for the largest N).
 struct WsLayout {
     size_t qx, sx, part, quant_end, total;
 };
 
 WsLayout ws_layout(int kind, int M, int N, int K) {
     WsLayout l{};
-    const int Kp = kp_of(kind, K);
+    const int wk = wkind(kind);
     l.qx = 0;
-    l.sx = a256((size_t)M * Kp);
+    l.sx = a256(cr::act_bytes(wk, M, K));
     l.part = l.sx + a256((size_t)M * 4);
     l.quant_end = l.part;
-    const cr::SkinnyPlan sp = cr::plan_skinny(M, N, K);
+    const cr::SmallPlan sp = cr::plan_small(wk, M, N, K);
     l.total = l.part + a256(sp.use ? sp.part_bytes : 0);
     if (l.total < 256) l.total = 256;
     if (l.quant_end < 256) l.quant_end = 256;
@@ -103,8 +106,6 @@ cr_status launch_err(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return fail(CR_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
-
-int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8); }
 
 cr_status check_m(int M) {
     if (M < 0 || M > CR_MAX_DIM) return fail(CR_ERR_SHAPE, "bad M=%d", M);
@@ -118,7 +119,8 @@ cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.quant_end);
     char* w = static_cast<char*>(ws);
     hipError_t e = cr::launch_quant_act(wkind(kind), static_cast<const uint16_t*>(x), M, K, kp_of(kind, K),
-                                        reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx), st);
+                                        reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
+                                        cr::act_packed(wkind(kind), M, K), st);
     return launch_err(e, "activation quantisation");
 }
 
@@ -306,7 +308,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if ((s = check_device()) != CR_OK) return s;
     const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
     return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
-                                           static_cast<int8_t*>(codes), scales, stream),
+                                           static_cast<int8_t*>(codes), scales, false, stream),
                       "activation quantisation");
 }
 

@@ -232,6 +232,14 @@ __device__ __forceinline__ v4i decode_w4a8(uint32_t p0, uint32_t p1, uint4 trow)
     return r;
 }
 
+// Raw buffer resource over [base, base + bytes) (bytes < 2^31): loads with a
+// per-lane VGPR offset and a wave-uniform SGPR offset; a lane whose offset is
+// past the end reads 0.
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }

@@ -14,6 +14,7 @@
 // the 32x32 int32 result leaves lane l with column m = l%32 and rows
 // n = 8*(r/4) + 4*(l/32) + r%4 for accumulator register r.
 #include "cr_device.h"
+#include "cr_epilogue.h"
 #include "cr_internal.h"
 
 namespace cr {
@@ -65,74 +66,6 @@ template <int WK>
 __device__ __forceinline__ int fix_acc(int v) {
     if constexpr (WK == WK_W4) return v >> 4;
     else return v;
-}
-
-// Epilogue operands, copied out of the kernel arguments.
-struct Epi {
-    const float* wscale;   // tensor scale (1 float) or s_channel [N]
-    const uint16_t* bias;  // [N] or null
-    uint16_t* y;           // [M, N]
-    int32_t* acc_out;      // [M, N] or null
-    int N;
-};
-
-__device__ __forceinline__ Epi make_epi(const GemmArgs& p) {
-    Epi e;
-    e.wscale = p.wscale; e.bias = p.bias; e.y = p.y; e.acc_out = p.acc_out; e.N = p.N;
-    return e;
-}
-
-// Writes 4 consecutive outputs n..n+3 of row m (n % 4 == 0, n < N).
-// sw0: the tensor scale (unused for W4A8, which reads s_channel[n]).
-template <int WK, bool ACC>
-__device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, float sw0, int a0,
-                                       int a1, int a2, int a3) {
-    const int N = e.N;
-    const bool full = (N & 3) == 0;          // n + 3 < N then, rows 8-byte aligned
-    if constexpr (ACC) {
-        int32_t* dst = e.acc_out + (size_t)m * N + n;
-        if (full) {
-            *reinterpret_cast<int4*>(dst) = make_int4(a0, a1, a2, a3);
-        } else {
-            dst[0] = a0;
-            if (n + 1 < N) dst[1] = a1;
-            if (n + 2 < N) dst[2] = a2;
-            if (n + 3 < N) dst[3] = a3;
-        }
-    } else if (full) {
-        float sw[4] = {sw0, sw0, sw0, sw0};
-        if constexpr (WK == WK_W4A8) {
-            const float4 c = *reinterpret_cast<const float4*>(e.wscale + n);
-            sw[0] = c.x; sw[1] = c.y; sw[2] = c.z; sw[3] = c.w;
-        }
-        float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        const bool has_bias = e.bias != nullptr;
-        if (has_bias) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(e.bias + n);
-            b[0] = bf16_lo(bb.x); b[1] = bf16_hi(bb.x); b[2] = bf16_lo(bb.y); b[3] = bf16_hi(bb.y);
-        }
-        const int a[4] = {a0, a1, a2, a3};
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[j] = (float)a[j] * sxm;
-            v[j] = v[j] * sw[j];
-            if (has_bias) v[j] = v[j] + b[j];
-        }
-        *reinterpret_cast<uint2*>(e.y + (size_t)m * N + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    } else {
-        const int a[4] = {a0, a1, a2, a3};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int nn = n + j;
-            if (nn < N) {
-                float v = (float)a[j] * sxm;
-                v = v * ((WK == WK_W4A8) ? e.wscale[nn] : sw0);
-                if (e.bias != nullptr) v = v + bf16_to_f32(e.bias[nn]);
-                e.y[(size_t)m * N + nn] = (uint16_t)f32_to_bf16_rne(v);
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -535,200 +468,6 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     wait_vmcnt<0>();
 }
 
-// ---------------------------------------------------------------------------
-// Small-M kernel (M <= 128).  Block = 4 waves over 128 weight rows (one 32-row
-// tile per wave) and one K slice of at most KSLMAX 64-chunks; the slice of the
-// activations (all rows) is staged in LDS once and shared by the 4 waves.
-// Each wave issues all of its weight loads up front.  With several K slices
-// each block stores its int32 partial sums in accumulator-register order
-// (fully coalesced) and k_splitk_reduce, the next kernel on the stream, adds
-// the slices in order and runs the epilogue: no atomics and no device-scope
-// fences (both cost far more than a second launch here).
-// ---------------------------------------------------------------------------
-constexpr int KSLMAX = 8;
-
-template <int WK, int MF, bool ACC>
-__global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs p, int splits) {
-    constexpr int MR = MF * 32;
-    constexpr int CAMAX = MR * KSLMAX * 4 / 256;
-    __shared__ __attribute__((aligned(16))) int8_t sA[MR * (KSLMAX * 64 + 16)];
-    __shared__ uint4 sT[WK == WK_W4A8 ? 256 : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-    const int bx = blockIdx.x, s = blockIdx.y;
-    const int M = p.M, Kp = p.Kp, N = p.N;
-    const int nkc = Kp >> 6;
-    const int kc0 = (int)((long long)s * nkc / splits);
-    const int kc1 = (int)((long long)(s + 1) * nkc / splits);
-    const int ksl = kc1 - kc0;
-    const int lrow = ksl * 64 + 16;
-    const int nb = bx * 4 + wave;
-    const bool active = nb < (p.Np >> 5);
-    const size_t codes_off = w4a8_codes_offset(p.N, p.K);
-
-    // 1. activation slice -> registers.  Thread chunk idx covers row
-    //    idx / (4*KSLMAX), 16-byte column idx % (4*KSLMAX); columns past the
-    //    slice re-read (and later re-store) the slice's last column, rows
-    //    past M re-read row M-1.  Issued before the weight loads so that the
-    //    wait for them does not wait for the weights.
-    uint4 ra[CAMAX];
-    int aoff[CAMAX];
-#pragma unroll
-    for (int c = 0; c < CAMAX; ++c) {
-        const int idx = tid + c * 256;
-        const int row = idx / (4 * KSLMAX);
-        const int col = min(idx % (4 * KSLMAX), ksl * 4 - 1);
-        const int m = min(row, M - 1);
-        ra[c] = *reinterpret_cast<const uint4*>(p.qx + (size_t)m * Kp + (size_t)kc0 * 64 + col * 16);
-        aoff[c] = row * lrow + col * 16;
-    }
-    // 2. all weight loads of this wave (chunks past the slice re-read its
-    //    last chunk and are not used; idle waves read tile 0)
-    WRaw<WK> wr[KSLMAX];
-    const int nbl = active ? nb : 0;
-#pragma unroll
-    for (int j = 0; j < KSLMAX; ++j) load_wraw<WK>(wr[j], p.wp, codes_off, nbl, nkc, kc0 + min(j, ksl - 1), lane);
-    // 3. activations -> LDS (duplicate chunks store identical bytes)
-#pragma unroll
-    for (int c = 0; c < CAMAX; ++c) *reinterpret_cast<uint4*>(sA + aoff[c]) = ra[c];
-    if constexpr (WK == WK_W4A8) {
-        const uint4* tg = reinterpret_cast<const uint4*>(p.wp + w4a8_table_offset(p.N, p.K));
-        for (int i = tid; i < 256; i += 256) sT[i] = tg[i];
-    }
-    __syncthreads();
-
-    v16i acc[MF];
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
-
-    if (active) {
-        const int8_t* sa = sA + (lane & 31) * lrow + 16 * h;
-#pragma unroll
-        for (int j = 0; j < KSLMAX; ++j) {
-            if (j < ksl) {
-                const v4i b0 = wfrag<WK, 0>(wr[j], sT, h);
-                const v4i b1 = wfrag<WK, 1>(wr[j], sT, h);
-#pragma unroll
-                for (int i = 0; i < MF; ++i) {
-                    const v4i a0 = *reinterpret_cast<const v4i*>(sa + i * 32 * lrow + j * 64);
-                    const v4i a1 = *reinterpret_cast<const v4i*>(sa + i * 32 * lrow + j * 64 + 32);
-                    acc[i] = mfma32(b0, a0, acc[i]);
-                    acc[i] = mfma32(b1, a1, acc[i]);
-                }
-            }
-        }
-    }
-
-    const Epi epi = make_epi(p);
-    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
-    if (splits == 1) {
-        if (!active) return;
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            const int m = i * 32 + (lane & 31);
-            if (m < M) {
-                const float sxm = ACC ? 0.0f : p.sx[m];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = nb * 32 + 8 * q + 4 * h;
-                    if (n < N)
-                        store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(acc[i][4 * q]), fix_acc<WK>(acc[i][4 * q + 1]),
-                                        fix_acc<WK>(acc[i][4 * q + 2]), fix_acc<WK>(acc[i][4 * q + 3]));
-                }
-            }
-        }
-        return;
-    }
-
-    // Split K: this slice's raw MFMA sums, in register order.
-    if (!active) return;
-    int4* dst = reinterpret_cast<int4*>(p.part) + ((((size_t)s * gridDim.x + bx) * 4 + wave) * MF) * 4 * 64 + lane;
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dst[(i * 4 + q) * 64] = make_int4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
-}
-
-// Sum of the K slices' partials (in slice order) + epilogue.  One thread per
-// (column block, wave, fragment, register quad, lane) of k_gemm_skinny.
-template <int WK, int MF, bool ACC>
-__global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs p, int splits, int nblk) {
-    const size_t items = (size_t)nblk * 4 * MF * 4 * 64;
-    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= items) return;
-    const int lane = (int)(id & 63);
-    size_t t = id >> 6;
-    const int q = (int)(t % 4); t /= 4;
-    const int i = (int)(t % MF); t /= MF;
-    const int wave = (int)(t % 4);
-    const int bx = (int)(t / 4);
-    const int nb = bx * 4 + wave;
-    if (nb >= (p.Np >> 5)) return;
-    const int m = i * 32 + (lane & 31);
-    const int n = nb * 32 + 8 * q + 4 * (lane >> 5);
-    if (m >= p.M || n >= p.N) return;
-    const int4* src = reinterpret_cast<const int4*>(p.part) + id;
-    const size_t stride = items;
-    int4 a = make_int4(0, 0, 0, 0);
-    int k = 0;
-    for (; k + 4 <= splits; k += 4) {
-        const int4 v0 = src[(k + 0) * stride], v1 = src[(k + 1) * stride];
-        const int4 v2 = src[(k + 2) * stride], v3 = src[(k + 3) * stride];
-        a.x += v0.x; a.y += v0.y; a.z += v0.z; a.w += v0.w;
-        a.x += v1.x; a.y += v1.y; a.z += v1.z; a.w += v1.w;
-        a.x += v2.x; a.y += v2.y; a.z += v2.z; a.w += v2.w;
-        a.x += v3.x; a.y += v3.y; a.z += v3.z; a.w += v3.w;
-    }
-    for (; k < splits; ++k) {
-        const int4 v = src[k * stride];
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-    }
-    const Epi epi = make_epi(p);
-    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
-    const float sxm = ACC ? 0.0f : p.sx[m];
-    store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(a.x), fix_acc<WK>(a.y), fix_acc<WK>(a.z), fix_acc<WK>(a.w));
-}
-
-// ---------------------------------------------------------------------------
-// Planning and launch.
-// ---------------------------------------------------------------------------
-SkinnyPlan plan_skinny(int M, int N, int K) {
-    SkinnyPlan sp{};
-    sp.use = M > 0 && M <= kSkinnyMaxM;
-    if (!sp.use) return sp;
-    const int Np = round_up(N, 32), Kp = round_up(K, 64);
-    const int nkc = Kp / 64;
-    sp.mf = (M + 31) / 32;
-    sp.nblk = (Np + 127) / 128;
-    sp.splits = (nkc + KSLMAX - 1) / KSLMAX;
-    sp.part_bytes = sp.splits > 1 ? (size_t)sp.splits * sp.nblk * 4 * sp.mf * 4 * 64 * 16 : 0;
-    return sp;
-}
-
-template <int WK, int MF, bool ACC>
-static hipError_t launch_skinny_mf(const GemmArgs& a, const SkinnyPlan& sp, hipStream_t st) {
-    k_gemm_skinny<WK, MF, ACC><<<dim3(sp.nblk, sp.splits), dim3(256), 0, st>>>(a, sp.splits);
-    if (sp.splits > 1) {
-        const size_t items = (size_t)sp.nblk * 4 * MF * 4 * 64;
-        k_splitk_reduce<WK, MF, ACC><<<dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st>>>(a, sp.splits, sp.nblk);
-    }
-    return hipGetLastError();
-}
-
-template <int WK, bool ACC>
-static hipError_t launch_skinny_t(const GemmArgs& a, const SkinnyPlan& sp, hipStream_t st) {
-    switch (sp.mf) {
-        case 1: return launch_skinny_mf<WK, 1, ACC>(a, sp, st);
-        case 2: return launch_skinny_mf<WK, 2, ACC>(a, sp, st);
-        case 3: return launch_skinny_mf<WK, 3, ACC>(a, sp, st);
-        case 4: return launch_skinny_mf<WK, 4, ACC>(a, sp, st);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 // Large-M configuration: 8 waves (block tile 256 x 256), one persistent block
 // per CU; ring depth 6 for 4-bit weights (144 KiB of LDS; W4A8 154 KiB with
 // its table), 4 for int8 weights (128 KiB).
@@ -767,10 +506,9 @@ static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
 
 template <int WK>
 static hipError_t launch_kind(const GemmArgs& a, hipStream_t st) {
-    const SkinnyPlan sp = plan_skinny(a.M, a.N, a.K);
-    const bool acc = a.acc_out != nullptr;
-    if (sp.use) return acc ? launch_skinny_t<WK, true>(a, sp, st) : launch_skinny_t<WK, false>(a, sp, st);
-    return acc ? launch_big_t<WK, true>(a, st) : launch_big_t<WK, false>(a, st);
+    const SmallPlan sp = plan_small(WK, a.M, a.N, a.K);
+    if (sp.use) return launch_small(a, sp, st);
+    return a.acc_out != nullptr ? launch_big_t<WK, true>(a, st) : launch_big_t<WK, false>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

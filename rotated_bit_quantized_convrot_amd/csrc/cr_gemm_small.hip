@@ -1,0 +1,423 @@
+// Small-M GEMM path (M <= 128): k_gemm_small and k_small_reduce, their plan
+// and launch.  Same arithmetic as the large-M kernel (exact int32
+// accumulators, rank-one epilogue).
+#include <algorithm>
+#include <cmath>
+
+#include "cr_device.h"
+#include "cr_epilogue.h"
+#include "cr_internal.h"
+
+namespace cr {
+
+// ---------------------------------------------------------------------------
+// Small-M kernel (M <= 128) on v_mfma_i32_16x16x64_i8.
+//
+// Operand roles: weights are the A operand (16 rows = n), activations the B
+// operand (16 columns = m).  Lane l supplies row/column l % 16 and 16 k
+// values of the 64-k chunk, k = kb(l / 16) + 0..15 with kb(g) =
+// 32 (g & 1) + 16 (g >> 1); both operands use the same k order, which is all
+// the dot product needs.  The result leaves lane l with column m = l % 16 and
+// rows n = 4 (l / 16) + r in register r.  In the packed 4-bit layouts the
+// 8 bytes a lane needs are contiguous (row r at r * 32, kb(g) at byte 8 g);
+// in the int8 layouts the 16 bytes are (weights) at 16 g of the row's 64 or
+// (activations [M, Kp]) at kb(g).
+//
+// Block = 8 waves over NT 16-row weight tiles and a range of 64-k chunks
+// (the whole K, or one of `splits` slices); wave w takes a contiguous run of
+// the range's chunks (run lengths differ by at most one), issues every load
+// of its run up front, then runs NT x MT MFMAs per chunk.  The eight waves'
+// int32 sums meet in LDS and each wave adds up and finishes a share of the
+// NT x MT output tiles: epilogue when the block covers all of K, else an
+// int32 partial tile for k_small_reduce.  W4A4 activations arrive packed
+// (4-bit, same layout as the weights, rows = m), the others as int8.
+// ---------------------------------------------------------------------------
+constexpr int SM_W = 8;   // waves per block
+
+// Loads of one chunk: NT weight fragments + MT activation fragments.
+template <int WK> struct SmW;
+template <> struct SmW<WK_W4> { v2i a; };
+template <> struct SmW<WK_I8> { v4i a; };
+template <> struct SmW<WK_W4A8> { v2i a; int c; };
+template <int WK> struct SmA { v4i a; };             // int8 activations
+template <> struct SmA<WK_W4> { v2i a; };            // packed 4-bit activations
+
+template <int WK>
+__device__ __forceinline__ int small_fix(int v) {
+    if constexpr (WK == WK_W4) return v >> 8;        // both operands carry a factor 16
+    else return v;
+}
+
+template <int WK, int MT, int NT, int CPW>
+__global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int cps, int acc_mode) {
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+    int4* red = reinterpret_cast<int4*>(smem);                         // [SM_W][NT*MT][64]
+    const uint4* stab = reinterpret_cast<const uint4*>(smem + SM_W * NT * MT * 1024);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int kb = 32 * (g & 1) + 16 * (g >> 1);
+    const int nkc = p.Kp >> 6;
+    const int nt16 = (p.N + 15) >> 4;
+    const int s = blockIdx.y;
+    const int kc0 = s * cps;
+    const int kcs = min(nkc - kc0, cps);                              // chunks of this block (>= 1)
+    // this wave's run: [kc0 + b0, kc0 + b0 + len)
+    const int base = kcs / SM_W, extra = kcs % SM_W;
+    const int len = base + (wave < extra ? 1 : 0);
+    const int b0 = wave * base + min(wave, extra);
+
+    // W4A8 decode table: loaded first, stored to LDS once the rest is in flight
+    v4i tabv = v4i{0, 0, 0, 0};
+    if constexpr (WK == WK_W4A8)
+        tabv = reinterpret_cast<const v4i*>(p.wp + w4a8_table_offset(p.N, p.K))[tid & 255];
+
+    // ---- epilogue operands of the (at most QPW) output tiles this wave
+    //      finishes, fetched now so their latency hides behind the loads
+    constexpr int QPW = (NT * MT + SM_W - 1) / SM_W;
+    Epi4 pre[QPW];
+    {
+        const Epi epi0 = make_epi(p);
+#pragma unroll
+        for (int k = 0; k < QPW; ++k) {
+            const int q = wave + SM_W * k;
+            const int nt = blockIdx.x * NT + q / MT;
+            const int m = (q % MT) * 16 + r16, n = nt * 16 + 4 * g;
+            pre[k] = epi4_fetch<WK>(epi0, p.sx, p.M, m, min(n, p.N - 1));
+        }
+    }
+
+    // ---- buffer resources and per-lane offsets.  Weights: the (at most
+    // three) 32-row bands the block's tiles live in; tile (band, chunk) is
+    // WT bytes, row r of it at r * RB.  Activations: the whole code array.
+    constexpr int WT = WK == WK_I8 ? 2048 : 1024, RB = WK == WK_I8 ? 64 : 32;
+    const int nt_first = min((int)blockIdx.x * NT, nt16 - 1);
+    const int band0 = nt_first >> 1;
+    const int nbands = min((p.Np >> 5) - band0, 3);
+    const uint32_t band_bytes = (uint32_t)nkc * WT;
+    const auto rs_w = buf_rsrc(p.wp + (size_t)band0 * band_bytes, (uint32_t)nbands * band_bytes);
+    uint32_t wvo[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int nt = min((int)blockIdx.x * NT + t, nt16 - 1);
+        wvo[t] = (uint32_t)((nt >> 1) - band0) * band_bytes + (uint32_t)(((nt & 1) * 16 + r16) * RB) +
+                 (uint32_t)(WK == WK_I8 ? 16 * g : 8 * g);
+    }
+    __amdgpu_buffer_rsrc_t rs_c = rs_w;                                 // replaced below for W4A8
+    uint32_t cvo[NT];
+    if constexpr (WK == WK_W4A8) {
+        const uint32_t cband = (uint32_t)nkc * 128;
+        rs_c = buf_rsrc(p.wp + w4a8_codes_offset(p.N, p.K) + (size_t)band0 * cband, (uint32_t)nbands * cband);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int nt = min((int)blockIdx.x * NT + t, nt16 - 1);
+            cvo[t] = (uint32_t)((nt >> 1) - band0) * cband + (uint32_t)(((nt & 1) * 16 + r16) * 4);
+        }
+    }
+    constexpr int AT = WK == WK_W4 ? 1024 : 64;                        // activation bytes per chunk step
+    // (this kernel runs only where the small-M plan exists, so W4A4 codes are packed)
+    const uint32_t a_bytes = WK == WK_W4 ? (uint32_t)round_up(p.M, 32) * (uint32_t)(p.K / 2)
+                                         : (uint32_t)p.M * (uint32_t)p.Kp;
+    const auto rs_a = buf_rsrc(p.qx, a_bytes);
+    uint32_t avo[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+        const int m = j * 16 + r16;
+        if constexpr (WK == WK_W4) avo[j] = (uint32_t)((m >> 5) * nkc) * 1024u + (uint32_t)((m & 31) * 32 + 8 * g);
+        else avo[j] = (uint32_t)min(m, p.M - 1) * (uint32_t)p.Kp + (uint32_t)kb;
+    }
+
+    // ---- all loads of the run (slots past the run re-read its last chunk;
+    //      a wave with an empty run reads the block's last chunk)
+    SmW<WK> wr[CPW][NT];
+    SmA<WK> ar[CPW][MT];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int kc = kc0 + min(b0 + i, kcs - 1);                      // wave-uniform
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if constexpr (WK == WK_I8) {
+                wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b128(rs_w, wvo[t], kc * WT, 0);
+            } else {
+                wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b64(rs_w, wvo[t], kc * WT, 0);
+                if constexpr (WK == WK_W4A8) wr[i][t].c = __builtin_amdgcn_raw_buffer_load_b32(rs_c, cvo[t], kc * 128, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            if constexpr (WK == WK_W4) ar[i][j].a = __builtin_amdgcn_raw_buffer_load_b64(rs_a, avo[j], kc * AT, 0);
+            else ar[i][j].a = __builtin_amdgcn_raw_buffer_load_b128(rs_a, avo[j], kc * AT, 0);
+        }
+    }
+    // keep every load above this point: all of the run is in flight before
+    // the first MFMA waits for its chunk
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (WK == WK_W4A8) {
+        if (tid < 256) const_cast<uint4*>(stab)[tid] = make_uint4((uint32_t)tabv.x, (uint32_t)tabv.y, (uint32_t)tabv.z, (uint32_t)tabv.w);
+        __syncthreads();
+    }
+
+    v4i acc[NT][MT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[t][j] = v4i{0, 0, 0, 0};
+
+    // Every slot runs its MFMAs (slots past the run with a zero weight
+    // operand), so no load is only used under a branch and none gets sunk
+    // behind the wait for another.
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const bool valid = i < len;
+        v4i b[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            if constexpr (WK == WK_W4) {
+                b[j] = unpack_w4x16((uint32_t)ar[i][j].a.x, (uint32_t)ar[i][j].a.y);
+            } else {
+                b[j] = ar[i][j].a;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            v4i a;
+            if constexpr (WK == WK_W4) {
+                a = unpack_w4x16((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y);
+            } else if constexpr (WK == WK_I8) {
+                a = wr[i][t].a;
+            } else {
+                const uint32_t code = ((uint32_t)wr[i][t].c >> (8 * (2 * (g & 1) + (g >> 1)))) & 0xFFu;
+                a = decode_w4a8((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y, stab[code]);
+            }
+            if (!valid) a = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+                acc[t][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[t][j], 0, 0, 0);
+        }
+    }
+
+    // ---- the eight waves' sums meet in LDS
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+            red[((wave * NT + t) * MT + j) * 64 + lane] = make_int4(acc[t][j].x, acc[t][j].y, acc[t][j].z, acc[t][j].w);
+    __syncthreads();
+
+    const Epi epi = make_epi(p);
+    const float sw0 = (WK == WK_W4A8 || acc_mode) ? 0.0f : p.wscale[0];
+#pragma unroll
+    for (int k = 0; k < QPW; ++k) {
+        const int q = wave + SM_W * k;
+        if (q >= NT * MT) break;
+        int4 sum = red[q * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < SM_W; ++w) {
+            const int4 v = red[(w * NT * MT + q) * 64 + lane];
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        }
+        const int t = q / MT, j = q % MT;
+        const int nt = blockIdx.x * NT + t;
+        if (nt >= nt16) continue;
+        if (splits > 1) {
+            reinterpret_cast<int4*>(p.part)[(((size_t)s * nt16 + nt) * MT + j) * 64 + lane] = sum;
+            continue;
+        }
+        const int m = j * 16 + r16, n = nt * 16 + 4 * g;
+        if (m >= p.M || n >= p.N) continue;
+        if (acc_mode)
+            store4<WK, true>(epi, m, n, 0.0f, 0.0f, small_fix<WK>(sum.x), small_fix<WK>(sum.y),
+                             small_fix<WK>(sum.z), small_fix<WK>(sum.w));
+        else if (pre[k].full)
+            store4_pre(epi, pre[k], m, n, small_fix<WK>(sum.x), small_fix<WK>(sum.y), small_fix<WK>(sum.z),
+                       small_fix<WK>(sum.w));
+        else
+            store4<WK, false>(epi, m, n, p.sx[m], sw0, small_fix<WK>(sum.x), small_fix<WK>(sum.y),
+                              small_fix<WK>(sum.z), small_fix<WK>(sum.w));
+    }
+}
+
+// Sum of the S K slices' partial tiles + epilogue; one thread per (16-row
+// weight tile, activation tile, lane).  S is a template parameter so that
+// all S loads are issued before the first add.
+template <int WK, int S>
+__global__ void __launch_bounds__(256) k_small_reduce(GemmArgs p, int mt, int acc_mode) {
+    const int nt16 = (p.N + 15) >> 4;
+    const size_t items = (size_t)nt16 * mt * 64;
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= items) return;
+    const int lane = (int)(id & 63);
+    const size_t q = id >> 6;
+    const int j = (int)(q % mt), nt = (int)(q / mt);
+    const int m = j * 16 + (lane & 15), n = nt * 16 + 4 * (lane >> 4);
+    if (m >= p.M || n >= p.N) return;
+    const int4* src = reinterpret_cast<const int4*>(p.part) + id;
+    int4 v[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) v[k] = src[(size_t)k * items];
+    int4 a = v[0];
+#pragma unroll
+    for (int k = 1; k < S; ++k) {
+        a.x += v[k].x; a.y += v[k].y; a.z += v[k].z; a.w += v[k].w;
+    }
+    const Epi epi = make_epi(p);
+    if (acc_mode) {
+        store4<WK, true>(epi, m, n, 0.0f, 0.0f, small_fix<WK>(a.x), small_fix<WK>(a.y), small_fix<WK>(a.z),
+                         small_fix<WK>(a.w));
+    } else {
+        const float sw0 = (WK == WK_W4A8) ? 0.0f : p.wscale[0];
+        store4<WK, false>(epi, m, n, p.sx[m], sw0, small_fix<WK>(a.x), small_fix<WK>(a.y), small_fix<WK>(a.z),
+                          small_fix<WK>(a.w));
+    }
+}
+
+template <int WK>
+static hipError_t launch_small_reduce(const GemmArgs& a, int splits, int mt, int acc_mode, hipStream_t st) {
+    const size_t items = (size_t)((a.N + 15) / 16) * mt * 64;
+    const dim3 grid((unsigned)((items + 255) / 256)), block(256);
+    switch (splits) {
+#define CR_RED_CASE(S_) \
+    case S_: k_small_reduce<WK, S_><<<grid, block, 0, st>>>(a, mt, acc_mode); break;
+        CR_RED_CASE(2) CR_RED_CASE(3) CR_RED_CASE(4) CR_RED_CASE(5) CR_RED_CASE(6) CR_RED_CASE(7)
+        CR_RED_CASE(8) CR_RED_CASE(9) CR_RED_CASE(10) CR_RED_CASE(11) CR_RED_CASE(12) CR_RED_CASE(13)
+        CR_RED_CASE(14) CR_RED_CASE(15) CR_RED_CASE(16)
+#undef CR_RED_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Planning and launch of the small-M path.
+// ---------------------------------------------------------------------------
+// 16-row weight tiles per block for MT activation tiles (the LDS meeting
+// point holds SM_W * NT * MT KiB).
+__host__ __device__ constexpr int small_nt(int mt) { return mt <= 5 ? 3 : 2; }
+constexpr int SM_CPW_MAX = 8;
+constexpr int SM_MAX_SPLITS = 16;
+
+// VGPRs of one chunk's loads; a wave holds at most 128 of them.
+__host__ __device__ constexpr int small_regs_per_chunk(int wk, int mt, int nt) {
+    return nt * (wk == WK_W4 ? 2 : (wk == WK_I8 ? 4 : 3)) + mt * (wk == WK_W4 ? 2 : 4);
+}
+constexpr int SM_LOAD_REGS = 128;
+
+SmallPlan plan_small(int kind, int M, int N, int K) {
+    SmallPlan sp{};
+    sp.use = M > 0 && M <= kSmallMaxM;
+    if (!sp.use) return sp;
+    const int Kp = kind == WK_I8 ? round_up(K, 64) : K;
+    const int nkc = Kp / 64;
+    const int nt16 = (N + 15) / 16;
+    sp.mt = (M + 15) / 16;
+    sp.nt = small_nt(sp.mt);
+    const int nblk = (nt16 + sp.nt - 1) / sp.nt;
+    const int per_chunk = small_regs_per_chunk(kind, sp.mt, sp.nt);
+    const double wbytes = kind == WK_W4 ? 0.5 : (kind == WK_I8 ? 1.0 : 0.5625);
+    const double abytes = kind == WK_W4 ? 0.5 : 1.0;
+    double best = 1e30;
+    for (int S = 1; S <= nkc && S <= SM_MAX_SPLITS; ++S) {
+        const int cps = (nkc + S - 1) / S;
+        const int splits = (nkc + cps - 1) / cps;
+        if (splits != S) continue;
+        const int cpw = (cps + SM_W - 1) / SM_W;
+        if (cpw > SM_CPW_MAX || cpw * per_chunk > SM_LOAD_REGS) continue;
+        // rough cycle model: per block max(L2->CU bytes at 64 B/clk, MFMA
+        // issue of 2 waves per SIMD) + latency, rounds of 256 blocks, and
+        // the partial round trip + second launch when K is split
+        const double blocks = (double)nblk * splits;
+        const double rounds = std::ceil(blocks / 256.0);
+        const double bytes = (double)cps * 64.0 * (sp.nt * 16 * wbytes + sp.mt * 16 * abytes);
+        const double mfma = 2.0 * cpw * sp.nt * sp.mt * 16.0;
+        double cost = rounds * (std::max(bytes / 64.0, mfma) + 2000.0);
+        if (splits > 1) cost += (double)splits * sp.mt * 16 * N * 8 / 4000.0 + 3000.0;
+        if (cost < best) {
+            best = cost;
+            sp.splits = splits;
+            sp.cps = cps;
+            sp.cpw = cpw;
+        }
+    }
+    if (best >= 1e30) {          // K beyond what the plan covers: no small-M path
+        sp.use = false;
+        return sp;
+    }
+    sp.nblk = nblk;
+    sp.part_bytes = sp.splits > 1 ? (size_t)sp.splits * nt16 * sp.mt * 64 * 16 : 0;
+    sp.lds = (size_t)SM_W * sp.nt * sp.mt * 1024 + (kind == WK_W4A8 ? 4096 : 0);
+    return sp;
+}
+
+template <int WK, int MT, int CPW>
+static hipError_t launch_small_c(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) {
+    constexpr int NT = small_nt(MT);
+    if constexpr (CPW * small_regs_per_chunk(WK, MT, NT) > SM_LOAD_REGS) {
+        return hipErrorInvalidValue;            // never planned
+    } else {
+    auto kern = &k_gemm_small<WK, MT, NT, CPW>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const int lds = SM_W * NT * MT * 1024 + (WK == WK_W4A8 ? 4096 : 0);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int acc_mode = a.acc_out != nullptr ? 1 : 0;
+    kern<<<dim3(sp.nblk, sp.splits), dim3(64 * SM_W), sp.lds, st>>>(a, sp.splits, sp.cps, acc_mode);
+    if (sp.splits > 1) return launch_small_reduce<WK>(a, sp.splits, MT, acc_mode, st);
+    return hipGetLastError();
+    }
+}
+
+template <int WK, int MT>
+static hipError_t launch_small_m(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) {
+    switch (sp.cpw) {
+        case 1: return launch_small_c<WK, MT, 1>(a, sp, st);
+        case 2: return launch_small_c<WK, MT, 2>(a, sp, st);
+        case 3: return launch_small_c<WK, MT, 3>(a, sp, st);
+        case 4: return launch_small_c<WK, MT, 4>(a, sp, st);
+        case 5: return launch_small_c<WK, MT, 5>(a, sp, st);
+        case 6: return launch_small_c<WK, MT, 6>(a, sp, st);
+        case 7: return launch_small_c<WK, MT, 7>(a, sp, st);
+        case 8: return launch_small_c<WK, MT, 8>(a, sp, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int WK>
+static hipError_t launch_small_t(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) {
+    switch (sp.mt) {
+        case 1: return launch_small_m<WK, 1>(a, sp, st);
+        case 2: return launch_small_m<WK, 2>(a, sp, st);
+        case 3: return launch_small_m<WK, 3>(a, sp, st);
+        case 4: return launch_small_m<WK, 4>(a, sp, st);
+        case 5: return launch_small_m<WK, 5>(a, sp, st);
+        case 6: return launch_small_m<WK, 6>(a, sp, st);
+        case 7: return launch_small_m<WK, 7>(a, sp, st);
+        case 8: return launch_small_m<WK, 8>(a, sp, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Whether a small-M plan exists does not depend on N (only its cost does).
+bool act_packed(int kind, int M, int K) {
+    return kind == WK_W4 && plan_small(kind, M, 16, K).use;
+}
+
+size_t act_bytes(int kind, int M, int K) {
+    if (act_packed(kind, M, K)) return (size_t)round_up(M, 32) * (size_t)K / 2;
+    return (size_t)M * (size_t)(kind == WK_I8 ? round_up(K, 64) : K);
+}
+
+hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) {
+    switch (a.kind) {
+        case WK_W4: return launch_small_t<WK_W4>(a, sp, st);
+        case WK_I8: return launch_small_t<WK_I8>(a, sp, st);
+        case WK_W4A8: return launch_small_t<WK_W4A8>(a, sp, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace cr

@@ -28,9 +28,11 @@ __host__ __device__ inline size_t w4a8_table_offset(int N, int K) {
 __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_offset(N, K) + 4096; }
 
 // Activation quantisation: codes int8 [M, Kp] (row-major, zero for k >= K)
-// and scales [M].
+// and scales [M]; with `packed` (W4A4 only) the codes go out 4-bit in the
+// packed weight layout with rows = m (round_up(M, 32) rows, rows >= M left
+// untouched).
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, hipStream_t st);
+                            float* sx, bool packed, hipStream_t st);
 
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
                           hipStream_t st);
@@ -54,18 +56,31 @@ struct GemmArgs {
     int32_t* part;         // split-K partial sums (small-M path)
 };
 
-// Small-M (split-K) path, used for M <= kSkinnyMaxM: a GEMM kernel that
-// writes each K slice's int32 partials to the workspace and a reduction
-// kernel that adds them and runs the epilogue.
-constexpr int kSkinnyMaxM = 128;
-struct SkinnyPlan {
+// Small-M path, used for M <= kSmallMaxM: 16-row MFMA tiles, blocks of 8
+// waves over 16 * nt weight rows that split their K range between the
+// waves and add the waves' sums in LDS; when K is also split across blocks
+// (`splits` > 1) a second kernel adds the int32 partial tiles and runs the
+// epilogue.  W4A4 activations are stored packed (4-bit) for this path.
+constexpr int kSmallMaxM = 128;
+struct SmallPlan {
     bool use;
-    int mf;        // 32-row activation fragments (1..4)
-    int nblk;      // 128-row weight blocks
-    int splits;    // K splits
-    size_t part_bytes;     // int32 partials, [splits][nblk][4 waves][mf][4][64 lanes] x int4
+    int mt;        // 16-row activation tiles (1..8)
+    int nt;        // 16-row weight tiles per block
+    int nblk;      // weight blocks
+    int splits;    // K slices across blocks
+    int cps;       // 64-k chunks per slice
+    int cpw;       // chunks per wave (at most)
+    size_t part_bytes;   // int32 partial tiles, [splits][N/16][mt][64 lanes] x int4
+    size_t lds;          // dynamic LDS bytes of the GEMM kernel
 };
-SkinnyPlan plan_skinny(int M, int N, int K);
+SmallPlan plan_small(int kind, int M, int N, int K);
+hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st);
+
+// Whether the activations of a linear are stored packed 4-bit (W4A4 on the
+// small-M path) rather than as int8 [M, Kp]; the same for every N.
+bool act_packed(int kind, int M, int K);
+// Bytes of the activation codes in the workspace.
+size_t act_bytes(int kind, int M, int K);
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 

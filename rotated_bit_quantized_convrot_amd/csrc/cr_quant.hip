@@ -102,7 +102,7 @@ __device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
 // whose 16 products come that close redoes them with the division.  |v/s_u|
 // <= QMAX (1 + 2^-23) keeps the fast codes inside [LO, HI].  Rows outside
 // the range take the literal path.
-template <int GPL, int QMAX, int LO, int HI>
+template <int GPL, int QMAX, int LO, int HI, bool PACKED>
 __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
                                                         int seg_log2, int8_t* __restrict__ qx,
                                                         float* __restrict__ sx) {
@@ -186,7 +186,22 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
             o.y = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
             o.z = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
             o.w = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
-            *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
+            if constexpr (PACKED) {
+                // 4-bit weight layout with rows = m: the lane's k0..k0+15
+                // (k0 = 256 g + 16 j) are the dwords (t, d = 0, 1) of half h
+                // of chunk k0 / 64, t = (k0 / 32) & 1, h = (k0 / 16) & 1;
+                // byte b of dword d holds k0 + 8d + b (low nibble) and
+                // k0 + 8d + 4 + b (high nibble).
+                const int k0 = g * 256 + j * 16;
+                const int kc = k0 >> 6, t = (k0 >> 5) & 1, h = (k0 >> 4) & 1;
+                const size_t off = ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
+                uint2 pk;
+                pk.x = (o.x & 0x0F0F0F0Fu) | ((o.y << 4) & 0xF0F0F0F0u);
+                pk.y = (o.z & 0x0F0F0F0Fu) | ((o.w << 4) & 0xF0F0F0F0u);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + off) = pk;
+            } else {
+                *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
+            }
         }
     }
 }
@@ -244,14 +259,14 @@ static int rot_threads(int G, int* gpl) {
     return threads;
 }
 
-template <int QMAX, int LO, int HI>
+template <int QMAX, int LO, int HI, bool PACKED>
 static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, hipStream_t st) {
     const int T = K / 16;              // lanes per row
     if (T <= 64) {
         int lg = 4;
         while ((1 << lg) < T) ++lg;
         const int rows = 256 >> lg;
-        k_quant_act_rot<1, QMAX, LO, HI><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx);
+        k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx);
         return hipGetLastError();
     }
     int gpl = 1;
@@ -259,18 +274,21 @@ static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float*
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, hipStream_t st) {
-    if (kind == WK_W4) return launch_rot<7, -8, 7>(x, M, K, qx, sx, st);
-    if (kind == WK_W4A8) return launch_rot<127, -128, 127>(x, M, K, qx, sx, st);
+                            float* sx, bool packed, hipStream_t st) {
+    if (kind == WK_W4) {
+        return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, st)
+                      : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, st);
+    }
+    if (kind == WK_W4A8) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, st);
     k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
 }

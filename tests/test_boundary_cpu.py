@@ -53,7 +53,11 @@ def test_sizes(L):
     assert L.cr_packed_bytes(0, 256, 2688) == 0
     assert L.cr_packed_bytes(0, 0, 256) == 0
     assert L.cr_packed_bytes(7, 256, 256) == 0
-    assert L.cr_workspace_bytes(0, 76, 9728, 2560) >= 76 * 2560 + 76 * 4
+    # workspace: W4A4 codes packed 4-bit at small M (rows rounded up to 32),
+    # int8 [M, K] otherwise; then the per-row scales
+    assert L.cr_workspace_bytes(0, 76, 9728, 2560) >= 96 * 2560 // 2 + 76 * 4
+    assert L.cr_workspace_bytes(0, 4096, 12288, 3072) >= 4096 * 3072 + 4096 * 4
+    assert L.cr_workspace_bytes(1, 76, 3072, 2688) >= 76 * 2688 + 76 * 4
     assert L.cr_workspace_bytes(1, -1, 16, 16) == 0
 
 
