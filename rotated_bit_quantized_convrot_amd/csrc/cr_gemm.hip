@@ -324,7 +324,6 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     };
 
     const Epi epi = make_epi(p);
-    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
 
     // Pipeline over the block's whole stage stream (its tiles back to back):
     // stage s lives in ring buffer s % NS and is loaded NS-1 stages ahead.
@@ -378,6 +377,11 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 
         if (++kc == nkc) {
             // Tile done: epilogue while the next tile's stages are in flight.
+            // The tensor scale is read here, next to its use: a scalar load
+            // left outstanding across the k-loop would turn every wait for
+            // LDS reads there into lgkmcnt(0) (scalar loads share that
+            // counter and return out of order).
+            const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
             int m0, n0;
             tile_origin(cur_tile, m0, n0);
             const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 3) == 0;
