@@ -362,7 +362,11 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         wait_vmcnt<(NS - 3) * C::LPS>();
         lds_barrier();
         issue_stage(IntC<(B + NS - 1) % NS>{});
-        read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
+        // W4A8: the last stage of a tile reads the next stage's fragments
+        // after the epilogue instead (fewer registers live across it; the
+        // other formats have them to spare and keep the plain schedule).
+        constexpr bool DEFER = WK == WK_W4A8;
+        if (!DEFER || kc + 1 != nkc) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
         __builtin_amdgcn_sched_barrier(0);   // the next stage's reads go out before the MFMAs
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -384,23 +388,20 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
             int m0, n0;
             tile_origin(cur_tile, m0, n0);
-            const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 3) == 0;
-            if (full && !ACC) {
-                // All epilogue operands are loaded up front (one wait), then
-                // every output quad is converted and stored without checks.
+            const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 7) == 0;
+            if (WK == WK_I8 && full && !ACC) {
+                // int8 weights: direct stores (the LDS-staged epilogue below
+                // needs more registers than this instantiation has spare).
                 float sxv[FM];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * WROWS + i * 32 + l32];
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     uint2 bv[4];
-                    float4 cv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
                         bv[q] = p.bias != nullptr ? *reinterpret_cast<const uint2*>(p.bias + n) : make_uint2(0u, 0u);
-                        if constexpr (WK == WK_W4A8) cv[q] = *reinterpret_cast<const float4*>(p.wscale + n);
-                        else cv[q] = make_float4(sw0, sw0, sw0, sw0);
                     }
 #pragma unroll
                     for (int i = 0; i < FM; ++i) {
@@ -408,8 +409,62 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
-                            const float c[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
                             const float b[4] = {bf16_lo(bv[q].x), bf16_hi(bv[q].x), bf16_lo(bv[q].y), bf16_hi(bv[q].y)};
+                            float v[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                v[j] = (float)fix_acc<WK>(acc[i][f][4 * q + j]) * sxv[i];
+                                v[j] = v[j] * sw0;
+                                if (p.bias != nullptr) v[j] = v[j] + b[j];
+                            }
+                            *reinterpret_cast<uint2*>(p.y + (size_t)m * p.N + n) =
+                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        }
+                    }
+                }
+            } else if (full && !ACC) {
+                // Full tile.  The MFMA layout gives each lane 4 consecutive
+                // columns of one row, so direct stores would write 16-byte
+                // pieces of 32 rows per instruction.  Instead each wave passes
+                // its results through LDS one 32-row x 32-column block at a
+                // time (every lane writes its 16 values of the block) and
+                // stores 64-byte row segments (4 lanes x 16 bytes per row, 16
+                // rows per store); the two blocks of a row's 128-byte line go
+                // out back to back.  Scratch: the ring buffer of this step's
+                // stage, which every wave has read (into registers) before the
+                // barrier below and which is refilled only after the next
+                // step's barrier.  Rows are padded to 80 bytes.  The wave's 64
+                // bias values and (W4A8) s_channel entries sit behind the rows.
+                constexpr int TR = 80;                        // scratch bytes per row
+                constexpr int OPB = 64 * 2 + 64 * 4;          // per-wave operand bytes
+                static_assert(NW * (32 * TR + OPB) <= C::STAGE, "epilogue scratch fits one stage buffer");
+                int8_t* scr = ring + B * C::STAGE + wave * 32 * TR;
+                int8_t* sop = ring + B * C::STAGE + NW * 32 * TR + wave * OPB;
+                float sxv[FM];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * WROWS + i * 32 + l32];
+                const int nw0 = n0 + wn * FN * 32;            // the wave's first column
+                const uint16_t bl = p.bias != nullptr ? p.bias[nw0 + lane] : (uint16_t)0;
+                float cl = sw0;
+                if constexpr (WK == WK_W4A8) cl = p.wscale[nw0 + lane];
+                lds_barrier();                                // stage buffer B is no longer read
+                reinterpret_cast<uint16_t*>(sop)[lane] = bl;
+                reinterpret_cast<float*>(sop + 128)[lane] = cl;
+                // per-lane bases; every other offset below is a constant
+                const int8_t* sbias = sop + 8 * h;            // bias of column 4h (+ 32f + 8q)
+                const int8_t* sscale = sop + 128 + 16 * h;    // scale of column 4h
+                int8_t* swr = scr + l32 * TR + 8 * h;         // this lane's row, its 4 columns
+                const int8_t* srd = scr + (lane >> 2) * TR + (lane & 3) * 16;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                    for (int f = 0; f < FN; ++f) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint2 bq = *reinterpret_cast<const uint2*>(sbias + 2 * (32 * f + 8 * q));
+                            const float4 cq = *reinterpret_cast<const float4*>(sscale + 4 * (32 * f + 8 * q));
+                            const float c[4] = {cq.x, cq.y, cq.z, cq.w};
+                            const float b[4] = {bf16_lo(bq.x), bf16_hi(bq.x), bf16_lo(bq.y), bf16_hi(bq.y)};
                             float v[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
@@ -417,8 +472,16 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                                 v[j] = v[j] * c[j];
                                 if (p.bias != nullptr) v[j] = v[j] + b[j];
                             }
-                            *reinterpret_cast<uint2*>(p.y + (size_t)m * p.N + n) =
+                            *reinterpret_cast<uint2*>(swr + q * 16) =
                                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        }
+#pragma unroll
+                        for (int sg = 0; sg < 2; ++sg) {
+                            const int lr = (lane >> 2) + 16 * sg;
+                            const uint4 o = *reinterpret_cast<const uint4*>(srd + sg * 16 * TR);
+                            const int m = m0 + wm * WROWS + i * 32 + lr;
+                            const int n = nw0 + f * 32 + (lane & 3) * 8;
+                            *reinterpret_cast<uint4*>(p.y + (size_t)m * p.N + n) = o;
                         }
                     }
                 }
@@ -452,6 +515,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                     for (int r = 0; r < 16; ++r) acc[i][f][r] = 0;
             kc = 0;
             ++cur_tile;
+            if constexpr (DEFER) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
         }
     };
     for (int gs = 0; gs < total_stages; gs += NS) {
