@@ -144,9 +144,10 @@ cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed,
  * by cr_gemm_quantized(kind, ...) on the same workspace and stream; results
  * are bit-identical.  One quantisation may feed GEMMs against several
  * weights with the same K (e.g. the gate and up projections of an MLP,
- * which read the same x); the workspace must then be sized with
- * cr_workspace_bytes() for the largest N, and GEMMs sharing it must run in
- * stream order.  The [QIE] card describes the rotation and quantisation of
+ * which read the same x); the workspace must then hold the largest
+ * cr_workspace_bytes() over the N values sharing it (not necessarily that of
+ * the largest N: the split-K partials depend on the tile count), and GEMMs
+ * sharing it must run in stream order.  The [QIE] card describes the rotation and quantisation of
  * the activations as part of the same fused kernel as the MMA; here they are
  * two kernels on one stream (rotation + quantisation need the whole row for
  * its scale before any code can be used). */

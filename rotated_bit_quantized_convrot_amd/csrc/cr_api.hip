@@ -83,7 +83,8 @@ int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? 
 // Workspace: [codes][scales M][split-K partials].  Codes are int8 [M, Kp],
 // or 4-bit packed (round_up(M, 32) x K/2 bytes) for W4A4 at small M.  The
 // codes and scales do not depend on N, so one quantisation can feed GEMMs
-// against several weights (with the workspace sized for the largest N).
+// against several weights (with the workspace sized for the largest need
+// over their N).
 struct WsLayout {
     size_t qx, sx, part, quant_end, total;
 };
@@ -96,7 +97,7 @@ WsLayout ws_layout(int kind, int M, int N, int K) {
     l.part = l.sx + a256((size_t)M * 4);
     l.quant_end = l.part;
     const cr::SmallPlan sp = cr::plan_small(wk, M, N, K);
-    l.total = l.part + a256(sp.use ? sp.part_bytes : 0);
+    l.total = l.part + a256(sp.use ? sp.part_bytes : cr::plan_big(wk, M, N, K).part_bytes);
     if (l.total < 256) l.total = 256;
     if (l.quant_end < 256) l.quant_end = 256;
     return l;

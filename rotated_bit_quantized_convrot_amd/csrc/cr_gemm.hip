@@ -17,49 +17,9 @@
 #include "cr_epilogue.h"
 #include "cr_internal.h"
 
+#include <cmath>
+
 namespace cr {
-
-constexpr int LDA = 80;   // LDS bytes per 64-k activation row (16 B pad: conflict-free b128 reads)
-
-template <int WK> struct WRaw;
-template <> struct WRaw<WK_W4> { uint4 a; };
-template <> struct WRaw<WK_I8> { uint4 a, b; };
-template <> struct WRaw<WK_W4A8> { uint4 a; uint32_t c; };
-
-// Loads this lane's part of weight tile (nb, kc).
-template <int WK>
-__device__ __forceinline__ void load_wraw(WRaw<WK>& w, const uint8_t* __restrict__ wp,
-                                          size_t codes_off, int nb, int nkc, int kc, int lane) {
-    const size_t tile = (size_t)nb * nkc + kc;
-    const int r = lane & 31, h = lane >> 5;
-    if constexpr (WK == WK_W4) {
-        w.a = *reinterpret_cast<const uint4*>(wp + tile * 1024 + r * 32 + 16 * h);
-    } else if constexpr (WK == WK_I8) {
-        const uint8_t* q = wp + tile * 2048 + r * 64 + 32 * h;
-        w.a = *reinterpret_cast<const uint4*>(q);
-        w.b = *reinterpret_cast<const uint4*>(q + 16);
-    } else {
-        w.a = *reinterpret_cast<const uint4*>(wp + tile * 1024 + r * 32 + 16 * h);
-        w.c = *reinterpret_cast<const uint32_t*>(wp + codes_off + tile * 128 + r * 4);
-    }
-}
-
-// The int8 A operand of MFMA step t (0 or 1) of a loaded tile.
-template <int WK, int T>
-__device__ __forceinline__ v4i wfrag(const WRaw<WK>& w, const uint4* __restrict__ stable, int h) {
-    if constexpr (WK == WK_W4) {
-        return T == 0 ? unpack_w4x16(w.a.x, w.a.y) : unpack_w4x16(w.a.z, w.a.w);
-    } else if constexpr (WK == WK_I8) {
-        const uint4 v = T == 0 ? w.a : w.b;
-        v4i r;
-        r.x = (int)v.x; r.y = (int)v.y; r.z = (int)v.z; r.w = (int)v.w;
-        return r;
-    } else {
-        const uint32_t code = (w.c >> (8 * (2 * T + h))) & 0xFFu;
-        const uint4 trow = stable[code];
-        return T == 0 ? decode_w4a8(w.a.x, w.a.y, trow) : decode_w4a8(w.a.z, w.a.w, trow);
-    }
-}
 
 // Exact accumulator from the MFMA sum (W4 operands carry a factor 16).
 template <int WK>
@@ -70,10 +30,13 @@ __device__ __forceinline__ int fix_acc(int v) {
 
 // ---------------------------------------------------------------------------
 // Large-M kernel.  Block tile 256 activation rows x 256 weight rows, 8 waves
-// (2 along m x 4 along n, 128 x 64 each), 64-k stages in a 4-deep LDS ring.
-// Stages are filled with direct-to-LDS loads (global_load_lds_dwordx4: lane i
-// of a wave writes its 16 bytes at base + 16 i), issued three stages ahead,
-// so no registers hold data in flight.  LDS layouts are XOR-swizzled so the
+// (2 along m x 4 along n, 128 x 64 each), 64-k stages in an NS-deep LDS ring.
+// Stages are filled with direct-to-LDS buffer loads (lane i of a wave writes
+// its 16 bytes at base + 16 i), issued NS - 1 stages ahead, so no registers
+// hold data in flight.  When the output has too few tiles to fill the chip,
+// the K range of every tile is split into equal slices taken by different
+// blocks, which store int32 partial tiles; a second kernel adds them and runs
+// the epilogue.  LDS layouts are XOR-swizzled so the
 // MFMA operand reads (ds_read_b128, 16 consecutive lanes = 16 rows) hit 16
 // distinct 16-byte bank groups:
 //   activations / int8 weights: row r (64 B) at r*64, 16-byte chunk c at
@@ -82,16 +45,6 @@ __device__ __forceinline__ int fix_acc(int v) {
 //     2r + (h ^ ((r >> 3) & 1)).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// global_load_lds_dwordx4 issued from inline asm: the compiler does not see
-// it as an LDS write, so it inserts no vmcnt(0) before later LDS reads (the
-// stage ring makes them independent); completion is tracked with explicit
-// wait_vmcnt<> before the barrier that publishes a stage.  The instruction
-// has no register result; M0 (the wave's LDS base) is set in the same block.
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(l), "v"(g) : "m0");
-}
 
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zero without touching memory.  Word 3 selects 32-bit untyped data.
@@ -106,8 +59,12 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // buffer_load_dwordx4 ... lds: lane i's 16 bytes at offset voff + soff of the
-// resource go to LDS address lds + 16 i (same inline-asm reasoning as
-// lds_dma16).
+// resource go to LDS address lds + 16 i.  Issued from inline asm, the load is
+// not seen by the compiler as an LDS write, so it inserts no vmcnt(0) before
+// later LDS reads (the stage ring makes them independent); completion is
+// tracked with explicit wait_vmcnt<> before the barrier that publishes a
+// stage.  The instruction has no register result; M0 (the LDS address) is set
+// in the same block.
 __device__ __forceinline__ void buf_lds16(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  : : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
@@ -131,6 +88,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr int BIG_BM = 256;
 constexpr int BIG_WM = 2;   // waves along m in the large-M kernel (wave tile 128 x 64)
 
+// Origin of output tile `lid` (0 .. tiles_m * tiles_n - 1): tiles are taken in
+// bands of 8 tile-rows, column by column inside a band, so that consecutive
+// ids share weight columns and activation rows.
+__device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_n, int& m0, int& n0) {
+    constexpr int GM = 8;
+    const int band = lid / (GM * tiles_n);
+    const int first_m = band * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_band = lid - band * GM * tiles_n;
+    m0 = (first_m + in_band % gm) * BIG_BM;
+    n0 = (in_band / gm) * 256;
+}
+
 // NW waves (2 along m x NW/2 along n; wave tile 128 x 512/NW), block tile
 // 256 x 256, NS-stage LDS ring.
 template <int WK, int NW, int NS>
@@ -147,8 +117,10 @@ struct BigCfg {
     static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0);
 };
 
-template <int WK, int NW, int NS, bool ACC>
-__global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n) {
+// SPLIT: units are K slices whose int32 sums go to partial tiles (splits > 1);
+// otherwise every unit is a whole tile and splits == 1.
+template <int WK, int NW, int NS, bool ACC, bool SPLIT>
+__global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n, int splits, int cps) {
     using C = BigCfg<WK, NW, NS>;
     constexpr int BN = C::BN;
     // WM waves along m, NW/WM along n; wave tile (256/WM) x (256*WM/NW)
@@ -174,27 +146,27 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         __syncthreads();
     }
 
-    // Persistent blocks: block b handles tiles b, b + G, b + 2G, ...  Blocks
-    // are dealt to the 8 XCDs round-robin, so within each round the blocks
-    // of one XCD take a contiguous run of tile ids (bands of 8 tile-rows),
-    // which keeps the operands they share in that XCD's L2.
+    // Persistent blocks: block b handles work units b, b + G, b + 2G, ...
+    // A unit is one K slice (cps 64-k chunks) of one output tile; unit id
+    // s * total + tile, so with one slice units are tiles.  Blocks are dealt
+    // to the 8 XCDs round-robin, so within each round the blocks of one XCD
+    // take a contiguous run of unit ids, which keeps the operands they share
+    // in that XCD's L2.
     const int total = tiles_m * tiles_n;
+    const int units = total * splits;
     const int G = gridDim.x, bid = blockIdx.x;
-    // slot: a permutation of 0..G-1; tile id j*G + slot for round j, so every
-    // tile id below `total` belongs to exactly one (block, round)
+    // slot: a permutation of 0..G-1; unit id j*G + slot for round j, so every
+    // unit id below `units` belongs to exactly one (block, round)
     const int slot = (G & 7) == 0 ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
-    const int my_tiles = (total - slot + G - 1) / G;
-    const int total_stages = my_tiles * nkc;
-    auto tile_origin = [&](int j, int& m0, int& n0) {
+    const int my_tiles = (units - slot + G - 1) / G;
+    const int total_stages = my_tiles * cps;
+    auto tile_origin = [&](int j, int& m0, int& n0, int& kc0, int& uid) {
         int lid = j * G + slot;
-        if (lid >= total) lid = total - 1;           // only for the clamped tail re-reads
-        constexpr int GM = 8;
-        const int band = lid / (GM * tiles_n);
-        const int first_m = band * GM;
-        const int gm = min(tiles_m - first_m, GM);
-        const int in_band = lid - band * GM * tiles_n;
-        m0 = (first_m + in_band % gm) * BIG_BM;
-        n0 = (in_band / gm) * BN;
+        if (lid >= units) lid = units - 1;           // only for the clamped tail re-reads
+        const int sl = SPLIT ? lid / total : 0;
+        big_tile_origin(lid - sl * total, tiles_m, tiles_n, m0, n0);
+        kc0 = sl * cps;
+        uid = lid;
     };
 
     // --- stage loads: buffer loads straight to LDS --------------------------
@@ -229,16 +201,16 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     v4i rs_a, rs_b, rs_c;
     uint32_t soff_a = 0, soff_b = 0, soff_c = 0;
     int is_tile = 0, is_kc = 0;   // issue cursor
-    auto aim = [&](int j) {       // resources of tile j, stage 0
-        int m0, n0;
-        tile_origin(j, m0, n0);
+    auto aim = [&](int j) {       // resources of unit j's tile, its first stage
+        int m0, n0, kc0, uid;
+        tile_origin(j, m0, n0, kc0, uid);
         rs_a = make_rsrc(p.qx + (size_t)m0 * Kp, (uint32_t)((size_t)(M - m0) * Kp));
         const int nb0 = n0 >> 5;
         const size_t tiles_left = (size_t)(nbmax + 1 - nb0);
         rs_b = make_rsrc(p.wp + (size_t)nb0 * nkc * BSTEP, (uint32_t)(tiles_left * nkc * BSTEP));
         if constexpr (WK == WK_W4A8)
             rs_c = make_rsrc(p.wp + codes_off + (size_t)nb0 * nkc * 128, (uint32_t)(tiles_left * nkc * 128));
-        soff_a = 0; soff_b = 0; soff_c = 0;
+        soff_a = (uint32_t)kc0 * 64; soff_b = (uint32_t)kc0 * BSTEP; soff_c = (uint32_t)kc0 * 128;
     };
     aim(0);
     auto issue_stage = [&](auto BUF) {
@@ -258,14 +230,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         }
         // advance (past the last stage the offsets stay put: the tail
         // re-reads it into a buffer that is never consumed)
-        if (++is_kc < nkc) {
+        if (++is_kc < cps) {
             soff_a += 64; soff_b += BSTEP; soff_c += 128;
         } else if (is_tile + 1 < my_tiles) {
             ++is_tile;
             is_kc = 0;
             aim(is_tile);
         } else {
-            is_kc = nkc;
+            is_kc = cps;
         }
     };
 
@@ -366,7 +338,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         // after the epilogue instead (fewer registers live across it; the
         // other formats have them to spare and keep the plain schedule).
         constexpr bool DEFER = WK == WK_W4A8;
-        if (!DEFER || kc + 1 != nkc) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
+        if (!DEFER || kc + 1 != cps) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
         __builtin_amdgcn_sched_barrier(0);   // the next stage's reads go out before the MFMAs
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -379,17 +351,29 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bt[f], cur.a[t][i], acc[i][f]);
         }
 
-        if (++kc == nkc) {
-            // Tile done: epilogue while the next tile's stages are in flight.
+        if (++kc == cps) {
+            // Unit done: epilogue while the next unit's stages are in flight.
             // The tensor scale is read here, next to its use: a scalar load
             // left outstanding across the k-loop would turn every wait for
             // LDS reads there into lgkmcnt(0) (scalar loads share that
             // counter and return out of order).
             const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
-            int m0, n0;
-            tile_origin(cur_tile, m0, n0);
+            int m0, n0, kc0, uid;
+            tile_origin(cur_tile, m0, n0, kc0, uid);
             const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 7) == 0;
-            if (WK == WK_I8 && full && !ACC) {
+            if constexpr (SPLIT) {
+                // K slice of a tile: the raw sums go to the unit's partial
+                // tile in fragment order, 1 KiB contiguous per store
+                int4* dst = reinterpret_cast<int4*>(p.part) + ((size_t)uid * NW + wave) * (FM * FN * 4 * 64) + lane;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int f = 0; f < FN; ++f)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            dst[((i * FN + f) * 4 + q) * 64] =
+                                make_int4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
+            } else if (WK == WK_I8 && full && !ACC) {
                 // int8 weights: direct stores (the LDS-staged epilogue below
                 // needs more registers than this instantiation has spare).
                 float sxv[FM];
@@ -555,20 +539,113 @@ static int num_cus() {
     return cache[dev];
 }
 
+// Second kernel of a K-split GEMM: adds the `splits` int32 partial tiles of
+// every output tile (exact, so the result does not depend on the split) and
+// runs the epilogue.  One wavefront per 32 x 32 fragment (tile, wave, i, f)
+// of the GEMM kernel, reading the partials in the order they were stored.
+template <int WK, bool ACC>
+__global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int tiles_n, int splits) {
+    constexpr int NW = BIG_NW, WM = BIG_WM, WNW = NW / WM, WROWS = BIG_BM / WM;
+    constexpr int FM = WROWS / 32, FN = 8 / WNW, FRAGS = NW * FM * FN;
+    const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+    const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+    const int total = tiles_m * tiles_n;
+    const int t = item / FRAGS;
+    if (t >= total) return;
+    const int r = item - t * FRAGS;                  // wave * FM * FN + i * FN + f
+    const int wave = r / (FM * FN), fi = r - wave * (FM * FN);
+    const int i = fi / FN, f = fi - i * FN;
+    int m0, n0;
+    big_tile_origin(t, tiles_m, tiles_n, m0, n0);
+    const int m = m0 + (wave % WM) * WROWS + i * 32 + l32;
+    const int4* src = reinterpret_cast<const int4*>(p.part) + (size_t)t * NW * FM * FN * 4 * 64 + r * 4 * 64 + lane;
+    const size_t sstride = (size_t)total * NW * FM * FN * 4 * 64;   // int4 per K slice
+    int4 sum[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[q] = make_int4(0, 0, 0, 0);
+#pragma unroll 4
+    for (int k = 0; k < splits; ++k) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 v = src[k * sstride + q * 64];
+            sum[q].x += v.x; sum[q].y += v.y; sum[q].z += v.z; sum[q].w += v.w;
+        }
+    }
+    if (m >= p.M) return;
+    const Epi epi = make_epi(p);
+    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
+    const float sxm = ACC ? 0.0f : p.sx[m];
+    const int nbase = n0 + ((wave / WM) * FN + f) * 32 + 4 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int n = nbase + 8 * q;
+        if (n < p.N)
+            store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(sum[q].x), fix_acc<WK>(sum[q].y),
+                            fix_acc<WK>(sum[q].z), fix_acc<WK>(sum[q].w));
+    }
+}
+
+// Large-M plan: the K slices per tile.  Rough time model in microseconds
+// (per 64-k stage of a 256 x 256 tile about 0.8 us for 4-bit weights, 1.0
+// for int8, 1.3 for W4A8; rounds of one unit per CU), plus for a split the
+// int32 partial tiles written and read back at about 4.5 TB/s and a second
+// launch.  Slices divide the K chunks evenly, at most 16.
+constexpr int BIG_CUS = 256;
+constexpr int BIG_MAX_SPLITS = 16;
+constexpr size_t BIG_PART_TILE = (size_t)BIG_BM * 256 * 4;   // bytes of one int32 partial tile
+
+BigPlan plan_big(int kind, int M, int N, int K) {
+    BigPlan bp{1, 0, 0};
+    if (M <= 0 || N <= 0 || K <= 0) return bp;
+    const int Kp = kind == WK_I8 ? round_up(K, 64) : K;
+    const int nkc = Kp / 64;
+    bp.cps = nkc;
+    const double total = (double)((M + BIG_BM - 1) / BIG_BM) * ((N + 255) / 256);
+    const double t_stage = kind == WK_W4 ? 0.8 : (kind == WK_I8 ? 1.0 : 1.3);
+    double best = 1e30;
+    for (int S = 1; S <= BIG_MAX_SPLITS && S <= nkc; ++S) {
+        if (nkc % S != 0) continue;
+        double cost = std::ceil(total * S / BIG_CUS) * (nkc / S) * t_stage;
+        if (S > 1) cost += (2.0 * total * S * (double)BIG_PART_TILE + 2.0 * M * N) / 4.5e6 + 4.0;
+        if (cost < best * 0.95) {                 // a split has to win clearly
+            best = cost;
+            bp.splits = S;
+            bp.cps = nkc / S;
+        }
+    }
+    bp.part_bytes = bp.splits > 1 ? (size_t)total * bp.splits * BIG_PART_TILE : 0;
+    return bp;
+}
+
 template <int WK, bool ACC>
 static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
     constexpr int NS = big_stages<WK>();
     using C = BigCfg<WK, BIG_NW, NS>;
     const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + C::BN - 1) / C::BN;
-    static bool attr_set = false;   // opt in to more than 64 KiB of dynamic LDS (once per process)
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+    const BigPlan bp = plan_big(WK, a.M, a.N, a.K);
+    if (bp.splits > 1 && a.part == nullptr) return hipErrorInvalidValue;
+    // opt in to more than 64 KiB of dynamic LDS (once per process and kernel)
+    static bool attr_set[2] = {false, false};
+    const bool split = bp.splits > 1;
+    if (!attr_set[split]) {
+        const void* k = split ? reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC, true>)
+                              : reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC, false>);
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set[split] = true;
     }
-    const int grid = min(tiles_m * tiles_n, num_cus());
-    k_gemm_big<WK, BIG_NW, NS, ACC><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n);
+    const int units = tiles_m * tiles_n * bp.splits;
+    const int grid = min(units, num_cus());
+    if (!split) {
+        k_gemm_big<WK, BIG_NW, NS, ACC, false><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, 1, bp.cps);
+        return hipGetLastError();
+    }
+    k_gemm_big<WK, BIG_NW, NS, ACC, true><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, bp.splits, bp.cps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int FRAGS = BIG_NW * (BIG_BM / BIG_WM / 32) * (8 / (BIG_NW / BIG_WM));
+    const int items = tiles_m * tiles_n * FRAGS;
+    k_big_fixup<WK, ACC><<<dim3((items + 3) / 4), dim3(256), 0, st>>>(a, tiles_m, tiles_n, bp.splits);
     return hipGetLastError();
 }
 

@@ -53,8 +53,19 @@ struct GemmArgs {
     const uint16_t* bias;  // [N] or null
     uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
     int32_t* acc_out;      // [M, N] int32 accumulators instead of y
-    int32_t* part;         // split-K partial sums (small-M path)
+    int32_t* part;         // split-K partial sums (workspace)
 };
+
+// Large-M path plan: K split into `splits` equal slices of `cps` 64-k chunks
+// when the output has too few 256 x 256 tiles to fill the chip; the slices'
+// int32 partial tiles ([splits][tiles][256 x 256] in fragment order) are
+// added by a second kernel.
+struct BigPlan {
+    int splits;
+    int cps;
+    size_t part_bytes;
+};
+BigPlan plan_big(int kind, int M, int N, int K);
 
 // Small-M path, used for M <= kSmallMaxM: 16-row MFMA tiles, blocks of 8
 // waves over 16 * nt weight rows that split their K range between the

@@ -240,6 +240,44 @@ def test_w4a8_acc_and_output(crp, M, K, N):
     assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
 
 
+# Shapes with few 256 x 256 output tiles and a long K: the large-M path splits
+# K across blocks and adds the int32 partial tiles in a second kernel.
+# Ragged M, N (N % 8 != 0, N % 4 != 0) and K (int8: K % 64 != 0) included.
+SPLIT_CASES = [
+    (0, 300, 4096, 512, False), (0, 520, 2560, 300, True),
+    (1, 260, 2688, 200, True), (1, 300, 1000, 37, False),
+    (2, 400, 1024, 264, True),
+]
+
+
+@pytest.mark.parametrize("kind,M,K,N,bias", SPLIT_CASES)
+def test_split_k_acc_and_output(crp, kind, M, K, N, bias):
+    tiles = -(-M // 256) * -(-N // 256)
+    # the workspace holds at least two slices of int32 partial tiles
+    assert crp.workspace_bytes(kind, M, N, K) >= 2 * tiles * 256 * 256 * 4
+    L = si.random_layer(M, K, N, seed=M * 5 + K + N + kind, bias=bias, outlier_count=6)
+    x = to_dev_bf16(L.x)
+    b = to_dev_bf16(L.bias) if bias else None
+    if kind == 0:
+        p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+        y = crp.linear_w4a4(x, p, s, N, b)
+        r = O.linear_w4a4(L.x, L.w, L.bias)
+    elif kind == 1:
+        p, s = crp.pack_weight_int8tw(to_dev_bf16(L.w))
+        y = crp.linear_int8tw(x, p, s, N, b)
+        r = O.linear_int8tw(L.x, L.w, L.bias)
+    else:
+        enc = O.w4a8_encode(L.w)
+        p = _w4a8_dev(crp, enc["idx_packed"], enc["s_rel"], enc["codebook"], N, K)
+        y = crp.linear_w4a8(x, p, to_dev(enc["s_channel"]), N, b)
+        r = O.linear_w4a8(L.x, enc["idx_packed"], enc["s_rel"], enc["codebook"], enc["s_channel"], L.bias)
+    a = crp.dbg_linear_acc(kind, x, p, N)
+    _sync()
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(r["y"]))
+
+
 def test_tiny_config_end_to_end(crp):
     L = si.tiny()
     y, a = _run_w4a4(crp, L)
