@@ -87,7 +87,8 @@ size_t cr_workspace_bytes(int kind, int M, int N, int K);
 
 /* Offline weight preparation: rotate each 256-block of every row of W,
  * s_w = absmax(rotated W) / 7, codes = clamp(rint(v / s_w), -8, 7), written
- * in the packed layout.
+ * in the packed layout: 4 bits per code (N rounded up to 32 rows) plus one
+ * int32 per row that the GEMM's exact integer arithmetic needs.
  *   w_bf16   [N,K] bf16                     (in)
  *   w_packed cr_packed_bytes(CR_W4A4,N,K)   (out)
  *   w_scale  1 float                        (out; also used as scratch)

@@ -69,7 +69,7 @@ cr_status check_nk(int kind, int N, int K) {
 
 size_t packed_bytes(int kind, int N, int K) {
     switch (kind) {
-        case CR_W4A4: return cr::w4_bytes(N, K);
+        case CR_W4A4: return cr::w4a4_bytes(N, K);
         case CR_INT8TW: return cr::i8_bytes(N, K);
         case CR_W4A8: return cr::w4a8_bytes(N, K);
         default: return 0;
@@ -80,13 +80,13 @@ int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K;
 
 int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8); }
 
-// Workspace: [codes][scales M][split-K partials].  Codes are int8 [M, Kp],
-// or 4-bit packed (round_up(M, 32) x K/2 bytes) for W4A4 at small M.  The
+// Workspace: [codes][scales M][W4A4: ra M][split-K partials].  Codes are
+// int8 [M, Kp], or for W4A4 4-bit tiles (round_up(M, 32) x K/2 bytes).  The
 // codes and scales do not depend on N, so one quantisation can feed GEMMs
 // against several weights (with the workspace sized for the largest need
 // over their N).
 struct WsLayout {
-    size_t qx, sx, part, quant_end, total;
+    size_t qx, sx, ra, part, quant_end, total;
 };
 
 WsLayout ws_layout(int kind, int M, int N, int K) {
@@ -94,7 +94,8 @@ WsLayout ws_layout(int kind, int M, int N, int K) {
     const int wk = wkind(kind);
     l.qx = 0;
     l.sx = a256(cr::act_bytes(wk, M, K));
-    l.part = l.sx + a256((size_t)M * 4);
+    l.ra = l.sx + a256((size_t)M * 4);
+    l.part = l.ra + (cr::act_packed(wk) ? a256((size_t)M * 4) : 0);
     l.quant_end = l.part;
     const cr::SmallPlan sp = cr::plan_small(wk, M, N, K);
     l.total = l.part + a256(sp.use ? sp.part_bytes : cr::plan_big(wk, M, N, K).part_bytes);
@@ -121,7 +122,7 @@ cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t
     char* w = static_cast<char*>(ws);
     hipError_t e = cr::launch_quant_act(wkind(kind), static_cast<const uint16_t*>(x), M, K, kp_of(kind, K),
                                         reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
-                                        cr::act_packed(wkind(kind), M, K), st);
+                                        reinterpret_cast<int32_t*>(w + l.ra), cr::act_packed(wkind(kind)), st);
     return launch_err(e, "activation quantisation");
 }
 
@@ -143,6 +144,10 @@ cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale
     a.y = static_cast<uint16_t*>(y);
     a.acc_out = acc;
     a.part = reinterpret_cast<int32_t*>(w + l.part);
+    if (cr::act_packed(a.kind)) {
+        a.ra = reinterpret_cast<const int32_t*>(w + l.ra);
+        a.cw = reinterpret_cast<const int32_t*>(a.wp + cr::w4_cw_offset(N, K));
+    }
     return launch_err(cr::launch_gemm(a, st), "integer GEMM");
 }
 
@@ -309,7 +314,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if ((s = check_device()) != CR_OK) return s;
     const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
     return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
-                                           static_cast<int8_t*>(codes), scales, false, stream),
+                                           static_cast<int8_t*>(codes), scales, nullptr, false, stream),
                       "activation quantisation");
 }
 

@@ -189,25 +189,39 @@ __device__ __forceinline__ int quant_code(float v, float s) {
 }
 
 // ---------------------------------------------------------------------------
-// Weight fragment producers.
+// W4A4 fragment producers (mixed nibble forms, see cr_internal.h).
 //
-// A packed 64-k chunk of one weight row is 32 bytes; the 16 bytes at 16*h
-// (h = lane / 32) hold, for MFMA step t = 0, 1, the dwords (t, d) at 8t + 4d.
-// Byte b of dword (t, d): low nibble k = 32t + 16h + 8d + b, high nibble
-// k = 32t + 16h + 8d + 4 + b.  So
-//    (P << 4) & 0xF0F0F0F0  = 16 * codes of k = .. + 8d + 0..3
-//    P & 0xF0F0F0F0         = 16 * codes of k = .. + 8d + 4..7
-// and the four dwords {lo(P0), hi(P0), lo(P1), hi(P1)} are the 16 int8
-// operands of the step in natural k order, each scaled by 16 (exact).
+// A packed 64-k chunk of one row is 32 bytes; the 16 bytes at 16*h
+// (h = lane / 32) hold, for MFMA step t = 0, 1, the dwords (t, d) at 8t + 4d,
+// dword (t, d) covering k0 + 0..7, k0 = 32t + 16h + 8d.  Activations: byte b
+// has k0 + b (offset-binary) low and k0 + 4 + b (two's complement) high;
+// weights the reverse.  One AND per output dword:
+//   P & 0x0F0F0F0F = code + 8 of the low nibbles,
+//   P & 0xF0F0F0F0 = 16 * code of the high nibbles,
+// and {first four k, next four k, ...} come out in natural k order for both
+// operands, each k pairing a low form with a high form.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
+__device__ __forceinline__ v4i unpack_act4(uint32_t p0, uint32_t p1) {
     v4i r;
-    r.x = (int)((p0 << 4) & 0xF0F0F0F0u);
+    r.x = (int)(p0 & 0x0F0F0F0Fu);
     r.y = (int)(p0 & 0xF0F0F0F0u);
-    r.z = (int)((p1 << 4) & 0xF0F0F0F0u);
+    r.z = (int)(p1 & 0x0F0F0F0Fu);
     r.w = (int)(p1 & 0xF0F0F0F0u);
     return r;
 }
+
+__device__ __forceinline__ v4i unpack_wt4(uint32_t p0, uint32_t p1) {
+    v4i r;
+    r.x = (int)(p0 & 0xF0F0F0F0u);
+    r.y = (int)(p0 & 0x0F0F0F0Fu);
+    r.z = (int)(p1 & 0xF0F0F0F0u);
+    r.w = (int)(p1 & 0x0F0F0F0Fu);
+    return r;
+}
+
+// Exact W4A4 dot product from the MFMA sum and the two correction terms
+// rn = -128 ra[m], cn = -128 cw[n].
+__device__ __forceinline__ int w4_exact(int acc, int rn, int cn) { return (acc + rn + cn) >> 4; }
 
 // Four codebook indices (one per byte, 0..15, in `sel`) looked up in a
 // 16-byte table row t0..t3: v_perm picks from the low and the high 8 entries
@@ -222,7 +236,8 @@ __device__ __forceinline__ uint32_t lut16(uint32_t sel, uint32_t t0, uint32_t t1
 }
 
 // W4A8: decode the 16 operands of one step from two packed index dwords
-// (same nibble order as above) and the table row of the group's scale code.
+// (byte b of the dword of k0..k0+7: k0 + b low, k0 + 4 + b high) and the
+// table row of the group's scale code.
 __device__ __forceinline__ v4i decode_w4a8(uint32_t p0, uint32_t p1, uint4 trow) {
     v4i r;
     r.x = (int)lut16(p0 & 0x0F0F0F0Fu, trow.x, trow.y, trow.z, trow.w);

@@ -1,6 +1,8 @@
 // Epilogue shared by the GEMM kernels: y[m,n] = bf16_rne(fl(fl(float(acc) *
 // s_x[m]) * s_w) + bias[n]) (s_channel[n] in place of s_w for W4A8), or the
-// raw int32 accumulator for the inspection hook.
+// exact int32 accumulator for the inspection hook.  The functions take the
+// MFMA sums; W4A4 sums are turned into the exact dot products here (see the
+// nibble forms in cr_internal.h).
 #pragma once
 #include "cr_device.h"
 #include "cr_internal.h"
@@ -13,21 +15,40 @@ struct Epi {
     const uint16_t* bias;  // [N] or null
     uint16_t* y;           // [M, N]
     int32_t* acc_out;      // [M, N] or null
+    const int32_t* ra;     // W4A4 correction sums [M] and [Np]
+    const int32_t* cw;
     int N;
 };
 
 __device__ __forceinline__ Epi make_epi(const GemmArgs& p) {
     Epi e;
     e.wscale = p.wscale; e.bias = p.bias; e.y = p.y; e.acc_out = p.acc_out; e.N = p.N;
+    e.ra = p.ra; e.cw = p.cw;
     return e;
 }
 
-// Writes 4 consecutive outputs n..n+3 of row m (n % 4 == 0, n < N).
-// sw0: the tensor scale (unused for W4A8, which reads s_channel[n]).
+// W4A4: exact dot products of row m, columns n..n+3 (n % 4 == 0, n < N; the
+// cw vector has Np >= n + 4 entries) from the MFMA sums, in place.
+template <int WK>
+__device__ __forceinline__ void exact4(const Epi& e, int m, int n, int& a0, int& a1, int& a2, int& a3) {
+    if constexpr (WK == WK_W4) {
+        const int rn = -128 * e.ra[m];
+        const int4 c = *reinterpret_cast<const int4*>(e.cw + n);
+        a0 = w4_exact(a0, rn, -128 * c.x);
+        a1 = w4_exact(a1, rn, -128 * c.y);
+        a2 = w4_exact(a2, rn, -128 * c.z);
+        a3 = w4_exact(a3, rn, -128 * c.w);
+    }
+}
+
+// Writes 4 consecutive outputs n..n+3 of row m (n % 4 == 0, n < N) from
+// their MFMA sums.  sw0: the tensor scale (unused for W4A8, which reads
+// s_channel[n]).
 template <int WK, bool ACC>
 __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, float sw0, int a0,
                                        int a1, int a2, int a3) {
     const int N = e.N;
+    exact4<WK>(e, m, n, a0, a1, a2, a3);
     const bool full = (N & 3) == 0;          // n + 3 < N then, rows 8-byte aligned
     if constexpr (ACC) {
         int32_t* dst = e.acc_out + (size_t)m * N + n;
@@ -80,6 +101,7 @@ __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, fl
 // `full` is false and store4 is used instead).
 struct Epi4 {
     float sx, sw[4], b[4];
+    int rn, cn[4];         // W4A4: -128 ra[m], -128 cw[n + j]
     bool full;
 };
 
@@ -114,13 +136,23 @@ __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M,
     const uint32_t b23 = (uint32_t)bp[e.bias != nullptr ? min(2, N - 1 - nc) : 0] |
                          ((uint32_t)bp[e.bias != nullptr ? min(3, N - 1 - nc) : 0] << 16);
     r.b[0] = bf16_lo(b01); r.b[1] = bf16_hi(b01); r.b[2] = bf16_lo(b23); r.b[3] = bf16_hi(b23);
+    if constexpr (WK == WK_W4) {
+        r.rn = -128 * e.ra[mc];
+        const int4 c = *reinterpret_cast<const int4*>(e.cw + (vec ? nc : 0));
+        r.cn[0] = -128 * c.x; r.cn[1] = -128 * c.y; r.cn[2] = -128 * c.z; r.cn[3] = -128 * c.w;
+    }
     return r;
 }
 
 // store4 with prefetched operands (r.full must hold): same arithmetic.
+template <int WK>
 __device__ __forceinline__ void store4_pre(const Epi& e, const Epi4& r, int m, int n, int a0, int a1,
                                            int a2, int a3) {
-    const int a[4] = {a0, a1, a2, a3};
+    int a[4] = {a0, a1, a2, a3};
+    if constexpr (WK == WK_W4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = w4_exact(a[j], r.rn, r.cn[j]);
+    }
     const bool has_bias = e.bias != nullptr;
     float v[4];
 #pragma unroll

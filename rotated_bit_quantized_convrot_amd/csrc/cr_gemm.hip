@@ -18,15 +18,9 @@
 #include "cr_internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace cr {
-
-// Exact accumulator from the MFMA sum (W4 operands carry a factor 16).
-template <int WK>
-__device__ __forceinline__ int fix_acc(int v) {
-    if constexpr (WK == WK_W4) return v >> 4;
-    else return v;
-}
 
 // ---------------------------------------------------------------------------
 // Large-M kernel.  Block tile 256 activation rows x 256 weight rows, 8 waves
@@ -36,7 +30,9 @@ __device__ __forceinline__ int fix_acc(int v) {
 // hold data in flight.  When the output has too few tiles to fill the chip,
 // the K range of every tile is split into equal slices taken by different
 // blocks, which store int32 partial tiles; a second kernel adds them and runs
-// the epilogue.  LDS layouts are XOR-swizzled so the
+// the epilogue.  W4A4 activations arrive as 4-bit tiles (rows = m) and go
+// through LDS like the weights; both operands are widened by one AND per
+// dword (nibble forms in cr_internal.h) and the epilogue corrects the sums.  LDS layouts are XOR-swizzled so the
 // MFMA operand reads (ds_read_b128, 16 consecutive lanes = 16 rows) hit 16
 // distinct 16-byte bank groups:
 //   activations / int8 weights: row r (64 B) at r*64, 16-byte chunk c at
@@ -45,6 +41,10 @@ __device__ __forceinline__ int fix_acc(int v) {
 //     2r + (h ^ ((r >> 3) & 1)).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Byte count of a buffer resource (32 bits; a block never reaches past 4 GiB
+// from the base of its resources).
+__host__ __device__ __forceinline__ uint32_t clamp_u32(size_t v) { return v > 0xFFFFFFFFu ? 0xFFFFFFFFu : (uint32_t)v; }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zero without touching memory.  Word 3 selects 32-bit untyped data.
@@ -106,15 +106,23 @@ __device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_
 template <int WK, int NW, int NS>
 struct BigCfg {
     static constexpr int BN = 256;
+    static constexpr bool PA = WK == WK_W4;                            // 4-bit activation tiles
     static constexpr int TPW = 8 / NW;                                 // 32-row weight tiles loaded per wave
-    static constexpr int A_BYTES = BIG_BM * 64;                       // activations per stage
+    static constexpr int A_BYTES = PA ? BIG_BM * 32 : BIG_BM * 64;    // activations per stage
     static constexpr int B_BYTES = WK == WK_I8 ? BN * 64 : BN * 32;
     static constexpr int C_BYTES = WK == WK_W4A8 ? BN * 4 : 0;        // W4A8 scale codes
     static constexpr int STAGE = A_BYTES + B_BYTES + C_BYTES;
-    static constexpr int LA = 16 / NW;                                 // activation loads per wave
+    static constexpr int LA = PA ? 8 / NW : 16 / NW;                   // activation loads per wave
     // direct-to-LDS loads per wave per stage
     static constexpr int LPS = LA + TPW * (WK == WK_I8 ? 2 : 1) + (WK == WK_W4A8 ? 1 : 0);
-    static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0);
+    // LDS-staged epilogue: per wave 32 rows of EPI_TR bytes, then its 64
+    // columns' bias (bf16), scale (fp32) and (W4A4) weight correction (int32)
+    static constexpr int EPI_TR = 80;
+    static constexpr int EPI_OPB = 64 * 2 + 64 * 4 + (PA ? 64 * 4 : 0);
+    static constexpr int EPI_BYTES = NW * (32 * EPI_TR + EPI_OPB);
+    // W4A4 stages are too small to hold it: its own region after the ring
+    static constexpr size_t EPI_OFF = (size_t)NS * STAGE;
+    static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0) + (PA ? EPI_BYTES : 0);
 };
 
 // SPLIT: units are K slices whose int32 sums go to partial tiles (splits > 1);
@@ -177,11 +185,18 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     //   activations: rows 16*(LA*wave + j) + lane/4, chunk (lane%4) ^ swizzle
     //   weights: tile n0/32 + wave, this lane's row and half (swizzled)
     constexpr int BSTEP = WK == WK_I8 ? 2048 : 1024;
+    //   4-bit activations: 32-row tile `wave` of the block, like the weights
+    static_assert(!C::PA || C::LA == 1, "one 4-bit activation tile per wave");
+    constexpr int ASTEP = C::PA ? 1024 : 64;                    // activation bytes per 64-k step
     uint32_t a_voff[C::LA];
 #pragma unroll
     for (int j = 0; j < C::LA; ++j) {
-        const int row = 16 * (C::LA * wave + j) + (lane >> 2);
-        a_voff[j] = (uint32_t)(row * Kp + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
+        if constexpr (C::PA) {
+            a_voff[j] = (uint32_t)(wave * nkc * 1024 + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
+        } else {
+            const int row = 16 * (C::LA * wave + j) + (lane >> 2);
+            a_voff[j] = (uint32_t)(row * Kp + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
+        }
     }
     uint32_t b_voff[C::TPW][2];
 #pragma unroll
@@ -204,20 +219,25 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     auto aim = [&](int j) {       // resources of unit j's tile, its first stage
         int m0, n0, kc0, uid;
         tile_origin(j, m0, n0, kc0, uid);
-        rs_a = make_rsrc(p.qx + (size_t)m0 * Kp, (uint32_t)((size_t)(M - m0) * Kp));
+        if constexpr (C::PA)
+            rs_a = make_rsrc(p.qx + (size_t)(m0 >> 5) * nkc * 1024,
+                             clamp_u32((size_t)((round_up(M, 32) - m0) >> 5) * nkc * 1024));
+        else
+            rs_a = make_rsrc(p.qx + (size_t)m0 * Kp, clamp_u32((size_t)(M - m0) * Kp));
         const int nb0 = n0 >> 5;
         const size_t tiles_left = (size_t)(nbmax + 1 - nb0);
-        rs_b = make_rsrc(p.wp + (size_t)nb0 * nkc * BSTEP, (uint32_t)(tiles_left * nkc * BSTEP));
+        rs_b = make_rsrc(p.wp + (size_t)nb0 * nkc * BSTEP, clamp_u32(tiles_left * nkc * BSTEP));
         if constexpr (WK == WK_W4A8)
-            rs_c = make_rsrc(p.wp + codes_off + (size_t)nb0 * nkc * 128, (uint32_t)(tiles_left * nkc * 128));
-        soff_a = (uint32_t)kc0 * 64; soff_b = (uint32_t)kc0 * BSTEP; soff_c = (uint32_t)kc0 * 128;
+            rs_c = make_rsrc(p.wp + codes_off + (size_t)nb0 * nkc * 128, clamp_u32(tiles_left * nkc * 128));
+        soff_a = (uint32_t)kc0 * ASTEP; soff_b = (uint32_t)kc0 * BSTEP; soff_c = (uint32_t)kc0 * 128;
     };
     aim(0);
     auto issue_stage = [&](auto BUF) {
         constexpr int buf = decltype(BUF)::value;
         const uint32_t st = ring_lds + buf * C::STAGE;
 #pragma unroll
-        for (int j = 0; j < C::LA; ++j) buf_lds16(rs_a, a_voff[j], soff_a, st + 16 * (C::LA * wave + j) * 64);
+        for (int j = 0; j < C::LA; ++j)
+            buf_lds16(rs_a, a_voff[j], soff_a, st + (C::PA ? wave * 1024 : 16 * (C::LA * wave + j) * 64));
         const uint32_t sb = st + C::A_BYTES;
 #pragma unroll
         for (int t = 0; t < C::TPW; ++t) {
@@ -231,7 +251,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         // advance (past the last stage the offsets stay put: the tail
         // re-reads it into a buffer that is never consumed)
         if (++is_kc < cps) {
-            soff_a += 64; soff_b += BSTEP; soff_c += 128;
+            soff_a += ASTEP; soff_b += BSTEP; soff_c += 128;
         } else if (is_tile + 1 < my_tiles) {
             ++is_tile;
             is_kc = 0;
@@ -254,6 +274,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     int aoff[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) aoff[t] = (wm * WROWS + l32) * 64 + (((2 * t + h) ^ swz) * 16);
+    // 4-bit activations: 32-row tile wm * FM + i, this lane's row and half
+    const int apoff = wm * FM * 1024 + (2 * l32 + (h ^ ((l32 >> 3) & 1))) * 16;
     int boff[FN];
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
@@ -284,7 +306,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             r.x = (int)v.x; r.y = (int)v.y; r.z = (int)v.z; r.w = (int)v.w;
             return r;
         } else if constexpr (WK == WK_W4) {
-            return t == 0 ? unpack_w4x16(w.a.x, w.a.y) : unpack_w4x16(w.a.z, w.a.w);
+            return t == 0 ? unpack_wt4(w.a.x, w.a.y) : unpack_wt4(w.a.z, w.a.w);
         } else {
             const uint4 tr = sT[(w.codes >> (8 * (2 * t + h))) & 0xFF];
             return t == 0 ? decode_w4a8(w.a.x, w.a.y, tr) : decode_w4a8(w.a.z, w.a.w, tr);
@@ -304,15 +326,29 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     // the second step's MFMAs run; a buffer is refilled only after the
     // barrier that follows the last read of it by every wave.
     static_assert(NS == 4 || NS == 6, "ring depth (even: register sets alternate per stage)");
-    // Fragments of one stage: activation operands of both MFMA steps and the
-    // weight bytes.  Two sets alternate: while the MFMAs of stage s run from
-    // one set, the reads of stage s+1 land in the other.
-    struct Frags { v4i a[2][FM]; WStage w[FN]; };
+    // Fragments of one stage: activation operands of both MFMA steps (int8)
+    // or the activation bytes (4-bit), and the weight bytes.  Two sets
+    // alternate: while the MFMAs of stage s run from one set, the reads of
+    // stage s+1 land in the other.
+    struct AI8 { v4i a[2][FM]; };
+    struct AP4 { uint4 r[FM]; };
+    struct Frags { typename std::conditional<C::PA, AP4, AI8>::type a; WStage w[FN]; };
     auto read_frags = [&](const int8_t* st, Frags& F) {
-        read_a(st, 0, F.a[0]);
-        read_a(st, 1, F.a[1]);
+        if constexpr (C::PA) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) F.a.r[i] = *reinterpret_cast<const uint4*>(st + apoff + i * 1024);
+        } else {
+            read_a(st, 0, F.a.a[0]);
+            read_a(st, 1, F.a.a[1]);
+        }
 #pragma unroll
         for (int f = 0; f < FN; ++f) F.w[f] = read_w(st, f);
+    };
+    auto aop = [&](const Frags& F, int t, int i) -> v4i {
+        if constexpr (C::PA)
+            return t == 0 ? unpack_act4(F.a.r[i].x, F.a.r[i].y) : unpack_act4(F.a.r[i].z, F.a.r[i].w);
+        else
+            return F.a.a[t][i];
     };
     issue_stage(IntC<0>{});
     issue_stage(IntC<1>{});
@@ -348,7 +384,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bt[f], cur.a[t][i], acc[i][f]);
+                for (int f = 0; f < FN; ++f) acc[i][f] = mfma32(bt[f], aop(cur, t, i), acc[i][f]);
         }
 
         if (++kc == cps) {
@@ -397,7 +433,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                             float v[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                v[j] = (float)fix_acc<WK>(acc[i][f][4 * q + j]) * sxv[i];
+                                v[j] = (float)acc[i][f][4 * q + j] * sxv[i];
                                 v[j] = v[j] * sw0;
                                 if (p.bias != nullptr) v[j] = v[j] + b[j];
                             }
@@ -414,29 +450,45 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 // time (every lane writes its 16 values of the block) and
                 // stores 64-byte row segments (4 lanes x 16 bytes per row, 16
                 // rows per store); the two blocks of a row's 128-byte line go
-                // out back to back.  Scratch: the ring buffer of this step's
-                // stage, which every wave has read (into registers) before the
-                // barrier below and which is refilled only after the next
-                // step's barrier.  Rows are padded to 80 bytes.  The wave's 64
-                // bias values and (W4A8) s_channel entries sit behind the rows.
-                constexpr int TR = 80;                        // scratch bytes per row
-                constexpr int OPB = 64 * 2 + 64 * 4;          // per-wave operand bytes
-                static_assert(NW * (32 * TR + OPB) <= C::STAGE, "epilogue scratch fits one stage buffer");
-                int8_t* scr = ring + B * C::STAGE + wave * 32 * TR;
-                int8_t* sop = ring + B * C::STAGE + NW * 32 * TR + wave * OPB;
+                // out back to back.  Rows are padded to 80 bytes; the wave's
+                // 64 bias values, scales and (W4A4) weight corrections sit
+                // behind them.  Scratch: W4A4 has a region of its own, each
+                // wave only touching its part; W4A8 uses the ring buffer of
+                // this step's stage, which every wave has read (into
+                // registers) before the barrier below and which is refilled
+                // only after the next step's barrier.
+                constexpr int TR = C::EPI_TR, OPB = C::EPI_OPB;
+                int8_t* ebase;
+                if constexpr (C::PA) {
+                    ebase = ring + C::EPI_OFF;
+                } else {
+                    static_assert(C::EPI_BYTES <= C::STAGE, "epilogue scratch fits one stage buffer");
+                    ebase = ring + B * C::STAGE;
+                }
+                int8_t* scr = ebase + wave * 32 * TR;
+                int8_t* sop = ebase + NW * 32 * TR + wave * OPB;
                 float sxv[FM];
+                int rnv[FM];                                  // W4A4: -128 ra[m]
 #pragma unroll
-                for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * WROWS + i * 32 + l32];
+                for (int i = 0; i < FM; ++i) {
+                    const int m = m0 + wm * WROWS + i * 32 + l32;
+                    sxv[i] = p.sx[m];
+                    if constexpr (C::PA) rnv[i] = -128 * p.ra[m];
+                }
                 const int nw0 = n0 + wn * FN * 32;            // the wave's first column
                 const uint16_t bl = p.bias != nullptr ? p.bias[nw0 + lane] : (uint16_t)0;
                 float cl = sw0;
                 if constexpr (WK == WK_W4A8) cl = p.wscale[nw0 + lane];
-                lds_barrier();                                // stage buffer B is no longer read
+                int cnl = 0;
+                if constexpr (C::PA) cnl = -128 * p.cw[nw0 + lane];
+                if constexpr (!C::PA) lds_barrier();          // stage buffer B is no longer read
                 reinterpret_cast<uint16_t*>(sop)[lane] = bl;
                 reinterpret_cast<float*>(sop + 128)[lane] = cl;
+                if constexpr (C::PA) reinterpret_cast<int*>(sop + 384)[lane] = cnl;
                 // per-lane bases; every other offset below is a constant
                 const int8_t* sbias = sop + 8 * h;            // bias of column 4h (+ 32f + 8q)
                 const int8_t* sscale = sop + 128 + 16 * h;    // scale of column 4h
+                const int8_t* scorr = sop + 384 + 16 * h;     // correction of column 4h
                 int8_t* swr = scr + l32 * TR + 8 * h;         // this lane's row, its 4 columns
                 const int8_t* srd = scr + (lane >> 2) * TR + (lane & 3) * 16;
 #pragma unroll
@@ -449,10 +501,18 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                             const float4 cq = *reinterpret_cast<const float4*>(sscale + 4 * (32 * f + 8 * q));
                             const float c[4] = {cq.x, cq.y, cq.z, cq.w};
                             const float b[4] = {bf16_lo(bq.x), bf16_hi(bq.x), bf16_lo(bq.y), bf16_hi(bq.y)};
+                            int a[4] = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
+                            if constexpr (C::PA) {
+                                const int4 rq = *reinterpret_cast<const int4*>(scorr + 4 * (32 * f + 8 * q));
+                                a[0] = w4_exact(a[0], rnv[i], rq.x);
+                                a[1] = w4_exact(a[1], rnv[i], rq.y);
+                                a[2] = w4_exact(a[2], rnv[i], rq.z);
+                                a[3] = w4_exact(a[3], rnv[i], rq.w);
+                            }
                             float v[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                v[j] = (float)fix_acc<WK>(acc[i][f][4 * q + j]) * sxv[i];
+                                v[j] = (float)a[j] * sxv[i];
                                 v[j] = v[j] * c[j];
                                 if (p.bias != nullptr) v[j] = v[j] + b[j];
                             }
@@ -482,10 +542,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                             for (int q = 0; q < 4; ++q) {
                                 const int n = nbase + 8 * q;
                                 if (n < p.N)
-                                    store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(acc[i][f][4 * q + 0]),
-                                                    fix_acc<WK>(acc[i][f][4 * q + 1]),
-                                                    fix_acc<WK>(acc[i][f][4 * q + 2]),
-                                                    fix_acc<WK>(acc[i][f][4 * q + 3]));
+                                    store4<WK, ACC>(epi, m, n, sxm, sw0, acc[i][f][4 * q + 0], acc[i][f][4 * q + 1],
+                                                    acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
                             }
                         }
                     }
@@ -580,8 +638,7 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
     for (int q = 0; q < 4; ++q) {
         const int n = nbase + 8 * q;
         if (n < p.N)
-            store4<WK, ACC>(epi, m, n, sxm, sw0, fix_acc<WK>(sum[q].x), fix_acc<WK>(sum[q].y),
-                            fix_acc<WK>(sum[q].z), fix_acc<WK>(sum[q].w));
+            store4<WK, ACC>(epi, m, n, sxm, sw0, sum[q].x, sum[q].y, sum[q].z, sum[q].w);
     }
 }
 

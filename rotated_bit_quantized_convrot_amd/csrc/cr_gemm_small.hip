@@ -30,7 +30,7 @@ namespace cr {
 // int32 sums meet in LDS and each wave adds up and finishes a share of the
 // NT x MT output tiles: epilogue when the block covers all of K, else an
 // int32 partial tile for k_small_reduce.  W4A4 activations arrive packed
-// (4-bit, same layout as the weights, rows = m), the others as int8.
+// (4-bit tiles, rows = m, activation nibble forms), the others as int8.
 // ---------------------------------------------------------------------------
 constexpr int SM_W = 8;   // waves per block
 
@@ -41,12 +41,6 @@ template <> struct SmW<WK_I8> { v4i a; };
 template <> struct SmW<WK_W4A8> { v2i a; int c; };
 template <int WK> struct SmA { v4i a; };             // int8 activations
 template <> struct SmA<WK_W4> { v2i a; };            // packed 4-bit activations
-
-template <int WK>
-__device__ __forceinline__ int small_fix(int v) {
-    if constexpr (WK == WK_W4) return v >> 8;        // both operands carry a factor 16
-    else return v;
-}
 
 template <int WK, int MT, int NT, int CPW>
 __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int cps, int acc_mode) {
@@ -116,7 +110,6 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
         }
     }
     constexpr int AT = WK == WK_W4 ? 1024 : 64;                        // activation bytes per chunk step
-    // (this kernel runs only where the small-M plan exists, so W4A4 codes are packed)
     const uint32_t a_bytes = WK == WK_W4 ? (uint32_t)round_up(p.M, 32) * (uint32_t)(p.K / 2)
                                          : (uint32_t)p.M * (uint32_t)p.Kp;
     const auto rs_a = buf_rsrc(p.qx, a_bytes);
@@ -174,7 +167,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
             if constexpr (WK == WK_W4) {
-                b[j] = unpack_w4x16((uint32_t)ar[i][j].a.x, (uint32_t)ar[i][j].a.y);
+                b[j] = unpack_act4((uint32_t)ar[i][j].a.x, (uint32_t)ar[i][j].a.y);
             } else {
                 b[j] = ar[i][j].a;
             }
@@ -183,7 +176,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
         for (int t = 0; t < NT; ++t) {
             v4i a;
             if constexpr (WK == WK_W4) {
-                a = unpack_w4x16((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y);
+                a = unpack_wt4((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y);
             } else if constexpr (WK == WK_I8) {
                 a = wr[i][t].a;
             } else {
@@ -227,14 +220,11 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
         const int m = j * 16 + r16, n = nt * 16 + 4 * g;
         if (m >= p.M || n >= p.N) continue;
         if (acc_mode)
-            store4<WK, true>(epi, m, n, 0.0f, 0.0f, small_fix<WK>(sum.x), small_fix<WK>(sum.y),
-                             small_fix<WK>(sum.z), small_fix<WK>(sum.w));
+            store4<WK, true>(epi, m, n, 0.0f, 0.0f, sum.x, sum.y, sum.z, sum.w);
         else if (pre[k].full)
-            store4_pre(epi, pre[k], m, n, small_fix<WK>(sum.x), small_fix<WK>(sum.y), small_fix<WK>(sum.z),
-                       small_fix<WK>(sum.w));
+            store4_pre<WK>(epi, pre[k], m, n, sum.x, sum.y, sum.z, sum.w);
         else
-            store4<WK, false>(epi, m, n, p.sx[m], sw0, small_fix<WK>(sum.x), small_fix<WK>(sum.y),
-                              small_fix<WK>(sum.z), small_fix<WK>(sum.w));
+            store4<WK, false>(epi, m, n, p.sx[m], sw0, sum.x, sum.y, sum.z, sum.w);
     }
 }
 
@@ -263,12 +253,10 @@ __global__ void __launch_bounds__(256) k_small_reduce(GemmArgs p, int mt, int ac
     }
     const Epi epi = make_epi(p);
     if (acc_mode) {
-        store4<WK, true>(epi, m, n, 0.0f, 0.0f, small_fix<WK>(a.x), small_fix<WK>(a.y), small_fix<WK>(a.z),
-                         small_fix<WK>(a.w));
+        store4<WK, true>(epi, m, n, 0.0f, 0.0f, a.x, a.y, a.z, a.w);
     } else {
         const float sw0 = (WK == WK_W4A8) ? 0.0f : p.wscale[0];
-        store4<WK, false>(epi, m, n, p.sx[m], sw0, small_fix<WK>(a.x), small_fix<WK>(a.y), small_fix<WK>(a.z),
-                          small_fix<WK>(a.w));
+        store4<WK, false>(epi, m, n, p.sx[m], sw0, a.x, a.y, a.z, a.w);
     }
 }
 
@@ -399,16 +387,6 @@ static hipError_t launch_small_t(const GemmArgs& a, const SmallPlan& sp, hipStre
         case 8: return launch_small_m<WK, 8>(a, sp, st);
         default: return hipErrorInvalidValue;
     }
-}
-
-// Whether a small-M plan exists does not depend on N (only its cost does).
-bool act_packed(int kind, int M, int K) {
-    return kind == WK_W4 && plan_small(kind, M, 16, K).use;
-}
-
-size_t act_bytes(int kind, int M, int K) {
-    if (act_packed(kind, M, K)) return (size_t)round_up(M, 32) * (size_t)K / 2;
-    return (size_t)M * (size_t)(kind == WK_I8 ? round_up(K, 64) : K);
 }
 
 hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) {

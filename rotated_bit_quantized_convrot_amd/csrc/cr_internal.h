@@ -10,17 +10,33 @@ enum WKind { WK_W4 = 0, WK_I8 = 1, WK_W4A8 = 2 };
 
 // Packed-weight geometry.
 //   Np = N rounded up to 32 (rows past N are zero), Kp = K rounded up to 64.
-//   W4 / W4A8 indices: 1 KiB tiles (32 rows x 64 k), tile (nb, kc) at
-//     (nb * Kp/64 + kc) * 1024; row r at r*32; the 16 bytes at 16h hold
-//     k = 32t + 16h + 8d + {0..3 low nibbles, 4..7 high nibbles} of byte
-//     8t + 4d + b.
+//   4-bit tiles (W4 codes, W4A8 indices, W4A4 activations): 1 KiB tiles
+//     (32 rows x 64 k), tile (nb, kc) at (nb * Kp/64 + kc) * 1024; row r at
+//     r*32; dword d of the 8 bytes at 16h + 8t holds k0 + 0..7,
+//     k0 = 64kc + 32t + 16h + 8d, byte b carrying k0 + b and k0 + 4 + b.
 //   int8: 2 KiB tiles, row r at r*64, byte 32h + 16t + p holds k = 32t + 16h + p.
+//
+// W4A4 nibble forms.  CDNA4 has no 4-bit integer MFMA: the codes are
+// widened to int8 in registers, one AND per dword, by using two forms of a
+// code c in [-8, 7]: in a high nibble as two's complement (the byte masked
+// with 0xF0 is the int8 16c), in a low nibble offset-binary (c ^ 8, the byte
+// masked with 0x0F is c + 8).  Activations keep k0 + b in the low nibble and
+// k0 + 4 + b in the high one, weights the other way round, so every k pairs
+// one operand's high form with the other's low form and contributes
+// 16 a w + 128 x (x the code in the high form).  Hence
+//   sum_k a[m,k] w[n,k] = (acc >> 4) - 8 (ra[m] + cw[n]),
+// ra / cw the sums of a row's codes held in high nibbles (activations:
+// k % 8 >= 4; weights: k % 8 < 4), int32 vectors next to the codes.
+// Bound: |acc| <= 16 * 64 K + 128 * 8 K = 2048 K < 2^31 for K <= 2^20.
 //   W4A8 extra: scale codes, 128-byte tiles, row r at r*4, byte 2t + h is the
 //     code of group (64kc + 32t + 16h)/16; then the 4 KiB decode table
 //     T[c*16 + i] = clamp(rint(codebook[i] * e4m3(c)), -127, 127).
 __host__ __device__ inline int round_up(int v, int a) { return (v + a - 1) / a * a; }
 __host__ __device__ inline size_t w4_bytes(int N, int K) { return (size_t)round_up(N, 32) * (size_t)K / 2; }
 __host__ __device__ inline size_t i8_bytes(int N, int K) { return (size_t)round_up(N, 32) * (size_t)round_up(K, 64); }
+// W4A4 packed weight: codes, then cw int32 [Np].
+__host__ __device__ inline size_t w4_cw_offset(int N, int K) { return w4_bytes(N, K); }
+__host__ __device__ inline size_t w4a4_bytes(int N, int K) { return w4_bytes(N, K) + 4 * (size_t)round_up(N, 32); }
 __host__ __device__ inline size_t w4a8_codes_offset(int N, int K) { return w4_bytes(N, K); }
 __host__ __device__ inline size_t w4a8_table_offset(int N, int K) {
     return w4_bytes(N, K) + (size_t)round_up(N, 32) * (size_t)K / 16;
@@ -29,10 +45,11 @@ __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_o
 
 // Activation quantisation: codes int8 [M, Kp] (row-major, zero for k >= K)
 // and scales [M]; with `packed` (W4A4 only) the codes go out 4-bit in the
-// packed weight layout with rows = m (round_up(M, 32) rows, rows >= M left
-// untouched).
+// 4-bit tile layout with rows = m (round_up(M, 32) rows, rows >= M left
+// untouched), in the activation nibble forms, and ra [M] (the sums of the
+// codes in high nibbles) beside them.
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, bool packed, hipStream_t st);
+                            float* sx, int32_t* ra, bool packed, hipStream_t st);
 
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
                           hipStream_t st);
@@ -54,6 +71,8 @@ struct GemmArgs {
     uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
     int32_t* acc_out;      // [M, N] int32 accumulators instead of y
     int32_t* part;         // split-K partial sums (workspace)
+    const int32_t* ra;     // W4A4: activation high-nibble code sums [M]
+    const int32_t* cw;     // W4A4: weight high-nibble code sums [Np]
 };
 
 // Large-M path plan: K split into `splits` equal slices of `cps` 64-k chunks
@@ -87,11 +106,14 @@ struct SmallPlan {
 SmallPlan plan_small(int kind, int M, int N, int K);
 hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st);
 
-// Whether the activations of a linear are stored packed 4-bit (W4A4 on the
-// small-M path) rather than as int8 [M, Kp]; the same for every N.
-bool act_packed(int kind, int M, int K);
+// Whether the activations of a linear are stored packed 4-bit (W4A4)
+// rather than as int8 [M, Kp].
+inline bool act_packed(int kind) { return kind == WK_W4; }
 // Bytes of the activation codes in the workspace.
-size_t act_bytes(int kind, int M, int K);
+inline size_t act_bytes(int kind, int M, int K) {
+    if (act_packed(kind)) return (size_t)round_up(M, 32) * (size_t)K / 2;
+    return (size_t)M * (size_t)(kind == WK_I8 ? round_up(K, 64) : K);
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 

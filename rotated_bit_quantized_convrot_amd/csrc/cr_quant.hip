@@ -102,11 +102,15 @@ __device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
 // whose 16 products come that close redoes them with the division.  |v/s_u|
 // <= QMAX (1 + 2^-23) keeps the fast codes inside [LO, HI].  Rows outside
 // the range take the literal path.
+//
+// PACKED (W4A4): codes in the 4-bit tile layout, activation nibble forms,
+// and ra[m] = the sum of the row's codes held in high nibbles (k % 8 >= 4).
 template <int GPL, int QMAX, int LO, int HI, bool PACKED>
 __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
                                                         int seg_log2, int8_t* __restrict__ qx,
-                                                        float* __restrict__ sx) {
+                                                        float* __restrict__ sx, int32_t* __restrict__ ra) {
     __shared__ float red[16];
+    __shared__ int ired[16];
     const int tid = threadIdx.x;
     int m, l, seg;
     if (seg_log2 >= 0) {
@@ -157,6 +161,7 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
     const float s_u = amax / (float)QMAX;
     const float rinv = sigma * (1.0f / s_u);          // undoes the lane's sign too
 
+    int hsum = 0;                                      // PACKED: codes going to high nibbles
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
         const int g = gslot + i * gstride;
@@ -187,22 +192,37 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
             o.z = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
             o.w = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
             if constexpr (PACKED) {
-                // 4-bit weight layout with rows = m: the lane's k0..k0+15
+                // 4-bit tile layout with rows = m: the lane's k0..k0+15
                 // (k0 = 256 g + 16 j) are the dwords (t, d = 0, 1) of half h
                 // of chunk k0 / 64, t = (k0 / 32) & 1, h = (k0 / 16) & 1;
-                // byte b of dword d holds k0 + 8d + b (low nibble) and
-                // k0 + 8d + 4 + b (high nibble).
+                // byte b of dword d holds k0 + 8d + b (low nibble,
+                // offset-binary: code ^ 8) and k0 + 8d + 4 + b (high nibble,
+                // two's complement).
                 const int k0 = g * 256 + j * 16;
                 const int kc = k0 >> 6, t = (k0 >> 5) & 1, h = (k0 >> 4) & 1;
                 const size_t off = ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
                 uint2 pk;
-                pk.x = (o.x & 0x0F0F0F0Fu) | ((o.y << 4) & 0xF0F0F0F0u);
-                pk.y = (o.z & 0x0F0F0F0Fu) | ((o.w << 4) & 0xF0F0F0F0u);
+                pk.x = ((o.x ^ 0x08080808u) & 0x0F0F0F0Fu) | ((o.y << 4) & 0xF0F0F0F0u);
+                pk.y = ((o.z ^ 0x08080808u) & 0x0F0F0F0Fu) | ((o.w << 4) & 0xF0F0F0F0u);
+                hsum += (int)(r[4] + r[5] + r[6] + r[7] + r[12] + r[13] + r[14] + r[15]);
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + off) = pk;
             } else {
                 *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
             }
         }
+    }
+    if constexpr (PACKED) {
+        // row sum over the segment (and, one row per block, over its waves)
+        const int sg = seg < 64 ? seg : 64;
+        for (int o = 1; o < sg; o <<= 1) hsum += __shfl_xor(hsum, o, 64);
+        if (seg > 64) {
+            const int wave = tid >> 6, nw = blockDim.x >> 6;
+            if ((tid & 63) == 0) ired[wave] = hsum;
+            __syncthreads();
+            hsum = 0;
+            for (int i = 0; i < nw; ++i) hsum += ired[i];
+        }
+        if (l == 0) ra[m] = hsum;
     }
 }
 
@@ -254,19 +274,17 @@ static int rot_threads(int G, int* gpl) {
     int g = 1;
     while (g < per) g <<= 1;
     *gpl = g;
-    int threads = nhw * 32;
-    if (threads < 64) threads = 64;
-    return threads;
+    return round_up(nhw * 32, 64);      // whole waves (half-waves past G idle)
 }
 
 template <int QMAX, int LO, int HI, bool PACKED>
-static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, hipStream_t st) {
+static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, int32_t* ra, hipStream_t st) {
     const int T = K / 16;              // lanes per row
     if (T <= 64) {
         int lg = 4;
         while ((1 << lg) < T) ++lg;
         const int rows = 256 >> lg;
-        k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx);
+        k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx, ra);
         return hipGetLastError();
     }
     int gpl = 1;
@@ -274,21 +292,22 @@ static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float*
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, bool packed, hipStream_t st) {
+                            float* sx, int32_t* ra, bool packed, hipStream_t st) {
     if (kind == WK_W4) {
-        return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, st)
-                      : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, st);
+        if (packed && ra == nullptr) return hipErrorInvalidValue;
+        return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, ra, st)
+                      : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, nullptr, st);
     }
-    if (kind == WK_W4A8) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, st);
+    if (kind == WK_W4A8) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
     k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
 }
@@ -313,12 +332,12 @@ __global__ void __launch_bounds__(512) k_absmax_rot_rows(const uint16_t* __restr
     if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(a));
 }
 
-// One dword of the W4 layout from 8 codes of k0..k0+7 (k0 % 8 == 0):
-// byte b = code(k0+b) | code(k0+4+b) << 4.
+// One dword of the W4 layout from 8 codes of k0..k0+7 (k0 % 8 == 0), the
+// weight nibble forms: byte b = (code(k0+4+b) ^ 8) | code(k0+b) << 4.
 __device__ __forceinline__ uint32_t w4_dword(const int (&q)[8]) {
     uint32_t o = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) o |= ((uint32_t)(q[b] & 0xF) | ((uint32_t)(q[b + 4] & 0xF) << 4)) << (8 * b);
+    for (int b = 0; b < 4; ++b) o |= ((uint32_t)((q[b + 4] ^ 8) & 0xF) | ((uint32_t)(q[b] & 0xF) << 4)) << (8 * b);
     return o;
 }
 
@@ -329,23 +348,30 @@ __device__ __forceinline__ size_t w4_dword_offset(int n, int k0, int K) {
     return ((size_t)nb * (K >> 6) + kc) * 1024 + r * 32 + 16 * h + 8 * t + 4 * d;
 }
 
+// One block per row (padding rows: zero codes); also cw[n], the sum of the
+// row's codes held in high nibbles (k % 8 < 4).
 template <int GPL>
 __global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w, int N, int K,
                                                  const float* __restrict__ amax_slot,
                                                  uint8_t* __restrict__ out) {
+    __shared__ int tot;
     const int n = blockIdx.x;
     const int G = K >> 8;
     const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
+    int32_t* cw = reinterpret_cast<int32_t*>(out + w4_cw_offset(N, K));
     if (n >= N) {  // padding rows
         for (int i = 0; i < GPL; ++i) {
             const int g = hw + i * nhw;
-            if (g < G) *reinterpret_cast<uint32_t*>(out + w4_dword_offset(n, g * 256 + lane32 * 8, K)) = 0u;
+            if (g < G) *reinterpret_cast<uint32_t*>(out + w4_dword_offset(n, g * 256 + lane32 * 8, K)) = 0x08080808u;
         }
+        if (threadIdx.x == 0) cw[n] = 0;
         return;
     }
+    if (threadIdx.x == 0) tot = 0;
     const float s = amax_slot[0] / 7.0f;
     RotRow<GPL> r;
     r.load_rotate(w + (size_t)n * K, G, hw, nhw, lane32);
+    int hsum = 0;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
         const int g = hw + i * nhw;
@@ -354,8 +380,13 @@ __global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w,
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = quant_code<-8, 7>(r.v[i][j], s);
             *reinterpret_cast<uint32_t*>(out + w4_dword_offset(n, g * 256 + lane32 * 8, K)) = w4_dword(q);
+            hsum += q[0] + q[1] + q[2] + q[3];
         }
     }
+    __syncthreads();
+    atomicAdd(&tot, hsum);
+    __syncthreads();
+    if (threadIdx.x == 0) cw[n] = tot;
 }
 
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
@@ -517,10 +548,10 @@ __global__ void __launch_bounds__(256) k_unpack_weight(int kind, const uint8_t* 
     } else {
         const int d = pp >> 3, b = pp & 3, hi = (pp >> 2) & 1;
         const uint8_t byte = p[tile * 1024 + r * 32 + 16 * h + 8 * t + 4 * d + b];
-        const int nib = hi ? (byte >> 4) : (byte & 0xF);
-        if (kind == WK_W4) {
-            v = nib >= 8 ? nib - 16 : nib;
+        if (kind == WK_W4) {          // k0 + b high (two's complement), k0 + 4 + b low (offset)
+            v = hi ? (int)(byte & 0xF) - 8 : (int)(int8_t)(byte & 0xF0) >> 4;
         } else {
+            const int nib = hi ? (byte >> 4) : (byte & 0xF);
             const uint8_t code = p[codes_off + tile * 128 + r * 4 + 2 * t + h];
             v = (int8_t)p[table_off + (size_t)code * 16 + nib];
         }

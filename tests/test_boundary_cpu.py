@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_sizes(L):
-    # W4A4: N rounded to 32 rows, two codes per byte
-    assert L.cr_packed_bytes(0, 12288, 3072) == 12288 * 3072 // 2
-    assert L.cr_packed_bytes(0, 100, 512) == 128 * 256
+    # W4A4: N rounded to 32 rows, two codes per byte, one int32 per row
+    assert L.cr_packed_bytes(0, 12288, 3072) == 12288 * 3072 // 2 + 12288 * 4
+    assert L.cr_packed_bytes(0, 100, 512) == 128 * 256 + 128 * 4
     # int8tw: rows to 32, K to 64
     assert L.cr_packed_bytes(1, 2688, 2688) == 2688 * 2688
     assert L.cr_packed_bytes(1, 7, 100) == 32 * 128
@@ -53,10 +53,11 @@ def test_sizes(L):
     assert L.cr_packed_bytes(0, 256, 2688) == 0
     assert L.cr_packed_bytes(0, 0, 256) == 0
     assert L.cr_packed_bytes(7, 256, 256) == 0
-    # workspace: W4A4 codes packed 4-bit at small M (rows rounded up to 32),
-    # int8 [M, K] otherwise; then the per-row scales
-    assert L.cr_workspace_bytes(0, 76, 9728, 2560) >= 96 * 2560 // 2 + 76 * 4
-    assert L.cr_workspace_bytes(0, 4096, 12288, 3072) >= 4096 * 3072 + 4096 * 4
+    # workspace: W4A4 codes packed 4-bit (rows rounded up to 32) with an
+    # int32 per row, int8 [M, K] otherwise; then the per-row scales
+    assert L.cr_workspace_bytes(0, 76, 9728, 2560) >= 96 * 2560 // 2 + 76 * 8
+    assert L.cr_workspace_bytes(0, 4096, 12288, 3072) >= 4096 * 3072 // 2 + 4096 * 8
+    assert L.cr_workspace_bytes(0, 4096, 12288, 3072) < 4096 * 3072
     assert L.cr_workspace_bytes(1, 76, 3072, 2688) >= 76 * 2688 + 76 * 4
     assert L.cr_workspace_bytes(1, -1, 16, 16) == 0
 
