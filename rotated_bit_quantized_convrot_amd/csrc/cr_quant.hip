@@ -82,6 +82,52 @@ __device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
     return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
+// Codes of a lane's 16 rotated values (unscaled, sign-tracked), see below.
+template <int QMAX, int LO, int HI>
+__device__ __forceinline__ void codes16(const float (&v)[16], bool fast, float rinv, float sigma, float s_u,
+                                        float s, float (&r)[16]) {
+    if (fast) {
+        float dmax = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const float q = v[t] * rinv;
+            r[t] = __builtin_rintf(q);
+            dmax = fmaxf(dmax, fabsf(q - r[t]));
+        }
+        if (dmax > 0.5f - (float)QMAX * 9.5367431640625e-07f) {   // within QMAX * 2^-20 of a tie
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const float q = __builtin_rintf((sigma * v[t]) / s_u);
+                r[t] = fminf(fmaxf(q, (float)LO), (float)HI);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[t]) * 0.0625f, s);
+    }
+}
+
+// W4A4 codes of 16 consecutive k (k0 % 16 == 0) in the activation nibble
+// forms: the two dwords of the 4-bit tile layout, byte b of dword d holding
+// k0 + 8d + b (low nibble, code ^ 8) and k0 + 8d + 4 + b (high nibble).
+__device__ __forceinline__ uint2 pack_act16(const float (&r)[16]) {
+    const uint32_t x0 = pack4_codes((int)r[0], (int)r[1], (int)r[2], (int)r[3]);
+    const uint32_t x1 = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
+    const uint32_t x2 = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
+    const uint32_t x3 = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
+    uint2 pk;
+    pk.x = ((x0 ^ 0x08080808u) & 0x0F0F0F0Fu) | ((x1 << 4) & 0xF0F0F0F0u);
+    pk.y = ((x2 ^ 0x08080808u) & 0x0F0F0F0Fu) | ((x3 << 4) & 0xF0F0F0F0u);
+    return pk;
+}
+
+// Byte offset of the 8 bytes of row m, k0..k0+15 (k0 % 16 == 0) in the 4-bit
+// tile layout with rows = m: dwords (t, d = 0, 1) of half h of chunk k0 / 64.
+__device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
+    const int kc = k0 >> 6, t = (k0 >> 5) & 1, h = (k0 >> 4) & 1;
+    return ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
+}
+
 // Rotated activations: codes [M, K] int8 (natural order) and scales [M].
 //
 // Each row is handled by a segment of lanes: 16 lanes per 256-group, each
@@ -167,46 +213,17 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
         const int g = gslot + i * gstride;
         if (g < G) {
             float r[16];
-            if (fast) {
-                float dmax = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const float q = v[i][t] * rinv;
-                    r[t] = __builtin_rintf(q);
-                    dmax = fmaxf(dmax, fabsf(q - r[t]));
-                }
-                if (dmax > 0.5f - (float)QMAX * 9.5367431640625e-07f) {   // within QMAX * 2^-20 of a tie
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        const float q = __builtin_rintf((sigma * v[i][t]) / s_u);
-                        r[t] = fminf(fmaxf(q, (float)LO), (float)HI);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[i][t]) * 0.0625f, s);
-            }
-            uint4 o;
-            o.x = pack4_codes((int)r[0], (int)r[1], (int)r[2], (int)r[3]);
-            o.y = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
-            o.z = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
-            o.w = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
+            codes16<QMAX, LO, HI>(v[i], fast, rinv, sigma, s_u, s, r);
             if constexpr (PACKED) {
-                // 4-bit tile layout with rows = m: the lane's k0..k0+15
-                // (k0 = 256 g + 16 j) are the dwords (t, d = 0, 1) of half h
-                // of chunk k0 / 64, t = (k0 / 32) & 1, h = (k0 / 16) & 1;
-                // byte b of dword d holds k0 + 8d + b (low nibble,
-                // offset-binary: code ^ 8) and k0 + 8d + 4 + b (high nibble,
-                // two's complement).
-                const int k0 = g * 256 + j * 16;
-                const int kc = k0 >> 6, t = (k0 >> 5) & 1, h = (k0 >> 4) & 1;
-                const size_t off = ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
-                uint2 pk;
-                pk.x = ((o.x ^ 0x08080808u) & 0x0F0F0F0Fu) | ((o.y << 4) & 0xF0F0F0F0u);
-                pk.y = ((o.z ^ 0x08080808u) & 0x0F0F0F0Fu) | ((o.w << 4) & 0xF0F0F0F0u);
+                const size_t off = act4_offset(m, g * 256 + j * 16, K);
                 hsum += (int)(r[4] + r[5] + r[6] + r[7] + r[12] + r[13] + r[14] + r[15]);
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + off) = pk;
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + off) = pack_act16(r);
             } else {
+                uint4 o;
+                o.x = pack4_codes((int)r[0], (int)r[1], (int)r[2], (int)r[3]);
+                o.y = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
+                o.z = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
+                o.w = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
                 *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
             }
         }
@@ -223,6 +240,77 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
             for (int i = 0; i < nw; ++i) hsum += ired[i];
         }
         if (l == 0) ra[m] = hsum;
+    }
+}
+
+// W4A4 activations, four rows per block: lanes 16r..16r+15 of every wave
+// work on row 4 blockIdx.x + r, wave w on groups w, w + nw, ... (GPL at
+// most), so that each store instruction writes, for every 64-k chunk it
+// touches, the four rows' 32-byte pieces: one whole 128-byte line of the
+// 4-bit tile.  Same arithmetic as k_quant_act_rot (PACKED).
+template <int GPL>
+__global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, int M, int K,
+                                                         int8_t* __restrict__ qx, float* __restrict__ sx,
+                                                         int32_t* __restrict__ ra) {
+    __shared__ float redm[16][4];
+    __shared__ int reds[16][4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6, nw = blockDim.x >> 6;
+    const int r = lane >> 4, j = lane & 15;
+    const int m = blockIdx.x * 4 + r;
+    const int G = K >> 8;
+    const bool row_ok = m < M;
+
+    float v[GPL][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = wave + i * nw;
+        if (row_ok && g < G) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)g * 256 + j * 16);
+            const uint4 r0 = src[0], r1 = src[1];
+            const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                v[i][2 * t] = bf16_lo(w[t]);
+                v[i][2 * t + 1] = bf16_hi(w[t]);
+            }
+            fwht256_x16_signed(v[i], j);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
+        }
+    }
+    amax = seg_max(amax, 16);
+    if (j == 0) redm[wave][r] = amax;
+    __syncthreads();
+    amax = 0.0f;
+    for (int w = 0; w < nw; ++w) amax = fmaxf(amax, redm[w][r]);
+
+    const float s = (amax * 0.0625f) / 7.0f;
+    const float sigma = fwht_x16_sign(j);
+    const bool fast = amax >= 0x1p-100f && amax <= 0x1p100f;
+    const float s_u = amax / 7.0f;
+    const float rinv = sigma * (1.0f / s_u);
+    int hsum = 0;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = wave + i * nw;
+        if (row_ok && g < G) {
+            float c[16];
+            codes16<7, -8, 7>(v[i], fast, rinv, sigma, s_u, s, c);
+            hsum += (int)(c[4] + c[5] + c[6] + c[7] + c[12] + c[13] + c[14] + c[15]);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + act4_offset(m, g * 256 + j * 16, K)) =
+                pack_act16(c);
+        }
+    }
+    for (int o = 1; o < 16; o <<= 1) hsum += __shfl_xor(hsum, o, 64);
+    if (j == 0) reds[wave][r] = hsum;
+    __syncthreads();
+    if (wave == 0 && j == 0 && row_ok) {
+        int t = 0;
+        for (int w = 0; w < nw; ++w) t += reds[w][r];
+        ra[m] = t;
+        sx[m] = s;
     }
 }
 
@@ -304,6 +392,22 @@ hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, i
                             float* sx, int32_t* ra, bool packed, hipStream_t st) {
     if (kind == WK_W4) {
         if (packed && ra == nullptr) return hipErrorInvalidValue;
+        const int G = K >> 8;
+        // four rows per block where there are rows enough to fill the chip
+        // with such blocks (at smaller M one row per block keeps more lanes busy)
+        if (packed && G <= 64 && M >= 2048) {
+            int gpl = 1;
+            while ((G + gpl - 1) / gpl > 16) gpl <<= 1;
+            const int nw = (G + gpl - 1) / gpl;
+            const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
+            switch (gpl) {
+                case 1: k_quant_w4_rows4<1><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+                case 2: k_quant_w4_rows4<2><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+                case 4: k_quant_w4_rows4<4><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
         return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, ra, st)
                       : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, nullptr, st);
     }
