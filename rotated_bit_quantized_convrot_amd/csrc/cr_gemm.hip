@@ -363,13 +363,24 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     // One stage in buffer B: publish stage B+1 (and free the buffer of the
     // previous stage), refill it, read the next stage's fragments into the
     // other register set, then run this stage's 16 MFMAs back to back.
+    // PAIR (rings of 6 or more): stages go in pairs with one barrier; an
+    // even step publishes stages B+1 and B+2 and refills the buffers of B-1
+    // and B, whose fragments every wave has read before that barrier.
+    constexpr bool PAIR = NS >= 6;
     auto step = [&](auto BUF) {
         constexpr int B = decltype(BUF)::value;
         Frags& cur = (B & 1) ? F1 : F0;
         Frags& nxt = (B & 1) ? F0 : F1;
-        wait_vmcnt<(NS - 3) * C::LPS>();
-        lds_barrier();
-        issue_stage(IntC<(B + NS - 1) % NS>{});
+        if constexpr (!PAIR) {
+            wait_vmcnt<(NS - 3) * C::LPS>();
+            lds_barrier();
+            issue_stage(IntC<(B + NS - 1) % NS>{});
+        } else if constexpr ((B & 1) == 0) {
+            wait_vmcnt<(NS - 4) * C::LPS>();
+            lds_barrier();
+            issue_stage(IntC<(B + NS - 1) % NS>{});
+            issue_stage(IntC<B % NS>{});
+        }
         // W4A8: the last stage of a tile reads the next stage's fragments
         // after the epilogue instead (fewer registers live across it; the
         // other formats have them to spare and keep the plain schedule).
