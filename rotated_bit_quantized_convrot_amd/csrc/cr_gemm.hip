@@ -86,55 +86,63 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 constexpr int BIG_BM = 256;
-constexpr int BIG_WM = 2;   // waves along m in the large-M kernel (wave tile 128 x 64)
 
-// Origin of output tile `lid` (0 .. tiles_m * tiles_n - 1): tiles are taken in
-// bands of 8 tile-rows, column by column inside a band, so that consecutive
-// ids share weight columns and activation rows.
-__device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_n, int& m0, int& n0) {
+// Origin of output tile `lid` (0 .. tiles_m * tiles_n - 1) of width bn: tiles
+// are taken in bands of 8 tile-rows, column by column inside a band, so that
+// consecutive ids share weight columns and activation rows.
+__device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_n, int bn, int& m0, int& n0) {
     constexpr int GM = 8;
     const int band = lid / (GM * tiles_n);
     const int first_m = band * GM;
     const int gm = min(tiles_m - first_m, GM);
     const int in_band = lid - band * GM * tiles_n;
     m0 = (first_m + in_band % gm) * BIG_BM;
-    n0 = (in_band / gm) * 256;
+    n0 = (in_band / gm) * bn;
 }
 
-// NW waves (2 along m x NW/2 along n; wave tile 128 x 512/NW), block tile
-// 256 x 256, NS-stage LDS ring.
-template <int WK, int NW, int NS>
+// 8 waves, block tile 256 (m) x BN (n), NS-stage LDS ring.  BN = 256: 2
+// waves along m x 4 along n, wave tile 128 x 64; BN = 192 (fills the chip
+// where 256-wide tiles leave CUs idle): 4 x 2, wave tile 64 x 96.
+template <int WK, int NW, int NS, int BN_>
 struct BigCfg {
-    static constexpr int BN = 256;
+    static_assert(NW == 8, "8 waves");
+    static_assert(BN_ == 256 || BN_ == 192, "block tile width");
+    static constexpr int BN = BN_;
+    static constexpr int NWT = BN / 32;                                // 32-row weight tiles per stage
+    static constexpr int WM = BN == 256 ? 2 : 4;                       // waves along m
+    static constexpr int WNW = NW / WM;                                // waves along n
+    static constexpr int WROWS = BIG_BM / WM, FM = WROWS / 32, FN = NWT / WNW;
     static constexpr bool PA = WK == WK_W4;                            // 4-bit activation tiles
-    static constexpr int TPW = 8 / NW;                                 // 32-row weight tiles loaded per wave
+    static constexpr int BSTEP = WK == WK_I8 ? 2048 : 1024;            // bytes of a weight tile's stage
     static constexpr int A_BYTES = PA ? BIG_BM * 32 : BIG_BM * 64;    // activations per stage
-    static constexpr int B_BYTES = WK == WK_I8 ? BN * 64 : BN * 32;
-    static constexpr int C_BYTES = WK == WK_W4A8 ? BN * 4 : 0;        // W4A8 scale codes
+    static constexpr int B_BYTES = NWT * BSTEP;
+    static constexpr int C_BYTES = WK == WK_W4A8 ? NWT * 128 : 0;     // W4A8 scale codes
     static constexpr int STAGE = A_BYTES + B_BYTES + C_BYTES;
-    static constexpr int LA = PA ? 8 / NW : 16 / NW;                   // activation loads per wave
-    // direct-to-LDS loads per wave per stage
-    static constexpr int LPS = LA + TPW * (WK == WK_I8 ? 2 : 1) + (WK == WK_W4A8 ? 1 : 0);
-    // LDS-staged epilogue: per wave 32 rows of EPI_TR bytes, then its 64
+    // Direct-to-LDS loads per wave per stage: each wave fills one NW-th of
+    // every operand's region, 1 KiB (64 lanes x 16 B) per load, the last one
+    // with fewer lanes where its share is not a whole KiB.
+    static constexpr int LA = A_BYTES / (NW * 1024);
+    static constexpr int WB = B_BYTES / NW, LW = (WB + 1023) / 1024;
+    static constexpr int CB = C_BYTES / NW;
+    static constexpr int LPS = LA + LW + (WK == WK_W4A8 ? 1 : 0);
+    // LDS-staged epilogue: per wave 32 rows of EPI_TR bytes, then its FN * 32
     // columns' bias (bf16), scale (fp32) and (W4A4) weight correction (int32)
     static constexpr int EPI_TR = 80;
-    static constexpr int EPI_OPB = 64 * 2 + 64 * 4 + (PA ? 64 * 4 : 0);
+    static constexpr int EPI_OPB = FN * 32 * (2 + 4 + (PA ? 4 : 0));
     static constexpr int EPI_BYTES = NW * (32 * EPI_TR + EPI_OPB);
     // W4A4 stages are too small to hold it: its own region after the ring
     static constexpr size_t EPI_OFF = (size_t)NS * STAGE;
     static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0) + (PA ? EPI_BYTES : 0);
+    static_assert(A_BYTES % (NW * 1024) == 0 && WB % 16 == 0 && CB % 16 == 0 && CB <= 1024, "load split");
 };
 
 // SPLIT: units are K slices whose int32 sums go to partial tiles (splits > 1);
 // otherwise every unit is a whole tile and splits == 1.
-template <int WK, int NW, int NS, bool ACC, bool SPLIT>
+template <int WK, int NW, int NS, int BN_, bool ACC, bool SPLIT>
 __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, int tiles_n, int splits, int cps) {
-    using C = BigCfg<WK, NW, NS>;
+    using C = BigCfg<WK, NW, NS, BN_>;
     constexpr int BN = C::BN;
-    // WM waves along m, NW/WM along n; wave tile (256/WM) x (256*WM/NW)
-    constexpr int WM = BIG_WM, WNW = NW / WM;
-    constexpr int WROWS = BIG_BM / WM;
-    constexpr int FM = WROWS / 32, FN = 8 / WNW;
+    constexpr int WM = C::WM, WROWS = C::WROWS, FM = C::FM, FN = C::FN;
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
     int8_t* ring = smem;
     uint4* sT = reinterpret_cast<uint4*>(smem + NS * C::STAGE);   // W4A8 decode table
@@ -172,7 +180,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         int lid = j * G + slot;
         if (lid >= units) lid = units - 1;           // only for the clamped tail re-reads
         const int sl = SPLIT ? lid / total : 0;
-        big_tile_origin(lid - sl * total, tiles_m, tiles_n, m0, n0);
+        big_tile_origin(lid - sl * total, tiles_m, tiles_n, BN, m0, n0);
         kc0 = sl * cps;
         uid = lid;
     };
@@ -184,7 +192,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     // past Np (weights) are outside the resource and load as zero.
     //   activations: rows 16*(LA*wave + j) + lane/4, chunk (lane%4) ^ swizzle
     //   weights: tile n0/32 + wave, this lane's row and half (swizzled)
-    constexpr int BSTEP = WK == WK_I8 ? 2048 : 1024;
+    constexpr int BSTEP = C::BSTEP;
     //   4-bit activations: 32-row tile `wave` of the block, like the weights
     static_assert(!C::PA || C::LA == 1, "one 4-bit activation tile per wave");
     constexpr int ASTEP = C::PA ? 1024 : 64;                    // activation bytes per 64-k step
@@ -198,20 +206,29 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             a_voff[j] = (uint32_t)(row * Kp + (((lane & 3) ^ ((row >> 2) & 3)) * 16));
         }
     }
-    uint32_t b_voff[C::TPW][2];
+    // weights / W4A8 codes: LDS byte o of the operand's stage region (this
+    // wave's share starts at wave * WB) comes from weight tile o / BSTEP of the
+    // block and, inside it, the swizzled position of slot (o % BSTEP) / 16
+    uint32_t b_voff[C::LW];
 #pragma unroll
-    for (int t = 0; t < C::TPW; ++t) {
-        const uint32_t tb = (uint32_t)((wave * C::TPW + t) * nkc * BSTEP);
+    for (int j = 0; j < C::LW; ++j) {
+        const int o = wave * C::WB + j * 1024 + lane * 16;
+        const int t = o / BSTEP, sl = (o % BSTEP) >> 4;
+        int src;
         if constexpr (WK == WK_I8) {
-            const int row0 = lane >> 2, row1 = row0 + 16;
-            b_voff[t][0] = tb + row0 * 64 + (((lane & 3) ^ ((row0 >> 2) & 3)) * 16);
-            b_voff[t][1] = tb + row1 * 64 + (((lane & 3) ^ ((row1 >> 2) & 3)) * 16);
+            const int r = sl >> 2;
+            src = r * 64 + (((sl & 3) ^ ((r >> 2) & 3)) * 16);
         } else {
-            b_voff[t][0] = tb + (lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) * 16);
-            b_voff[t][1] = b_voff[t][0];
+            const int r = sl >> 1;
+            src = r * 32 + (((sl & 1) ^ ((r >> 3) & 1)) * 16);
         }
+        b_voff[j] = (uint32_t)(t * nkc * BSTEP + src);
     }
-    const uint32_t c_voff = (uint32_t)((wave * C::TPW + (lane >> 3)) * nkc * 128 + (lane & 7) * 16);
+    uint32_t c_voff = 0;
+    if constexpr (WK == WK_W4A8) {
+        const int o = wave * C::CB + lane * 16;
+        c_voff = (uint32_t)((o / 128) * nkc * 128 + (o % 128));
+    }
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr)ring;
     v4i rs_a, rs_b, rs_c;
     uint32_t soff_a = 0, soff_b = 0, soff_c = 0;
@@ -238,15 +255,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
         for (int j = 0; j < C::LA; ++j)
             buf_lds16(rs_a, a_voff[j], soff_a, st + (C::PA ? wave * 1024 : 16 * (C::LA * wave + j) * 64));
-        const uint32_t sb = st + C::A_BYTES;
+        const uint32_t sb = st + C::A_BYTES + wave * C::WB;
 #pragma unroll
-        for (int t = 0; t < C::TPW; ++t) {
-            const uint32_t dst = sb + (wave * C::TPW + t) * BSTEP;
-            buf_lds16(rs_b, b_voff[t][0], soff_b, dst);
-            if constexpr (WK == WK_I8) buf_lds16(rs_b, b_voff[t][1], soff_b, dst + 1024);
+        for (int j = 0; j < C::LW; ++j) {
+            if (C::WB % 1024 == 0 || j + 1 < C::LW || lane < (C::WB % 1024) / 16)
+                buf_lds16(rs_b, b_voff[j], soff_b, sb + j * 1024);
         }
         if constexpr (WK == WK_W4A8) {
-            if (lane < 8 * C::TPW) buf_lds16(rs_c, c_voff, soff_c, st + C::A_BYTES + C::B_BYTES + wave * C::TPW * 128);
+            if (lane < C::CB / 16) buf_lds16(rs_c, c_voff, soff_c, st + C::A_BYTES + C::B_BYTES + wave * C::CB);
         }
         // advance (past the last stage the offsets stay put: the tail
         // re-reads it into a buffer that is never consumed)
@@ -487,19 +503,33 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                     if constexpr (C::PA) rnv[i] = -128 * p.ra[m];
                 }
                 const int nw0 = n0 + wn * FN * 32;            // the wave's first column
-                const uint16_t bl = p.bias != nullptr ? p.bias[nw0 + lane] : (uint16_t)0;
-                float cl = sw0;
-                if constexpr (WK == WK_W4A8) cl = p.wscale[nw0 + lane];
-                int cnl = 0;
-                if constexpr (C::PA) cnl = -128 * p.cw[nw0 + lane];
+                constexpr int NCW = FN * 32;                  // the wave's columns
+                constexpr int OS = NCW * 2, OC = NCW * 6;     // scale and correction offsets in sop
+                uint16_t bl[(NCW + 63) / 64];
+                float cl[(NCW + 63) / 64];
+                int cnl[(NCW + 63) / 64];
+#pragma unroll
+                for (int c = 0; c < (NCW + 63) / 64; ++c) {
+                    const int col = min(c * 64 + lane, NCW - 1);
+                    bl[c] = p.bias != nullptr ? p.bias[nw0 + col] : (uint16_t)0;
+                    cl[c] = sw0;
+                    if constexpr (WK == WK_W4A8) cl[c] = p.wscale[nw0 + col];
+                    cnl[c] = 0;
+                    if constexpr (C::PA) cnl[c] = -128 * p.cw[nw0 + col];
+                }
                 if constexpr (!C::PA) lds_barrier();          // stage buffer B is no longer read
-                reinterpret_cast<uint16_t*>(sop)[lane] = bl;
-                reinterpret_cast<float*>(sop + 128)[lane] = cl;
-                if constexpr (C::PA) reinterpret_cast<int*>(sop + 384)[lane] = cnl;
+#pragma unroll
+                for (int c = 0; c < (NCW + 63) / 64; ++c) {
+                    if (NCW % 64 == 0 || c * 64 + lane < NCW) {
+                        reinterpret_cast<uint16_t*>(sop)[c * 64 + lane] = bl[c];
+                        reinterpret_cast<float*>(sop + OS)[c * 64 + lane] = cl[c];
+                        if constexpr (C::PA) reinterpret_cast<int*>(sop + OC)[c * 64 + lane] = cnl[c];
+                    }
+                }
                 // per-lane bases; every other offset below is a constant
                 const int8_t* sbias = sop + 8 * h;            // bias of column 4h (+ 32f + 8q)
-                const int8_t* sscale = sop + 128 + 16 * h;    // scale of column 4h
-                const int8_t* scorr = sop + 384 + 16 * h;     // correction of column 4h
+                const int8_t* sscale = sop + OS + 16 * h;     // scale of column 4h
+                const int8_t* scorr = sop + OC + 16 * h;      // correction of column 4h
                 int8_t* swr = scr + l32 * TR + 8 * h;         // this lane's row, its 4 columns
                 const int8_t* srd = scr + (lane >> 2) * TR + (lane & 3) * 16;
 #pragma unroll
@@ -612,10 +642,11 @@ static int num_cus() {
 // every output tile (exact, so the result does not depend on the split) and
 // runs the epilogue.  One wavefront per 32 x 32 fragment (tile, wave, i, f)
 // of the GEMM kernel, reading the partials in the order they were stored.
-template <int WK, bool ACC>
+template <int WK, bool ACC, int BN>
 __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int tiles_n, int splits) {
-    constexpr int NW = BIG_NW, WM = BIG_WM, WNW = NW / WM, WROWS = BIG_BM / WM;
-    constexpr int FM = WROWS / 32, FN = 8 / WNW, FRAGS = NW * FM * FN;
+    using C = BigCfg<WK, BIG_NW, 4, BN>;            // tile geometry only
+    constexpr int NW = BIG_NW, WM = C::WM, WROWS = C::WROWS;
+    constexpr int FM = C::FM, FN = C::FN, FRAGS = NW * FM * FN;
     const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
     const int item = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
     const int total = tiles_m * tiles_n;
@@ -625,7 +656,7 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
     const int wave = r / (FM * FN), fi = r - wave * (FM * FN);
     const int i = fi / FN, f = fi - i * FN;
     int m0, n0;
-    big_tile_origin(t, tiles_m, tiles_n, m0, n0);
+    big_tile_origin(t, tiles_m, tiles_n, BN, m0, n0);
     const int m = m0 + (wave % WM) * WROWS + i * 32 + l32;
     const int4* src = reinterpret_cast<const int4*>(p.part) + (size_t)t * NW * FM * FN * 4 * 64 + r * 4 * 64 + lane;
     const size_t sstride = (size_t)total * NW * FM * FN * 4 * 64;   // int4 per K slice
@@ -653,51 +684,61 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
     }
 }
 
-// Large-M plan: the K slices per tile.  Rough time model in microseconds
-// (per 64-k stage of a 256 x 256 tile about 0.8 us for 4-bit weights, 1.0
-// for int8, 1.3 for W4A8; rounds of one unit per CU), plus for a split the
-// int32 partial tiles written and read back at about 4.5 TB/s and a second
-// launch.  Slices divide the K chunks evenly, at most 16.
+// Large-M plan: the block tile width and the K slices per tile.  Rough time
+// model in microseconds: per 64-k stage of a 256 x 256 tile about 0.8 us for
+// 4-bit weights, 1.0 for int8, 1.3 for W4A8, and 0.9 of that for a 256 x 192
+// tile (three quarters of the work; its 64 x 96 wave tiles read more LDS bytes
+// and widen more operands per MFMA, measured ~1.2x the time per op);
+// rounds of one unit per CU; plus, for a split, the int32 partial tiles
+// written and read back at about 4.5 TB/s and a second launch.  Anything
+// other than 256-wide whole tiles has to win by 5%.  Slices divide the K
+// chunks evenly, at most 16.  W4A8 keeps 256-wide tiles (its LDS has no room
+// for the narrower tile's epilogue scratch).
 constexpr int BIG_CUS = 256;
 constexpr int BIG_MAX_SPLITS = 16;
-constexpr size_t BIG_PART_TILE = (size_t)BIG_BM * 256 * 4;   // bytes of one int32 partial tile
 
 BigPlan plan_big(int kind, int M, int N, int K) {
-    BigPlan bp{1, 0, 0};
+    BigPlan bp{1, 0, 0, 256};
     if (M <= 0 || N <= 0 || K <= 0) return bp;
     const int Kp = kind == WK_I8 ? round_up(K, 64) : K;
     const int nkc = Kp / 64;
     bp.cps = nkc;
-    const double total = (double)((M + BIG_BM - 1) / BIG_BM) * ((N + 255) / 256);
     const double t_stage = kind == WK_W4 ? 0.8 : (kind == WK_I8 ? 1.0 : 1.3);
-    double best = 1e30;
-    for (int S = 1; S <= BIG_MAX_SPLITS && S <= nkc; ++S) {
-        if (nkc % S != 0) continue;
-        double cost = std::ceil(total * S / BIG_CUS) * (nkc / S) * t_stage;
-        if (S > 1) cost += (2.0 * total * S * (double)BIG_PART_TILE + 2.0 * M * N) / 4.5e6 + 4.0;
-        if (cost < best * 0.95) {                 // a split has to win clearly
-            best = cost;
-            bp.splits = S;
-            bp.cps = nkc / S;
+    const double tiles_m = (double)((M + BIG_BM - 1) / BIG_BM);
+    double best = std::ceil(tiles_m * ((N + 255) / 256) / BIG_CUS) * nkc * t_stage;
+    for (int bn : {256, 192}) {
+        if (bn == 192 && kind == WK_W4A8) continue;
+        const double total = tiles_m * ((N + bn - 1) / bn);
+        const double ts = t_stage * (bn == 256 ? 1.0 : 0.9);
+        for (int S = 1; S <= BIG_MAX_SPLITS && S <= nkc; ++S) {
+            if (nkc % S != 0 || (bn == 256 && S == 1)) continue;
+            double cost = std::ceil(total * S / BIG_CUS) * (nkc / S) * ts;
+            if (S > 1) cost += (2.0 * total * S * BIG_BM * bn * 4.0 + 2.0 * M * N) / 4.5e6 + 4.0;
+            if (cost < best * 0.95) {
+                best = cost;
+                bp.bn = bn;
+                bp.splits = S;
+                bp.cps = nkc / S;
+            }
         }
     }
-    bp.part_bytes = bp.splits > 1 ? (size_t)total * bp.splits * BIG_PART_TILE : 0;
+    const double total = tiles_m * ((N + bp.bn - 1) / bp.bn);
+    bp.part_bytes = bp.splits > 1 ? (size_t)total * bp.splits * BIG_BM * bp.bn * 4 : 0;
     return bp;
 }
 
-template <int WK, bool ACC>
-static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
+template <int WK, bool ACC, int BN>
+static hipError_t launch_big_bn(const GemmArgs& a, const BigPlan& bp, hipStream_t st) {
     constexpr int NS = big_stages<WK>();
-    using C = BigCfg<WK, BIG_NW, NS>;
-    const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + C::BN - 1) / C::BN;
-    const BigPlan bp = plan_big(WK, a.M, a.N, a.K);
+    using C = BigCfg<WK, BIG_NW, NS, BN>;
+    const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + BN - 1) / BN;
     if (bp.splits > 1 && a.part == nullptr) return hipErrorInvalidValue;
     // opt in to more than 64 KiB of dynamic LDS (once per process and kernel)
     static bool attr_set[2] = {false, false};
     const bool split = bp.splits > 1;
     if (!attr_set[split]) {
-        const void* k = split ? reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC, true>)
-                              : reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, ACC, false>);
+        const void* k = split ? reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, BN, ACC, true>)
+                              : reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, BN, ACC, false>);
         hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
         if (e != hipSuccess) return e;
         attr_set[split] = true;
@@ -705,16 +746,26 @@ static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
     const int units = tiles_m * tiles_n * bp.splits;
     const int grid = min(units, num_cus());
     if (!split) {
-        k_gemm_big<WK, BIG_NW, NS, ACC, false><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, 1, bp.cps);
+        k_gemm_big<WK, BIG_NW, NS, BN, ACC, false><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, 1, bp.cps);
         return hipGetLastError();
     }
-    k_gemm_big<WK, BIG_NW, NS, ACC, true><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, bp.splits, bp.cps);
+    k_gemm_big<WK, BIG_NW, NS, BN, ACC, true><<<dim3(grid), dim3(64 * BIG_NW), C::LDS, st>>>(a, tiles_m, tiles_n, bp.splits, bp.cps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int FRAGS = BIG_NW * (BIG_BM / BIG_WM / 32) * (8 / (BIG_NW / BIG_WM));
+    constexpr int FRAGS = BIG_NW * C::FM * C::FN;
     const int items = tiles_m * tiles_n * FRAGS;
-    k_big_fixup<WK, ACC><<<dim3((items + 3) / 4), dim3(256), 0, st>>>(a, tiles_m, tiles_n, bp.splits);
+    k_big_fixup<WK, ACC, BN><<<dim3((items + 3) / 4), dim3(256), 0, st>>>(a, tiles_m, tiles_n, bp.splits);
     return hipGetLastError();
+}
+
+template <int WK, bool ACC>
+static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
+    const BigPlan bp = plan_big(WK, a.M, a.N, a.K);
+    if constexpr (WK != WK_W4A8) {
+        if (bp.bn == 192) return launch_big_bn<WK, ACC, 192>(a, bp, st);
+    }
+    if (bp.bn != 256) return hipErrorInvalidValue;
+    return launch_big_bn<WK, ACC, 256>(a, bp, st);
 }
 
 template <int WK>

@@ -75,14 +75,16 @@ struct GemmArgs {
     const int32_t* cw;     // W4A4: weight high-nibble code sums [Np]
 };
 
-// Large-M path plan: K split into `splits` equal slices of `cps` 64-k chunks
-// when the output has too few 256 x 256 tiles to fill the chip; the slices'
-// int32 partial tiles ([splits][tiles][256 x 256] in fragment order) are
-// added by a second kernel.
+// Large-M path plan: block tiles 256 x bn (bn = 256, or 192 where that fills
+// more of the chip), K split into `splits` equal slices of `cps` 64-k chunks
+// when the output has too few tiles to fill the chip; the slices' int32
+// partial tiles ([splits][tiles][256 x bn] in fragment order) are added by a
+// second kernel.
 struct BigPlan {
     int splits;
     int cps;
     size_t part_bytes;
+    int bn;
 };
 BigPlan plan_big(int kind, int M, int N, int K);
 

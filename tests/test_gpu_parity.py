@@ -199,6 +199,8 @@ SHAPES = [
     (129, 512, 256), (300, 768, 384), (257, 256, 96), (96, 2048, 2560), (2, 9728, 64),
     # the four-rows-per-block activation quantiser (M >= 2048), with a partial quad
     (2049, 512, 64), (2048, 1024, 96),
+    # 256 x 192 block tiles, full ones included (odd M: with bias)
+    (1025, 512, 768),
 ]
 
 
@@ -214,7 +216,7 @@ def test_w4a4_acc_and_output(crp, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(64, 2688, 256), (7, 2688, 7), (130, 100, 40), (76, 3072, 384),
-                                   (5, 7, 9), (200, 192, 64)])
+                                   (5, 7, 9), (200, 192, 64), (2048, 256, 1536)])
 def test_int8tw_acc_and_output(crp, M, K, N):
     L = si.random_layer(M, K, N, seed=M + K * 3 + N, bias=True)
     x = to_dev_bf16(L.x)
