@@ -41,6 +41,7 @@ ACT_CASES = [
     (0, 64, 512), (0, 76, 2560), (0, 33, 9728), (0, 3, 256), (0, 5, 12288), (0, 2, 65536),
     (0, 33, 512), (0, 17, 768), (0, 9, 1024), (0, 7, 1280), (0, 3, 32768), (0, 300, 3072),
     (1, 64, 2688), (1, 9, 100), (1, 17, 3072), (1, 1, 7),
+    (1, 33, 512), (1, 5, 4096), (1, 130, 1000), (1, 4, 4104),
     (2, 40, 3840), (2, 3, 256),
 ]
 
@@ -99,7 +100,7 @@ def test_quant_act_exact_ties(crp, kind):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("kind", [0, 2])
+@pytest.mark.parametrize("kind", [0, 1, 2])
 def test_quant_act_extreme_magnitudes(crp, kind):
     """Rows whose max lies outside [2^-100, 2^100] before the 1/16 (tiny,
     huge, subnormal bf16) next to ordinary rows."""
@@ -111,6 +112,26 @@ def test_quant_act_extreme_magnitudes(crp, kind):
     q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
     _sync()
     q_ref, s_ref = KIND_ORACLE_ACT[kind](x)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_act_int8_exact_ties(crp):
+    """int8_tensorwise rows whose values sit exactly on half-integer multiples
+    of the scale (s = 2^e exactly): round half to even decides."""
+    K = 1024
+    rows = []
+    for e in (-6, 0, 3):
+        r = np.zeros(K, np.float32)
+        r[0] = 127.0 * 2.0 ** e                           # the row maximum: scale 2^e
+        for i in range(1, 40):
+            r[i] = (-1) ** i * ((i % 9) + 0.5) * 2.0 ** e
+        rows.append(r)
+    x = si.f32_to_bf16_bits(np.stack(rows))
+    assert np.array_equal(si.bf16_bits_to_f32(x), np.stack(rows))
+    q, s = crp.dbg_quant_act(1, to_dev_bf16(x))
+    _sync()
+    q_ref, s_ref = KIND_ORACLE_ACT[1](x)
     assert np.array_equal(q.cpu().numpy(), q_ref)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 
