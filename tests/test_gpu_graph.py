@@ -1,6 +1,7 @@
 """The linears under HIP graph capture: every replay equals the eager result,
-with other eager work and synchronisation between replays (the small-M path's
-split-K counters must be clear at every replay)."""
+with other eager work and synchronisation between replays.  Shapes cover the
+small-M path, the large-M path with whole tiles (256- and 192-wide) and the
+large-M path with K split across blocks (two kernels per GEMM)."""
 import numpy as np
 import pytest
 
@@ -11,7 +12,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-@pytest.mark.parametrize("M,K,N", [(76, 2560, 1024), (300, 512, 256)])
+@pytest.mark.parametrize("M,K,N", [(76, 2560, 1024), (300, 512, 256), (300, 4096, 512), (1025, 512, 768)])
 def test_graph_replays_match_eager(M, K, N):
     import rotated_bit_quantized_convrot_amd as crp
     L = si.random_layer(M, K, N, seed=M + N, bias=True)
