@@ -4,8 +4,9 @@
 // y[m,n] = bf16(fl(fl(float(acc) * s_x[m]) * s_w) + bias[n])
 // ([QIE] model card, "Speed" table: fused ConvRot + rank-one s4 MMA kernel;
 // [REB] "Why W4A8 instead of GGUF": the W4A8 weights stay 4-bit in memory and
-// the math is int8).  CDNA4 has no int4 MFMA, so 4-bit weights are widened to
-// int8 in registers: W4 codes as 16*code (exact, then acc >> 4), W4A8 indices
+// the math is int8).  CDNA4 has no int4 MFMA, so 4-bit codes are widened to
+// int8 in registers: W4A4 weights and activations by one AND per dword (two
+// nibble forms, exact after the epilogue's integer correction), W4A8 indices
 // through a per-group 16-entry table row.
 //
 // MFMA operand roles: the weight fragment is the A operand (32 rows = n) and
