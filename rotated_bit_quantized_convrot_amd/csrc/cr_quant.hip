@@ -398,6 +398,10 @@ hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, i
         if (packed && G <= 64 && M >= 2048) {
             int gpl = 1;
             while ((G + gpl - 1) / gpl > 16) gpl <<= 1;
+            // two groups per lane from K = 2048 up: half as many waves, so the
+            // whole grid is resident at once instead of a thin last round
+            // (DiT W1: 11.1 -> 9.7 us)
+            if (gpl == 1 && G >= 8) gpl = 2;
             const int nw = (G + gpl - 1) / gpl;
             const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
             switch (gpl) {

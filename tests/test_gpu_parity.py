@@ -219,7 +219,7 @@ SHAPES = [
     (64, 512, 256), (1, 256, 64), (33, 512, 100), (76, 2560, 512), (128, 1024, 256),
     (129, 512, 256), (300, 768, 384), (257, 256, 96), (96, 2048, 2560), (2, 9728, 64),
     # the four-rows-per-block activation quantiser (M >= 2048), with a partial quad
-    (2049, 512, 64), (2048, 1024, 96),
+    (2049, 512, 64), (2048, 1024, 96), (2050, 2304, 64),
     # 256 x 192 block tiles, full ones included (odd M: with bias)
     (1025, 512, 768),
 ]
