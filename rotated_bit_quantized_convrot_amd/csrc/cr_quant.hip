@@ -377,6 +377,11 @@ static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float*
     }
     int gpl = 1;
     while ((T + gpl - 1) / gpl > 1024) gpl <<= 1;
+    // more groups per lane (fewer waves) while the grid would exceed what the
+    // chip holds at once (~8192 waves) and a row keeps at least one whole wave
+    // (text-encoder down layer at M=1220: 14.5 -> 11.9 us)
+    while (gpl < 4 && (long)M * (round_up((T + gpl - 1) / gpl, 64) / 64) > 8192 && (T + 2 * gpl - 1) / (2 * gpl) >= 64)
+        gpl <<= 1;
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
@@ -416,7 +421,8 @@ hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, i
                       : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, nullptr, st);
     }
     if (kind == WK_W4A8) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
-    k_quant_act_plain<<<dim3(M), dim3(256), 0, st>>>(x, M, K, Kp, qx, sx);
+    // two waves per row when four per row would exceed what the chip holds at once
+    k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ ACT_CASES = [
     (1, 64, 2688), (1, 9, 100), (1, 17, 3072), (1, 1, 7),
     (1, 33, 512), (1, 5, 4096), (1, 130, 1000), (1, 4, 4104),
     (2, 40, 3840), (2, 3, 256),
+    # grids larger than the chip holds at once: two groups per lane (rotated)
+    # or two waves per row (int8_tensorwise)
+    (2, 2100, 3840), (0, 1100, 8192), (1, 2100, 640),
 ]
 
 
