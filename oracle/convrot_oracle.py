@@ -61,6 +61,13 @@ R10 W4A8 encode (offline): s_channel[n] = absmax_k |W~[n,:]| / 127;
     quantiles, at most 100 iterations; idx = the cell of u (a value on a
     threshold goes to the lower level).
 R11 Canonical int4 storage: two's complement nibbles, low nibble = even k.
+R12 ConvRot INT8 row-scaled ([Q3N] file table: INT8 with group-256 Hadamard
+    rotation and row-wise scaling; converter flags: int8, row scaling,
+    dynamic ConvRot, group 256): the weight is rotated like R2, then
+    quantised per output row, s_w[n] = absmax_k |W~[n,k]| / 127, codes
+    clip(rint(W~ / s_w[n]), -128, 127); the activations are rotated online
+    and quantised per row as in R8; one int32 accumulation over the full K;
+    the epilogue takes s_w[n] per output column (as s_channel in R8).
 
 Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
 codebooks are correct and the GPU consumes whatever codebook it is given; its
@@ -221,6 +228,22 @@ def quant_act_w4a8(x_bits: np.ndarray, group: int = GROUP):
     return quant_rows(xr, 127, -128, 127)
 
 
+# --- ConvRot INT8, row-scaled (reading R12) --------------------------------
+
+def quant_act_int8rot(x_bits: np.ndarray, group: int = GROUP):
+    """ConvRot INT8 activations: group-256 rotation (dynamic ConvRot), then
+    per-row int8 codes (absmax/127)."""
+    xr = fwht(bf16_to_f32(x_bits), group)
+    return quant_rows(xr, 127, -128, 127)
+
+
+def quant_weight_int8rot(w_bits: np.ndarray, group: int = GROUP):
+    """ConvRot INT8 row-scaled weight [N, K]: group-256 rotation, then one
+    int8 scale per output row (absmax of the rotated row / 127)."""
+    wr = fwht(bf16_to_f32(w_bits), group)
+    return quant_rows(wr, 127, -128, 127)
+
+
 # ---------------------------------------------------------------------------
 # Canonical nibble packing (reading R11)
 # ---------------------------------------------------------------------------
@@ -319,6 +342,16 @@ def linear_int8tw(x_bits, w_bits, bias_bits=None):
     formats": no group constraint]."""
     qx, sx = quant_act_int8(x_bits)
     qw, sw = quant_weight_int8tw(w_bits)
+    acc = int_gemm(qx, qw)
+    return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
+
+
+def linear_int8rot(x_bits, w_bits, bias_bits=None, group: int = GROUP):
+    """ConvRot INT8 row-scaled linear [Q3N file table and converter flags]:
+    rotated per-row int8 activations, rotated row-scaled int8 weight, exact
+    int32 accumulation, epilogue with the weight scale of each output column."""
+    qx, sx = quant_act_int8rot(x_bits, group)
+    qw, sw = quant_weight_int8rot(w_bits, group)
     acc = int_gemm(qx, qw)
     return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
 

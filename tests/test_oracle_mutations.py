@@ -84,6 +84,16 @@ def _decode_clamp128(idx, s_rel, codebook):
     return np.clip(np.rint((cb[np.asarray(idx)] * s).astype(F32)), -128, 127).astype(np.int8)
 
 
+def _int8rot_weight_tensor_scale(w_bits, group=256):
+    wr = _real_fwht(O.bf16_to_f32(w_bits), group)
+    q, s = O.quant_tensor(wr, 127, -128, 127)
+    return q, np.full(wr.shape[0], s, F32)
+
+
+def _int8rot_weight_unrotated(w_bits, group=256):
+    return O.quant_rows(O.bf16_to_f32(w_bits), 127, -128, 127)
+
+
 def _pack_high_first(q):
     u = (np.asarray(q, np.int8).astype(np.int16) & 0xF).astype(np.uint8)
     return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
@@ -104,6 +114,8 @@ MUTATIONS = {
     "e4m3_wrong_bias": ("e4m3_to_f32", _e4m3_bias8),
     "w4a8_clamp_128": ("w4a8_decode", _decode_clamp128),
     "pack_nibble_order": ("pack_int4", _pack_high_first),
+    "int8rot_weight_scale_per_tensor": ("quant_weight_int8rot", _int8rot_weight_tensor_scale),
+    "int8rot_weight_unrotated": ("quant_weight_int8rot", _int8rot_weight_unrotated),
 }
 
 PINS = [
@@ -123,6 +135,9 @@ PINS = [
     P.test_end_to_end_close_to_float_linear,
     P.test_e4m3_decode_matches_torch,
     P.test_w4a8_decode_hand_cases,
+    P.test_int8rot_row_scale_invariance,
+    P.test_int8rot_one_hot_weight_rows,
+    P.test_int8rot_acc_brute_force_python_ints,
 ]
 
 

@@ -351,3 +351,79 @@ def test_bf16_rne():
     w = (rng.normal(size=10000) * 10).astype(F32)
     want = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(O.f32_to_bf16_rne(w), want)
+
+
+# ---------------------------------------------------------------------------
+# ConvRot INT8, row-scaled (reading R12)
+# ---------------------------------------------------------------------------
+
+def test_int8rot_row_scale_invariance():
+    """Rows that are power-of-two multiples of one row: the rotation and the
+    per-row scale commute with the power of two, so every row gets the same
+    codes and its scale is the base scale times that power, exactly.  (One
+    scale for the whole tensor would give the small rows other codes.)"""
+    rng = np.random.default_rng(11)
+    K = 512
+    base = O.bf16_to_f32(si.f32_to_bf16_bits(rng.standard_normal((1, K)).astype(F32)))
+    ks = [0, -3, 2, 5, -1]
+    w = np.concatenate([base * F32(2.0 ** k) for k in ks]).astype(F32)
+    wb = si.f32_to_bf16_bits(w)
+    assert np.array_equal(O.bf16_to_f32(wb), w)
+    q, s = O.quant_weight_int8rot(wb)
+    for i, k in enumerate(ks):
+        assert np.array_equal(q[i], q[0])
+        assert s[i] == F32(s[0] * F32(2.0 ** k))
+    assert np.max(np.abs(q[0])) == 127
+
+
+def test_int8rot_one_hot_weight_rows():
+    """A weight row c * e_j in group g rotates to c/16 times row j of the
+    Sylvester matrix in group g: codes +-127 in that sign pattern there, 0 in
+    the other groups, scale fl(fl(|c|/16)/127)."""
+    K = 768
+    rows = [(2.0, 37, 1), (-0.75, 0, 0), (5.0, 255, 2)]
+    w = np.zeros((len(rows), K), F32)
+    for n, (c, j, g) in enumerate(rows):
+        w[n, 256 * g + j] = c
+    q, s = O.quant_weight_int8rot(si.f32_to_bf16_bits(w))
+    for n, (c, j, g) in enumerate(rows):
+        sign = np.array([1 if _popcount(j & k) % 2 == 0 else -1 for k in range(256)])
+        want = np.zeros(K, np.int8)
+        want[256 * g:256 * (g + 1)] = (127 * sign * (1 if c > 0 else -1)).astype(np.int8)
+        assert np.array_equal(q[n], want)
+        assert s[n] == F32(F32(abs(c) / 16) / F32(127))
+
+
+def test_int8rot_acc_brute_force_python_ints():
+    """acc[m, n] = sum_k qx[m, k] * qw[n, k] over Python integers, and the
+    epilogue's scale of column n is the weight row n's scale."""
+    L = si.random_layer(3, 256, 5, seed=21, bias=True, outlier_count=3)
+    r = O.linear_int8rot(L.x, L.w, L.bias)
+    qx, qw = r["qx"].astype(int), r["qw"].astype(int)
+    for m in range(3):
+        for n in range(5):
+            assert int(r["acc"][m, n]) == sum(int(qx[m, k]) * int(qw[n, k]) for k in range(256))
+    b = O.bf16_to_f32(L.bias)
+    for m in range(3):
+        for n in range(5):
+            want = F32(F32(F32(r["acc"][m, n]) * r["sx"][m]) * r["sw"][n]) + b[n]
+            assert r["y"][m, n] == want
+
+
+def test_int8rot_row_scaling_beats_tensorwise_on_uneven_rows():
+    """Weights whose rows differ in magnitude by 2^6: per-row scales keep every
+    row at full int8 resolution, one tensor scale does not."""
+    rng = np.random.default_rng(3)
+    N, K = 32, 1024
+    w = rng.normal(0, 0.02, (N, K)).astype(F32)
+    w[::4] *= 64
+    wb = si.f32_to_bf16_bits(w)
+    wr = O.fwht(O.bf16_to_f32(wb))
+    q, s = O.quant_weight_int8rot(wb)
+    err_row = np.linalg.norm(q * s[:, None] - wr) / np.linalg.norm(wr)
+    qt, st = O.quant_tensor(wr, 127, -128, 127)
+    small = np.arange(N) % 4 != 0
+    err_small_row = np.linalg.norm((q * s[:, None] - wr)[small]) / np.linalg.norm(wr[small])
+    err_small_t = np.linalg.norm((qt * st - wr)[small]) / np.linalg.norm(wr[small])
+    assert err_small_row < 0.02 and err_small_t > 4 * err_small_row
+    assert err_row < 0.02
