@@ -20,7 +20,9 @@ calls and timing it with HIP events on the launch stream:
   * every other row of the hot path: DiT W2, text-encoder gate/up and down
     at M=76 (weight-stream GB/s with cold weights cycled through 48 copies,
     more than twice the 256 MB last-level cache) and M=1220, the
-    int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer.
+    int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer, and the
+    ConvRot INT8 row-scaled format on a square text-encoder projection
+    (K=N=2560) at M=76 and M=1220.
 The CPU oracle (NumPy) is timed on a row sample of the headline layer.
 
 Prints one JSON line.
@@ -73,6 +75,8 @@ def row_specs():
         "int8tw_vo": dict(kind=1, gen=lambda: si.int8tw_vo(), cold=False),
         "int8tw_k2688": dict(kind=1, gen=lambda: si.int8tw_k2688(), cold=False),
         "w4a8": dict(kind=2, gen=lambda: si.w4a8_layer(), cold=False),
+        "int8rot_attn_M76": dict(kind=3, gen=lambda: si.te_attn_proj(76), cold=True),
+        "int8rot_attn_M1220": dict(kind=3, gen=lambda: si.te_attn_proj(1220), cold=False),
     }
 
 
@@ -95,13 +99,13 @@ class Layer:
             s = torch.from_numpy(s_ch).to(dev)
         else:
             w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
-            p, s = (crp.pack_weight_w4 if kind == 0 else crp.pack_weight_int8tw)(w)
+            p, s = {0: crp.pack_weight_w4, 1: crp.pack_weight_int8tw, 3: crp.pack_weight_int8rot}[kind](w)
             del w
         self.packed = [p] + [p.clone() for _ in range(copies - 1)]
         self.scale = s
         self.y = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
         self.ws = torch.empty(crp.workspace_bytes(kind, L.M, L.N, L.K), dtype=torch.uint8, device=dev)
-        self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8}[kind]
+        self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8, 3: crp.linear_int8rot}[kind]
 
     def linear(self, i=0):
         return self.fn(self.x, self.packed[i], self.scale, self.N, self.bias, self.y, self.ws)
@@ -122,15 +126,19 @@ class Layer:
             return self.N * self.K / 2
         if self.kind == 1:
             return self.N * self.K
+        if self.kind == 3:
+            return self.N * self.K + 4 * self.N
         return self.N * self.K / 2 + self.N * self.K / 16 + 4 * self.N
 
     def gemm_bytes(self):
-        qx = self.M * self.K
+        qx = self.M * self.K / 2 if self.kind == 0 else self.M * self.K    # activation codes
         y = self.M * self.N * 2
         b = self.N * 2 if self.bias is not None else 0
         return qx + self.weight_bytes() + y + b + 4 * self.M
 
     def quant_bytes(self):
+        if self.kind == 0:      # 4-bit codes, scale and correction sum per row
+            return self.M * self.K * 2 + self.M * self.K / 2 + 8 * self.M
         return self.M * self.K * 2 + self.M * self.K + 4 * self.M
 
     def linear_bytes(self):

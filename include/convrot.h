@@ -12,6 +12,9 @@
  *         an fp8 scale per group of 16, a scale per output channel, 16
  *         Lloyd-Max levels), int8 GEMM; layers whose input width is not a
  *         multiple of 256 use int8_tensorwise instead.
+ *   [Q3N] "qwen3-4b-nvfp4-convrot", file table and converter flags: ConvRot
+ *         INT8, int8 weights with a group-256 Hadamard rotation and one scale
+ *         per row.
  *
  * Arithmetic (shared by every entry point, float32 unless stated):
  *   rotation   each contiguous 256-block of K is multiplied by the Sylvester
@@ -20,11 +23,12 @@
  *   act quant  per row m: s_x[m] = absmax_k / Q (IEEE division),
  *              code = clamp(rint(v / s_x[m])) with round-half-even;
  *              Q = 7, codes [-8,7] (W4A4); Q = 127, codes [-128,127]
- *              (int8_tensorwise: no rotation; W4A8: rotated).  s = 0 -> 0.
+ *              (int8_tensorwise: no rotation; W4A8, ConvRot INT8:
+ *              rotated).  s = 0 -> 0.
  *   GEMM       acc[m,n] = sum_k qx[m,k] * qw[n,k], exact int32.
  *   epilogue   y[m,n] = bf16_rne(fl(fl(float(acc) * s_x[m]) * s_w) + bias[n])
- *              with s_w the tensor scale (W4A4, int8_tensorwise) or
- *              s_channel[n] (W4A8).
+ *              with s_w the tensor scale (W4A4, int8_tensorwise),
+ *              s_channel[n] (W4A8) or the row scale s_w[n] (ConvRot INT8).
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -68,10 +72,12 @@ typedef enum {
 #define CR_W4A4 0    /* ConvRot W4A4: INT4 weights (tensorwise), INT4 activations */
 #define CR_INT8TW 1  /* int8_tensorwise: int8 weights (tensorwise), int8 activations */
 #define CR_W4A8 2    /* asym W4A8 codebook: 4-bit codebook weights, int8 activations */
+#define CR_INT8ROT 3 /* ConvRot INT8 row-scaled: rotated int8 weights (one scale per
+                        output row), rotated int8 activations */
 
 /* Limits: 1 <= N, K <= CR_MAX_DIM; 0 <= M <= CR_MAX_DIM. */
 #define CR_MAX_DIM (1 << 20)
-/* Largest K the rotated activation quantiser accepts (W4A4, W4A8). */
+/* Largest K the rotated activation quantiser accepts (W4A4, W4A8, ConvRot INT8). */
 #define CR_MAX_ROT_K 65536
 
 /* Bytes of the packed weight of `kind` for an [N,K] weight (0 on bad args). */
@@ -119,6 +125,28 @@ cr_status cr_linear_int8tw(const void* x_bf16, int M, int K, const void* w_packe
                            const float* w_scale, int N, const void* bias_bf16,
                            void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- ConvRot INT8, row-scaled ([Q3N] file table: INT8 with group-256
+ *      Hadamard rotation and row-wise scaling; converter flags) ------------ */
+
+/* Offline weight preparation: rotate each 256-block of every row of W,
+ * s_w[n] = absmax(rotated row n) / 127, codes = clamp(rint(v / s_w[n]),
+ * -128, 127), written in the int8 packed layout.
+ *   w_bf16   [N,K] bf16                        (in)
+ *   w_packed cr_packed_bytes(CR_INT8ROT,N,K)   (out)
+ *   w_scale  [N] float, one scale per row      (out)
+ * K must be a multiple of 256 (CR_ERR_GROUP otherwise). */
+cr_status cr_pack_weight_int8rot(const void* w_bf16, int N, int K, void* w_packed,
+                                 float* w_scale, hipStream_t stream);
+
+/* y = ConvRot INT8 linear: x rotated online and quantised per row to int8
+ * (absmax/127), exact int32 GEMM against the packed weight, epilogue
+ * y[m,n] = bf16(fl(fl(acc * s_x[m]) * w_scale[n]) + bias[n]).
+ *   w_packed / w_scale from cr_pack_weight_int8rot with the same N, K;
+ *   ws / ws_bytes: workspace of at least cr_workspace_bytes(CR_INT8ROT,M,N,K). */
+cr_status cr_linear_int8rot(const void* x_bf16, int M, int K, const void* w_packed,
+                            const float* w_scale, int N, const void* bias_bf16,
+                            void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- asym W4A8 codebook ([REB] "What's inside a file", "Why W4A8 instead of
  *      GGUF": int8 GEMM at ~0.56 B/param) -------------------------------- */
 
@@ -160,7 +188,8 @@ cr_status cr_quantize_activations(int kind, const void* x_bf16, int M, int K, vo
 
 /* GEMM + rank-one epilogue from a workspace filled by
  * cr_quantize_activations(kind, x, M, K, ...).  w_scale is the tensor scale
- * (W4A4, int8_tensorwise) or s_channel [N] (W4A8).
+ * (W4A4, int8_tensorwise), s_channel [N] (W4A8) or the row scales [N]
+ * (ConvRot INT8).
  * ws_bytes >= cr_workspace_bytes(kind, M, N, K). */
 cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const float* w_scale,
                             int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
@@ -179,7 +208,8 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K,
                            void* codes, float* scales, hipStream_t stream);
 
 /* Weight codes from a packed weight, canonical row-major [N,K] int8
- * (W4A4: [-8,7]; int8_tensorwise: [-128,127]; W4A8: the decoded int8 w8). */
+ * (W4A4: [-8,7]; int8_tensorwise, ConvRot INT8: [-128,127]; W4A8: the
+ * decoded int8 w8). */
 cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K,
                                void* codes, hipStream_t stream);
 

@@ -25,15 +25,15 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A4", "INT8TW", "W4A8", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
-    "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8",
-    "linear_w4a4", "linear_int8tw", "linear_w4a8",
+    "W4A4", "INT8TW", "W4A8", "INT8ROT", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
+    "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8", "pack_weight_int8rot",
+    "linear_w4a4", "linear_int8tw", "linear_w4a8", "linear_int8rot",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
 ]
 
-W4A4, INT8TW, W4A8 = 0, 1, 2
+W4A4, INT8TW, W4A8, INT8ROT = 0, 1, 2, 3
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.so")
 _LIB = None
 
@@ -45,6 +45,7 @@ EXPORTS = [
     "cr_pack_weight_int8tw", "cr_linear_int8tw", "cr_pack_weight_w4a8", "cr_linear_w4a8",
     "cr_status_str", "cr_last_error", "cr_dbg_quant_act", "cr_dbg_unpack_weight",
     "cr_dbg_linear_acc", "cr_quantize_activations", "cr_gemm_quantized",
+    "cr_pack_weight_int8rot", "cr_linear_int8rot",
 ]
 
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "cr_pack_weight_w4": (i, [vp, i, i, vp, vp, vp]),
         "cr_pack_weight_int8tw": (i, [vp, i, i, vp, vp, vp]),
         "cr_pack_weight_w4a8": (i, [vp, vp, vp, i, i, vp, vp]),
+        "cr_pack_weight_int8rot": (i, [vp, i, i, vp, vp, vp]),
+        "cr_linear_int8rot": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
@@ -155,6 +158,20 @@ def pack_weight_int8tw(w: torch.Tensor):
     return out, scale
 
 
+def pack_weight_int8rot(w: torch.Tensor):
+    """bf16 [N,K] -> (packed uint8, row scales float32[N]) in the ConvRot INT8
+    row-scaled format (K % 256 == 0)."""
+    _dev(w, "w", torch.bfloat16)
+    N, K = w.shape
+    nb = packed_bytes(INT8ROT, N, K)
+    if nb == 0:
+        _check(lib().cr_pack_weight_int8rot(_ptr(w), N, K, None, None, None) or 2)
+    out = _empty_u8(nb, w.device)
+    scale = torch.empty(max(N, 4), dtype=torch.float32, device=w.device)
+    _check(lib().cr_pack_weight_int8rot(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
+    return out, scale
+
+
 def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Tensor, N: int, K: int):
     """Stored W4A8 tensors -> packed uint8 (index nibbles [N,K/2], e4m3 scale
     codes [N,K/16] as uint8, codebook float32[16])."""
@@ -215,6 +232,11 @@ def linear_int8tw(x, packed, scale, N, bias=None, out=None, workspace=None):
     return _linear("cr_linear_int8tw", INT8TW, x, packed, scale, N, bias, out, workspace)
 
 
+def linear_int8rot(x, packed, scale, N, bias=None, out=None, workspace=None):
+    """y = ConvRot INT8 row-scaled linear (K % 256 == 0); scale float32 [N]."""
+    return _linear("cr_linear_int8rot", INT8ROT, x, packed, scale, N, bias, out, workspace)
+
+
 def linear_w4a8(x, packed, s_channel, N, bias=None, out=None, workspace=None):
     """y = asym W4A8 codebook linear; s_channel float32 [N]."""
     return _linear("cr_linear_w4a8", W4A8, x, packed, s_channel, N, bias, out, workspace)
@@ -225,7 +247,7 @@ def linear_w4a8(x, packed, s_channel, N, bias=None, out=None, workspace=None):
 # ---------------------------------------------------------------------------
 
 def quantize_activations(kind: int, x: torch.Tensor, workspace: torch.Tensor):
-    """Rotate (W4A4, W4A8) and quantise x [M,K] into ``workspace``."""
+    """Rotate (W4A4, W4A8, ConvRot INT8) and quantise x [M,K] into ``workspace``."""
     _dev(x, "x", torch.bfloat16)
     _dev(workspace, "workspace", torch.uint8)
     M, K = x.shape
@@ -296,14 +318,19 @@ class PackedWeight:
     N: int
     K: int
     packed: torch.Tensor
-    scale: torch.Tensor              # tensor scale (W4A4, int8tw) or s_channel (W4A8)
+    scale: torch.Tensor              # tensor scale (W4A4, int8tw), s_channel (W4A8), row scales (INT8ROT)
     bias: Optional[torch.Tensor] = None
 
 
-def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None) -> PackedWeight:
-    """Pack a bf16 [N,K] weight: W4A4 ConvRot when K % 256 == 0, otherwise
-    int8_tensorwise ([REB] "Mixed formats where the kernel demands it")."""
+def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None, int8: bool = False) -> PackedWeight:
+    """Pack a bf16 [N,K] weight: W4A4 ConvRot when K % 256 == 0 (ConvRot INT8
+    row-scaled instead with ``int8=True``, the format [Q3N] gives attention
+    projections), otherwise int8_tensorwise ([REB] "Mixed formats where the
+    kernel demands it")."""
     N, K = w.shape
+    if K % 256 == 0 and int8:
+        p, s = pack_weight_int8rot(w)
+        return PackedWeight(INT8ROT, N, K, p, s, bias)
     if K % 256 == 0:
         p, s = pack_weight_w4(w)
         return PackedWeight(W4A4, N, K, p, s, bias)
@@ -312,5 +339,5 @@ def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None) -> PackedW
 
 
 def linear(x: torch.Tensor, pw: PackedWeight, out=None, workspace=None) -> torch.Tensor:
-    fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8}[pw.kind]
+    fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8, INT8ROT: linear_int8rot}[pw.kind]
     return fn(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace)

@@ -48,10 +48,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t a256(size_t v) { return (v + 255) / 256 * 256; }
 
-bool rotated(int kind) { return kind == CR_W4A4 || kind == CR_W4A8; }
+bool rotated(int kind) { return kind == CR_W4A4 || kind == CR_W4A8 || kind == CR_INT8ROT; }
 
 cr_status check_kind(int kind) {
-    if (kind != CR_W4A4 && kind != CR_INT8TW && kind != CR_W4A8) return fail(CR_ERR_KIND, "unknown kind %d", kind);
+    if (kind != CR_W4A4 && kind != CR_INT8TW && kind != CR_W4A8 && kind != CR_INT8ROT)
+        return fail(CR_ERR_KIND, "unknown kind %d", kind);
     return CR_OK;
 }
 
@@ -72,13 +73,21 @@ size_t packed_bytes(int kind, int N, int K) {
         case CR_W4A4: return cr::w4a4_bytes(N, K);
         case CR_INT8TW: return cr::i8_bytes(N, K);
         case CR_W4A8: return cr::w4a8_bytes(N, K);
+        case CR_INT8ROT: return cr::i8_bytes(N, K);
         default: return 0;
     }
 }
 
 int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K; }
 
-int wkind(int kind) { return kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8); }
+int wkind(int kind) {
+    switch (kind) {
+        case CR_W4A4: return cr::WK_W4;
+        case CR_INT8TW: return cr::WK_I8;
+        case CR_INT8ROT: return cr::WK_I8R;
+        default: return cr::WK_W4A8;
+    }
+}
 
 // Workspace: [codes][scales M][W4A4: ra M][split-K partials].  Codes are
 // int8 [M, Kp], or for W4A4 4-bit tiles (round_up(M, 32) x K/2 bytes).  The
@@ -241,6 +250,22 @@ cr_status cr_pack_weight_w4a8(const void* idx, const void* s_rel_e4m3, const flo
                       "W4A8 weight packing");
 }
 
+cr_status cr_pack_weight_int8rot(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
+                                 hipStream_t stream) {
+    cr_status s = pack_common_checks(CR_INT8ROT, w_bf16, N, K, w_packed, w_scale);
+    if (s != CR_OK) return s;
+    return launch_err(cr::launch_pack_i8rot(static_cast<const uint16_t*>(w_bf16), N, K,
+                                            static_cast<uint8_t*>(w_packed), w_scale, stream),
+                      "ConvRot INT8 weight packing");
+}
+
+cr_status cr_linear_int8rot(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
+                            int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    return run_linear(CR_INT8ROT, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws,
+                      ws_bytes, stream);
+}
+
 cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
                          int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
@@ -312,7 +337,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if (x_bf16 == nullptr || codes == nullptr || scales == nullptr) return fail(CR_ERR_NULL, "NULL argument");
     if (!aligned16(x_bf16) || !aligned16(codes)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
     if ((s = check_device()) != CR_OK) return s;
-    const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
+    const int wk = wkind(kind);
     return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
                                            static_cast<int8_t*>(codes), scales, nullptr, false, stream),
                       "activation quantisation");
@@ -326,7 +351,7 @@ cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K, voi
     if (w_packed == nullptr || codes == nullptr) return fail(CR_ERR_NULL, "NULL argument");
     if (!aligned16(w_packed)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
     if ((s = check_device()) != CR_OK) return s;
-    const int wk = kind == CR_W4A4 ? cr::WK_W4 : (kind == CR_INT8TW ? cr::WK_I8 : cr::WK_W4A8);
+    const int wk = wkind(kind);
     return launch_err(cr::launch_unpack_weight(wk, static_cast<const uint8_t*>(w_packed), N, K,
                                                static_cast<int8_t*>(codes), stream),
                       "weight unpacking");

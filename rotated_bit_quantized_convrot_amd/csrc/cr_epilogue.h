@@ -1,5 +1,6 @@
 // Epilogue shared by the GEMM kernels: y[m,n] = bf16_rne(fl(fl(float(acc) *
-// s_x[m]) * s_w) + bias[n]) (s_channel[n] in place of s_w for W4A8), or the
+// s_x[m]) * s_w) + bias[n]) (a per-column scale in place of s_w for W4A8 and
+// ConvRot INT8), or the
 // exact int32 accumulator for the inspection hook.  The functions take the
 // MFMA sums; W4A4 sums are turned into the exact dot products here (see the
 // nibble forms in cr_internal.h).
@@ -42,8 +43,8 @@ __device__ __forceinline__ void exact4(const Epi& e, int m, int n, int& a0, int&
 }
 
 // Writes 4 consecutive outputs n..n+3 of row m (n % 4 == 0, n < N) from
-// their MFMA sums.  sw0: the tensor scale (unused for W4A8, which reads
-// s_channel[n]).
+// their MFMA sums.  sw0: the tensor scale (unused with per-column scales,
+// which are read from wscale[n]).
 template <int WK, bool ACC>
 __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, float sw0, int a0,
                                        int a1, int a2, int a3) {
@@ -62,7 +63,7 @@ __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, fl
         }
     } else if (full) {
         float sw[4] = {sw0, sw0, sw0, sw0};
-        if constexpr (WK == WK_W4A8) {
+        if constexpr (wk_chan(WK)) {
             const float4 c = *reinterpret_cast<const float4*>(e.wscale + n);
             sw[0] = c.x; sw[1] = c.y; sw[2] = c.z; sw[3] = c.w;
         }
@@ -88,7 +89,7 @@ __device__ __forceinline__ void store4(const Epi& e, int m, int n, float sxm, fl
             const int nn = n + j;
             if (nn < N) {
                 float v = (float)a[j] * sxm;
-                v = v * ((WK == WK_W4A8) ? e.wscale[nn] : sw0);
+                v = v * (wk_chan(WK) ? e.wscale[nn] : sw0);
                 if (e.bias != nullptr) v = v + bf16_to_f32(e.bias[nn]);
                 e.y[(size_t)m * N + nn] = (uint16_t)f32_to_bf16_rne(v);
             }
@@ -121,7 +122,7 @@ __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M,
     const int nc = vec ? min(n, N - 4) : 0;
     r.sx = sx[mc];
     const float* wsp = has_w ? e.wscale : sx;
-    if constexpr (WK == WK_W4A8) {
+    if constexpr (wk_chan(WK)) {
         const float* sc = wsp + (has_w ? nc : 0);
         r.sw[0] = sc[0];
         r.sw[1] = sc[has_w ? min(1, N - 1 - nc) : 0];

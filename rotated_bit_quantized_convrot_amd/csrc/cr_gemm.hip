@@ -114,7 +114,7 @@ struct BigCfg {
     static constexpr int WNW = NW / WM;                                // waves along n
     static constexpr int WROWS = BIG_BM / WM, FM = WROWS / 32, FN = NWT / WNW;
     static constexpr bool PA = WK == WK_W4;                            // 4-bit activation tiles
-    static constexpr int BSTEP = WK == WK_I8 ? 2048 : 1024;            // bytes of a weight tile's stage
+    static constexpr int BSTEP = wk_i8w(WK) ? 2048 : 1024;             // bytes of a weight tile's stage
     static constexpr int A_BYTES = PA ? BIG_BM * 32 : BIG_BM * 64;    // activations per stage
     static constexpr int B_BYTES = NWT * BSTEP;
     static constexpr int C_BYTES = WK == WK_W4A8 ? NWT * 128 : 0;     // W4A8 scale codes
@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         const int o = wave * C::WB + j * 1024 + lane * 16;
         const int t = o / BSTEP, sl = (o % BSTEP) >> 4;
         int src;
-        if constexpr (WK == WK_I8) {
+        if constexpr (wk_i8w(WK)) {
             const int r = sl >> 2;
             src = r * 64 + (((sl & 3) ^ ((r >> 2) & 3)) * 16);
         } else {
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
         const int tile = wn * FN + f;
-        if constexpr (WK == WK_I8) boff[f] = tile * 2048 + l32 * 64;
+        if constexpr (wk_i8w(WK)) boff[f] = tile * 2048 + l32 * 64;
         else boff[f] = tile * 1024 + (2 * l32 + (h ^ ((l32 >> 3) & 1))) * 16;
     }
 
@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
     auto read_w = [&](const int8_t* st, int f) -> WStage {
         WStage w;
         const int8_t* sb = st + C::A_BYTES;
-        if constexpr (WK == WK_I8) {
+        if constexpr (wk_i8w(WK)) {
             w.a = *reinterpret_cast<const uint4*>(sb + boff[f] + (((2 * h + 0) ^ swz) * 16));
             w.b = *reinterpret_cast<const uint4*>(sb + boff[f] + (((2 * h + 1) ^ swz) * 16));
         } else {
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         return w;
     };
     auto wop = [&](const WStage& w, int t) -> v4i {
-        if constexpr (WK == WK_I8) {
+        if constexpr (wk_i8w(WK)) {
             const uint4 v = t == 0 ? w.a : w.b;
             v4i r;
             r.x = (int)v.x; r.y = (int)v.y; r.z = (int)v.z; r.w = (int)v.w;
@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
             // left outstanding across the k-loop would turn every wait for
             // LDS reads there into lgkmcnt(0) (scalar loads share that
             // counter and return out of order).
-            const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
+            const float sw0 = (wk_chan(WK) || ACC) ? 0.0f : p.wscale[0];
             int m0, n0, kc0, uid;
             tile_origin(cur_tile, m0, n0, kc0, uid);
             const bool full = m0 + BIG_BM <= M && n0 + BN <= p.N && (p.N & 7) == 0;
@@ -441,19 +441,23 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                         for (int q = 0; q < 4; ++q)
                             dst[((i * FN + f) * 4 + q) * 64] =
                                 make_int4(acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]);
-            } else if (WK == WK_I8 && full && !ACC) {
+            } else if (wk_i8w(WK) && full && !ACC) {
                 // int8 weights: direct stores (the LDS-staged epilogue below
-                // needs more registers than this instantiation has spare).
+                // needs more registers than this instantiation has spare);
+                // ConvRot INT8 takes a scale per column.
                 float sxv[FM];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) sxv[i] = p.sx[m0 + wm * WROWS + i * 32 + l32];
 #pragma unroll
                 for (int f = 0; f < FN; ++f) {
                     uint2 bv[4];
+                    float4 cv[4];                             // per-column scales (ConvRot INT8)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
                         bv[q] = p.bias != nullptr ? *reinterpret_cast<const uint2*>(p.bias + n) : make_uint2(0u, 0u);
+                        cv[q] = make_float4(sw0, sw0, sw0, sw0);
+                        if constexpr (wk_chan(WK)) cv[q] = *reinterpret_cast<const float4*>(p.wscale + n);
                     }
 #pragma unroll
                     for (int i = 0; i < FM; ++i) {
@@ -462,11 +466,12 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                         for (int q = 0; q < 4; ++q) {
                             const int n = n0 + (wn * FN + f) * 32 + 4 * h + 8 * q;
                             const float b[4] = {bf16_lo(bv[q].x), bf16_hi(bv[q].x), bf16_lo(bv[q].y), bf16_hi(bv[q].y)};
+                            const float c[4] = {cv[q].x, cv[q].y, cv[q].z, cv[q].w};
                             float v[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 v[j] = (float)acc[i][f][4 * q + j] * sxv[i];
-                                v[j] = v[j] * sw0;
+                                v[j] = v[j] * c[j];
                                 if (p.bias != nullptr) v[j] = v[j] + b[j];
                             }
                             *reinterpret_cast<uint2*>(p.y + (size_t)m * p.N + n) =
@@ -518,7 +523,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                     const int col = min(c * 64 + lane, NCW - 1);
                     bl[c] = p.bias != nullptr ? p.bias[nw0 + col] : (uint16_t)0;
                     cl[c] = sw0;
-                    if constexpr (WK == WK_W4A8) cl[c] = p.wscale[nw0 + col];
+                    if constexpr (wk_chan(WK)) cl[c] = p.wscale[nw0 + col];
                     cnl[c] = 0;
                     if constexpr (C::PA) cnl[c] = -128 * p.cw[nw0 + col];
                 }
@@ -628,7 +633,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 // per CU; ring depth 6 for 4-bit weights (144 KiB of LDS; W4A8 154 KiB with
 // its table), 4 for int8 weights (128 KiB).
 constexpr int BIG_NW = 8;
-template <int WK> constexpr int big_stages() { return WK == WK_I8 ? 4 : 6; }
+template <int WK> constexpr int big_stages() { return wk_i8w(WK) ? 4 : 6; }
 
 // Compute units of the current device (cached per device).
 static int num_cus() {
@@ -678,7 +683,7 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
     }
     if (m >= p.M) return;
     const Epi epi = make_epi(p);
-    const float sw0 = (WK == WK_W4A8 || ACC) ? 0.0f : p.wscale[0];
+    const float sw0 = (wk_chan(WK) || ACC) ? 0.0f : p.wscale[0];
     const float sxm = ACC ? 0.0f : p.sx[m];
     const int nbase = n0 + ((wave / WM) * FN + f) * 32 + 4 * h;
 #pragma unroll
@@ -705,10 +710,10 @@ constexpr int BIG_MAX_SPLITS = 16;
 BigPlan plan_big(int kind, int M, int N, int K) {
     BigPlan bp{1, 0, 0, 256};
     if (M <= 0 || N <= 0 || K <= 0) return bp;
-    const int Kp = kind == WK_I8 ? round_up(K, 64) : K;
+    const int Kp = wk_i8w(kind) ? round_up(K, 64) : K;
     const int nkc = Kp / 64;
     bp.cps = nkc;
-    const double t_stage = kind == WK_W4 ? 0.8 : (kind == WK_I8 ? 1.0 : 1.3);
+    const double t_stage = kind == WK_W4 ? 0.8 : (wk_i8w(kind) ? 1.0 : 1.3);
     const double tiles_m = (double)((M + BIG_BM - 1) / BIG_BM);
     double best = std::ceil(tiles_m * ((N + 255) / 256) / BIG_CUS) * nkc * t_stage;
     for (int bn : {256, 192}) {
@@ -785,6 +790,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         case WK_W4: return launch_kind<WK_W4>(a, st);
         case WK_I8: return launch_kind<WK_I8>(a, st);
         case WK_W4A8: return launch_kind<WK_W4A8>(a, st);
+        case WK_I8R: return launch_kind<WK_I8R>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -38,6 +38,7 @@ constexpr int SM_W = 8;   // waves per block
 template <int WK> struct SmW;
 template <> struct SmW<WK_W4> { v2i a; };
 template <> struct SmW<WK_I8> { v4i a; };
+template <> struct SmW<WK_I8R> { v4i a; };
 template <> struct SmW<WK_W4A8> { v2i a; int c; };
 template <int WK> struct SmA { v4i a; };             // int8 activations
 template <> struct SmA<WK_W4> { v2i a; };            // packed 4-bit activations
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     // ---- buffer resources and per-lane offsets.  Weights: the (at most
     // three) 32-row bands the block's tiles live in; tile (band, chunk) is
     // WT bytes, row r of it at r * RB.  Activations: the whole code array.
-    constexpr int WT = WK == WK_I8 ? 2048 : 1024, RB = WK == WK_I8 ? 64 : 32;
+    constexpr int WT = wk_i8w(WK) ? 2048 : 1024, RB = wk_i8w(WK) ? 64 : 32;
     const int nt_first = min((int)blockIdx.x * NT, nt16 - 1);
     const int band0 = nt_first >> 1;
     const int nbands = min((p.Np >> 5) - band0, 3);
@@ -96,7 +97,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     for (int t = 0; t < NT; ++t) {
         const int nt = min((int)blockIdx.x * NT + t, nt16 - 1);
         wvo[t] = (uint32_t)((nt >> 1) - band0) * band_bytes + (uint32_t)(((nt & 1) * 16 + r16) * RB) +
-                 (uint32_t)(WK == WK_I8 ? 16 * g : 8 * g);
+                 (uint32_t)(wk_i8w(WK) ? 16 * g : 8 * g);
     }
     __amdgpu_buffer_rsrc_t rs_c = rs_w;                                 // replaced below for W4A8
     uint32_t cvo[NT];
@@ -130,7 +131,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
         const int kc = kc0 + min(b0 + i, kcs - 1);                      // wave-uniform
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if constexpr (WK == WK_I8) {
+            if constexpr (wk_i8w(WK)) {
                 wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b128(rs_w, wvo[t], kc * WT, 0);
             } else {
                 wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b64(rs_w, wvo[t], kc * WT, 0);
@@ -177,7 +178,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
             v4i a;
             if constexpr (WK == WK_W4) {
                 a = unpack_wt4((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y);
-            } else if constexpr (WK == WK_I8) {
+            } else if constexpr (wk_i8w(WK)) {
                 a = wr[i][t].a;
             } else {
                 const uint32_t code = ((uint32_t)wr[i][t].c >> (8 * (2 * (g & 1) + (g >> 1)))) & 0xFFu;
@@ -199,7 +200,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     __syncthreads();
 
     const Epi epi = make_epi(p);
-    const float sw0 = (WK == WK_W4A8 || acc_mode) ? 0.0f : p.wscale[0];
+    const float sw0 = (wk_chan(WK) || acc_mode) ? 0.0f : p.wscale[0];
 #pragma unroll
     for (int k = 0; k < QPW; ++k) {
         const int q = wave + SM_W * k;
@@ -255,7 +256,7 @@ __global__ void __launch_bounds__(256) k_small_reduce(GemmArgs p, int mt, int ac
     if (acc_mode) {
         store4<WK, true>(epi, m, n, 0.0f, 0.0f, a.x, a.y, a.z, a.w);
     } else {
-        const float sw0 = (WK == WK_W4A8) ? 0.0f : p.wscale[0];
+        const float sw0 = wk_chan(WK) ? 0.0f : p.wscale[0];
         store4<WK, false>(epi, m, n, p.sx[m], sw0, a.x, a.y, a.z, a.w);
     }
 }
@@ -287,7 +288,7 @@ constexpr int SM_MAX_SPLITS = 16;
 
 // VGPRs of one chunk's loads; a wave holds at most 128 of them.
 __host__ __device__ constexpr int small_regs_per_chunk(int wk, int mt, int nt) {
-    return nt * (wk == WK_W4 ? 2 : (wk == WK_I8 ? 4 : 3)) + mt * (wk == WK_W4 ? 2 : 4);
+    return nt * (wk == WK_W4 ? 2 : (wk_i8w(wk) ? 4 : 3)) + mt * (wk == WK_W4 ? 2 : 4);
 }
 constexpr int SM_LOAD_REGS = 128;
 
@@ -295,14 +296,14 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
     SmallPlan sp{};
     sp.use = M > 0 && M <= kSmallMaxM;
     if (!sp.use) return sp;
-    const int Kp = kind == WK_I8 ? round_up(K, 64) : K;
+    const int Kp = wk_i8w(kind) ? round_up(K, 64) : K;
     const int nkc = Kp / 64;
     const int nt16 = (N + 15) / 16;
     sp.mt = (M + 15) / 16;
     sp.nt = small_nt(sp.mt);
     const int nblk = (nt16 + sp.nt - 1) / sp.nt;
     const int per_chunk = small_regs_per_chunk(kind, sp.mt, sp.nt);
-    const double wbytes = kind == WK_W4 ? 0.5 : (kind == WK_I8 ? 1.0 : 0.5625);
+    const double wbytes = kind == WK_W4 ? 0.5 : (wk_i8w(kind) ? 1.0 : 0.5625);
     const double abytes = kind == WK_W4 ? 0.5 : 1.0;
     double best = 1e30;
     for (int S = 1; S <= nkc && S <= SM_MAX_SPLITS; ++S) {
@@ -394,6 +395,7 @@ hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st) 
         case WK_W4: return launch_small_t<WK_W4>(a, sp, st);
         case WK_I8: return launch_small_t<WK_I8>(a, sp, st);
         case WK_W4A8: return launch_small_t<WK_W4A8>(a, sp, st);
+        case WK_I8R: return launch_small_t<WK_I8R>(a, sp, st);
         default: return hipErrorInvalidValue;
     }
 }

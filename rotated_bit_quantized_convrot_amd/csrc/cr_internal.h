@@ -6,7 +6,13 @@
 
 namespace cr {
 
-enum WKind { WK_W4 = 0, WK_I8 = 1, WK_W4A8 = 2 };
+enum WKind { WK_W4 = 0, WK_I8 = 1, WK_W4A8 = 2, WK_I8R = 3 };
+
+// int8 weights in the int8 tile layout (int8_tensorwise; ConvRot INT8,
+// row-scaled) and weights with one scale per output column (W4A8 s_channel;
+// ConvRot INT8's row scales).
+__host__ __device__ constexpr bool wk_i8w(int wk) { return wk == WK_I8 || wk == WK_I8R; }
+__host__ __device__ constexpr bool wk_chan(int wk) { return wk == WK_W4A8 || wk == WK_I8R; }
 
 // Packed-weight geometry.
 //   Np = N rounded up to 32 (rows past N are zero), Kp = K rounded up to 64.
@@ -55,6 +61,9 @@ hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* 
                           hipStream_t st);
 hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
                           hipStream_t st);
+// ConvRot INT8 row-scaled: rotated rows, scale[n] = absmax / 127 per row.
+hipError_t launch_pack_i8rot(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                             hipStream_t st);
 hipError_t launch_pack_w4a8(const uint8_t* idx, const uint8_t* s_rel, const float* cb, int N,
                             int K, uint8_t* out, hipStream_t st);
 hipError_t launch_unpack_weight(int kind, const uint8_t* packed, int N, int K, int8_t* out,
@@ -114,7 +123,7 @@ inline bool act_packed(int kind) { return kind == WK_W4; }
 // Bytes of the activation codes in the workspace.
 inline size_t act_bytes(int kind, int M, int K) {
     if (act_packed(kind)) return (size_t)round_up(M, 32) * (size_t)K / 2;
-    return (size_t)M * (size_t)(kind == WK_I8 ? round_up(K, 64) : K);
+    return (size_t)M * (size_t)(wk_i8w(kind) ? round_up(K, 64) : K);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

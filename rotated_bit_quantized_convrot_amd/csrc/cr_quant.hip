@@ -420,7 +420,8 @@ hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, i
         return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, ra, st)
                       : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, nullptr, st);
     }
-    if (kind == WK_W4A8) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
+    // W4A8 and ConvRot INT8: rotated, per-row int8
+    if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
     // two waves per row when four per row would exceed what the chip holds at once
     k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
@@ -578,6 +579,64 @@ hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* 
     return hipGetLastError();
 }
 
+// --- ConvRot INT8, row-scaled ---------------------------------------------
+
+// One block per row n of the padded weight: the row rotated group by group,
+// its absmax, scale[n] = absmax / 127 (IEEE division), codes
+// clamp(rint(v / scale[n]), -128, 127) in the int8 tile layout (K % 256 == 0,
+// so Kp = K).  Padding rows get zero codes.
+template <int GPL>
+__global__ void __launch_bounds__(512) k_pack_i8rot(const uint16_t* __restrict__ w, int N, int K,
+                                                    uint8_t* __restrict__ out, float* __restrict__ scale) {
+    __shared__ float red[16];
+    const int n = blockIdx.x;
+    const int G = K >> 8, nkc = K >> 6;
+    const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
+    const int nb = n >> 5, r = n & 31;
+    // the 8 codes of k0..k0+7 (k0 % 8 == 0) are 8 consecutive bytes of the tile
+    auto dst = [&](int k0) -> uint2* {
+        const int kc = k0 >> 6, kk = k0 & 63;
+        return reinterpret_cast<uint2*>(out + ((size_t)nb * nkc + kc) * 2048 + r * 64 +
+                                        32 * ((kk >> 4) & 1) + 16 * (kk >> 5) + (kk & 15));
+    };
+    if (n >= N) {                                       // padding rows (whole block)
+        for (int i = 0; i < GPL; ++i) {
+            const int g = hw + i * nhw;
+            if (g < G) *dst(g * 256 + lane32 * 8) = make_uint2(0u, 0u);
+        }
+        return;
+    }
+    RotRow<GPL> rr;
+    const float amax = block_max(rr.load_rotate(w + (size_t)n * K, G, hw, nhw, lane32), red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) scale[n] = s;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const int g = hw + i * nhw;
+        if (g < G) {
+            int q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quant_code<-128, 127>(rr.v[i][j], s);
+            *dst(g * 256 + lane32 * 8) = make_uint2(pack4_i8(q[0], q[1], q[2], q[3]), pack4_i8(q[4], q[5], q[6], q[7]));
+        }
+    }
+}
+
+hipError_t launch_pack_i8rot(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+                             hipStream_t st) {
+    const int Np = round_up(N, 32);
+    int gpl = 1;
+    const int threads = rot_threads(K >> 8, &gpl);
+    switch (gpl) {
+#define CR_PACK8R_CASE(G_) \
+    case G_: k_pack_i8rot<G_><<<dim3(Np), dim3(threads), 0, st>>>(w, N, K, out, scale); break;
+        CR_PACK8R_CASE(1) CR_PACK8R_CASE(2) CR_PACK8R_CASE(4) CR_PACK8R_CASE(8) CR_PACK8R_CASE(16)
+#undef CR_PACK8R_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // --- W4A8 -----------------------------------------------------------------
 
 // One thread per W4-layout dword: re-orders the canonical index nibbles
@@ -657,7 +716,7 @@ __global__ void __launch_bounds__(256) k_unpack_weight(int kind, const uint8_t* 
     const int t = kk >> 5, h = (kk >> 4) & 1, pp = kk & 15;
     const size_t tile = (size_t)nb * (Kp >> 6) + kc;
     int v;
-    if (kind == WK_I8) {
+    if (wk_i8w(kind)) {
         v = (int8_t)p[tile * 2048 + r * 64 + 32 * h + 16 * t + pp];
     } else {
         const int d = pp >> 3, b = pp & 3, hi = (pp >> 2) & 1;

@@ -114,6 +114,14 @@ def te_down(M: int = 76, seed: int = 1) -> LayerInputs:
                       outlier_frac=0.005, outlier_scale=40.0)
 
 
+def te_attn_proj(M: int = 76, seed: int = 2) -> LayerInputs:
+    """Stand-in for a text-encoder attention projection in the ConvRot INT8
+    row-scaled format: square, at the encoder's hidden width (the pages give
+    the format's role, not the layer dimensions)."""
+    return make_layer(f"te_attn_proj_M{M}", M, 2560, 2560, seed=seed,
+                      outlier_frac=0.005, outlier_scale=40.0)
+
+
 def dit_w1(M: int = 4096, seed: int = 0) -> LayerInputs:
     return make_layer(f"dit_w1_M{M}", M, 3072, 12288, seed=seed, x_dist="student_t",
                       outlier_frac=0.01, outlier_scale=50.0, bias_std=0.01)

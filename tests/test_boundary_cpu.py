@@ -122,3 +122,15 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("the oracle", ""), f
+
+
+def test_int8rot_sizes_and_group(L):
+    # ConvRot INT8 row-scaled: int8 tile layout (rows to 32); K % 256 == 0
+    assert L.cr_packed_bytes(3, 2560, 2560) == 2560 * 2560
+    assert L.cr_packed_bytes(3, 100, 512) == 128 * 512
+    assert L.cr_packed_bytes(3, 64, 2688) == 0
+    assert L.cr_workspace_bytes(3, 1220, 2560, 2560) >= 1220 * 2560 + 1220 * 4
+    assert L.cr_packed_bytes(4, 64, 256) == 0
+    vp = ctypes.c_void_p(16)
+    assert L.cr_pack_weight_int8rot(vp, 64, 2688, vp, vp, None) == CR["GROUP"]
+    assert L.cr_linear_int8rot(vp, 8, 300, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]

@@ -66,6 +66,28 @@ def test_w4a4_full_size(crp, name):
     _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, sw, L.bias))
 
 
+INT8ROT_LAYERS = {"int8rot_attn_M76": lambda: si.te_attn_proj(76),
+                  "int8rot_attn_M1220": lambda: si.te_attn_proj(1220)}
+
+
+@pytest.mark.parametrize("name", list(INT8ROT_LAYERS))
+def test_int8rot_full_size(crp, name):
+    print(f"[fullsize] {name}", flush=True)
+    L = INT8ROT_LAYERS[name]()
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_int8rot(to_dev_bf16(L.w))
+    ws = torch.empty(crp.workspace_bytes(3, L.M, L.N, L.K), dtype=torch.uint8, device="cuda")
+    y = crp.linear_int8rot(x, p, s, L.N, workspace=ws)
+    acc = crp.dbg_linear_acc(3, x, p, L.N, workspace=ws)
+    torch.cuda.synchronize()
+    rows = _rows(L.M)
+    qw, sw = O.quant_weight_int8rot(L.w)
+    assert np.array_equal(s.cpu().numpy()[:L.N].view(np.uint32), sw.view(np.uint32))
+    qx, sx = O.quant_act_int8rot(L.x[rows])
+    ref_acc = O.int_gemm(qx, qw)
+    _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, sw, None))
+
+
 INT8_LAYERS = {"int8tw_vo": lambda: si.int8tw_vo(), "int8tw_k2688": lambda: si.int8tw_k2688()}
 
 

@@ -30,6 +30,7 @@ KIND_ORACLE_ACT = {
     0: O.quant_act_w4a4,
     1: O.quant_act_int8,
     2: O.quant_act_w4a8,
+    3: O.quant_act_int8rot,
 }
 
 
@@ -46,6 +47,7 @@ ACT_CASES = [
     # grids larger than the chip holds at once: two groups per lane (rotated)
     # or two waves per row (int8_tensorwise)
     (2, 2100, 3840), (0, 1100, 8192), (1, 2100, 640),
+    (3, 76, 2560), (3, 300, 512), (3, 5, 9728),
 ]
 
 
@@ -301,6 +303,36 @@ def test_split_k_acc_and_output(crp, kind, M, K, N, bias):
         r = O.linear_w4a8(L.x, enc["idx_packed"], enc["s_rel"], enc["codebook"], enc["s_channel"], L.bias)
     a = crp.dbg_linear_acc(kind, x, p, N)
     _sync()
+    assert np.array_equal(a.cpu().numpy(), r["acc"])
+    assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(r["y"]))
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (100, 2560), (33, 256)])
+def test_pack_int8rot_bitexact(crp, N, K):
+    """ConvRot INT8 row-scaled weight: codes and per-row scales bit-exact."""
+    L = si.random_layer(1, K, N, seed=N + 3 * K, outlier_count=4)
+    L.w[min(5, N - 1), :] = 0                               # a zero row: scale 0, codes 0
+    p, s = crp.pack_weight_int8rot(to_dev_bf16(L.w))
+    codes = crp.dbg_unpack_weight(3, p, N, K)
+    _sync()
+    q_ref, s_ref = O.quant_weight_int8rot(L.w)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy()[:N].view(np.uint32), s_ref.view(np.uint32))
+
+
+# small M, K split across blocks at large M, full 256 x 192 tiles, ragged N
+@pytest.mark.parametrize("M,K,N,bias", [(76, 2560, 512, False), (7, 256, 33, True), (300, 4096, 512, True),
+                                        (1025, 512, 768, True), (260, 2560, 200, False)])
+def test_int8rot_acc_and_output(crp, M, K, N, bias):
+    L = si.random_layer(M, K, N, seed=M + K + N, bias=bias, outlier_count=6)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_int8rot(to_dev_bf16(L.w))
+    b = to_dev_bf16(L.bias) if bias else None
+    y = crp.linear_int8rot(x, p, s, N, b)
+    a = crp.dbg_linear_acc(3, x, p, N)
+    _sync()
+    r = O.linear_int8rot(L.x, L.w, L.bias)
     assert np.array_equal(a.cpu().numpy(), r["acc"])
     assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
     assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(r["y"]))
