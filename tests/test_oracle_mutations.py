@@ -99,6 +99,14 @@ def _pack_high_first(q):
     return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
 
 
+def _fwht_group_ignored(v, group=256, dtype=np.float32):
+    return _fwht_generic(v, 256, dtype)
+
+
+def _fwht_norm_of_256(v, group=256, dtype=np.float32):
+    return (_fwht_generic(v, group, dtype, scale=False) * dtype(1.0 / 16.0)).astype(dtype)
+
+
 MUTATIONS = {
     "fwht_descending_order": ("fwht", lambda v, group=256, dtype=np.float32:
                               _fwht_generic(v, group, dtype, order="desc")),
@@ -116,6 +124,8 @@ MUTATIONS = {
     "pack_nibble_order": ("pack_int4", _pack_high_first),
     "int8rot_weight_scale_per_tensor": ("quant_weight_int8rot", _int8rot_weight_tensor_scale),
     "int8rot_weight_unrotated": ("quant_weight_int8rot", _int8rot_weight_unrotated),
+    "fwht_group_ignored": ("fwht", _fwht_group_ignored),
+    "fwht_group_norm_of_256": ("fwht", _fwht_norm_of_256),
 }
 
 PINS = [
@@ -138,6 +148,11 @@ PINS = [
     P.test_int8rot_row_scale_invariance,
     P.test_int8rot_one_hot_weight_rows,
     P.test_int8rot_acc_brute_force_python_ints,
+    lambda: P.test_fwht_group_unit_vectors_block_diagonal(16),
+    lambda: P.test_fwht_group_float64_equals_dense_block_product(64),
+    lambda: P.test_group_one_hot_row_codes(64),
+    lambda: P.test_group_constant_row_codes(16, 0.5),
+    lambda: P.test_group_weight_one_hot_codes(16),
 ]
 
 

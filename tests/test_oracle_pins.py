@@ -427,3 +427,109 @@ def test_int8rot_row_scaling_beats_tensorwise_on_uneven_rows():
     err_small_t = np.linalg.norm((qt * st - wr)[small]) / np.linalg.norm(wr[small])
     assert err_small_row < 0.02 and err_small_t > 4 * err_small_row
     assert err_row < 0.02
+
+
+# ---------------------------------------------------------------------------
+# Smaller rotation groups ([ZIT] "Where Z-Image sits": group sizes 64 and 16)
+# ---------------------------------------------------------------------------
+
+def _sylvester(n):
+    g = np.array([[1.0]])
+    while g.shape[0] < n:
+        g = np.block([[g, g], [g, -g]])
+    return g
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_fwht_group_unit_vectors_block_diagonal(G):
+    """e_j rotated in groups of G: (-1)^popcount((j % G) & (k % G)) / sqrt(G)
+    inside j's group, zero in every other group."""
+    K = 256
+    got = O.fwht(np.eye(K, dtype=F32), G).astype(np.float64)
+    want = np.zeros((K, K))
+    for j in range(K):
+        for k in range(K):
+            if j // G == k // G:
+                want[j, k] = (-1.0) ** _popcount((j % G) & (k % G)) / np.sqrt(G)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_fwht_group_float64_equals_dense_block_product(G):
+    rng = np.random.default_rng(G)
+    x = rng.normal(size=(3, 512))
+    got = O.fwht(x, G, dtype=np.float64)
+    H = _sylvester(G) / np.sqrt(G)
+    want = (x.reshape(3, 512 // G, G) @ H).reshape(3, 512)
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_fwht_group_float32_within_error_bound(G):
+    rng = np.random.default_rng(40 + G)
+    x32 = rng.standard_t(3, size=(6, 512)).astype(F32)
+    got = O.fwht(x32, G).astype(np.float64)
+    H = _sylvester(G) / np.sqrt(G)
+    want = (x32.astype(np.float64).reshape(6, 512 // G, G) @ H).reshape(6, 512)
+    stages = int(np.log2(G))
+    l1 = np.abs(x32.astype(np.float64)).reshape(6, 512 // G, G).sum(-1)
+    bound = stages * 2.0 ** -24 * l1 / np.sqrt(G) * 1.0001
+    err = np.abs(got - want).reshape(6, 512 // G, G)
+    assert np.all(err <= bound[:, :, None])
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_group_one_hot_row_codes(G):
+    """x = 3 e_j: codes 7 (-1)^popcount((j % G) & (k % G)) in j's group, 0
+    elsewhere; scale fl(fl(3 / sqrt(G)) / 7)."""
+    K, j = 512, 300
+    x = np.zeros((1, K), F32)
+    x[0, j] = 3.0
+    q, s = O.quant_act_w4a4(si.f32_to_bf16_bits(x), G)
+    want = np.zeros(K, np.int8)
+    g0 = (j // G) * G
+    for k in range(G):
+        want[g0 + k] = 7 if _popcount((j % G) & k) % 2 == 0 else -7
+    assert np.array_equal(q[0], want)
+    assert s[0] == F32(F32(3.0 / np.sqrt(G)) / F32(7))
+
+
+@pytest.mark.parametrize("G", [16, 64])
+@pytest.mark.parametrize("c", [0.5, -2.0])
+def test_group_constant_row_codes(G, c):
+    """A constant row rotates to sqrt(G) c at the first k of every group and 0
+    elsewhere: codes +-7 there, scale fl(fl(sqrt(G) |c|) / 7)."""
+    K = 768
+    x = np.full((1, K), c, F32)
+    q, s = O.quant_act_w4a4(si.f32_to_bf16_bits(x), G)
+    want = np.zeros(K, np.int8)
+    want[0::G] = 7 if c > 0 else -7
+    assert np.array_equal(q[0], want)
+    assert s[0] == F32(F32(np.sqrt(G) * abs(c)) / F32(7))
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_group_exact_identity_before_quantisation(G):
+    L = si.tiny()
+    x = O.bf16_to_f32(L.x).astype(np.float64)
+    w = O.bf16_to_f32(L.w).astype(np.float64)
+    lhs = O.fwht(x, G, dtype=np.float64) @ O.fwht(w, G, dtype=np.float64).T
+    rhs = x @ w.T
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_group_weight_one_hot_codes(G):
+    """A weight whose largest entry is c e_j in row n: that row's codes are
+    7 (-1)^popcount(...) in j's group (the tensor absmax comes from it)."""
+    N, K, n, j = 4, 256, 2, 77
+    w = np.zeros((N, K), F32)
+    w[n, j] = -5.0
+    w[0, 3] = 1.0
+    q, s = O.quant_weight_w4(si.f32_to_bf16_bits(w), G)
+    g0 = (j // G) * G
+    for k in range(G):
+        sign = 1 if _popcount((j % G) & k) % 2 == 0 else -1
+        assert q[n, g0 + k] == -7 * sign
+    assert np.all(q[n, :g0] == 0) and np.all(q[n, g0 + G:] == 0)
+    assert s == F32(F32(5.0 / np.sqrt(G)) / F32(7))
