@@ -60,7 +60,8 @@ typedef enum {
     CR_OK = 0,
     CR_ERR_NULL = 1,       /* a required pointer is NULL                        */
     CR_ERR_SHAPE = 2,      /* M < 0, N < 1, K < 1, or a size beyond the limits  */
-    CR_ERR_GROUP = 3,      /* K is not a multiple of 256 (W4A4, W4A8)           */
+    CR_ERR_GROUP = 3,      /* K is not a multiple of 256 (rotated formats), or an
+                              unsupported rotation group size                   */
     CR_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                  */
     CR_ERR_WORKSPACE = 5,  /* workspace smaller than cr_workspace_bytes()       */
     CR_ERR_DEVICE = 6,     /* current device is not gfx950 / no device          */
@@ -74,6 +75,8 @@ typedef enum {
 #define CR_W4A8 2    /* asym W4A8 codebook: 4-bit codebook weights, int8 activations */
 #define CR_INT8ROT 3 /* ConvRot INT8 row-scaled: rotated int8 weights (one scale per
                         output row), rotated int8 activations */
+#define CR_W4A4_G64 4 /* ConvRot W4A4 with rotation groups of 64 (layout as CR_W4A4) */
+#define CR_W4A4_G16 5 /* ConvRot W4A4 with rotation groups of 16 (layout as CR_W4A4) */
 
 /* Limits: 1 <= N, K <= CR_MAX_DIM; 0 <= M <= CR_MAX_DIM. */
 #define CR_MAX_DIM (1 << 20)
@@ -112,6 +115,24 @@ cr_status cr_pack_weight_w4(const void* w_bf16, int N, int K, void* w_packed,
 cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed,
                          const float* w_scale, int N, const void* bias_bf16,
                          void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- W4A4 with smaller rotation groups ([ZIT] "Where Z-Image sits": the
+ *      ConvRot group-size sweep 256 / 64 / 16) ------------------------------
+ * As cr_pack_weight_w4 / cr_linear_w4a4 with the Hadamard rotation applied
+ * to groups of `group` = 256, 64 or 16 consecutive k (normalised by
+ * 1/sqrt(group)); any other value -> CR_ERR_GROUP.  K must still be a
+ * multiple of 256.  The packed layout and sizes are those of CR_W4A4
+ * (cr_packed_bytes / cr_workspace_bytes with CR_W4A4_G64 or CR_W4A4_G16 give
+ * the same figures); the generic calls (cr_quantize_activations,
+ * cr_gemm_quantized, cr_dbg_*) take the kinds CR_W4A4_G64 / CR_W4A4_G16.
+ * A weight must be used with the group it was packed with: nothing in the
+ * packed bytes records it. */
+cr_status cr_pack_weight_w4_group(const void* w_bf16, int N, int K, int group, void* w_packed,
+                                  float* w_scale, hipStream_t stream);
+
+cr_status cr_linear_w4a4_group(const void* x_bf16, int M, int K, int group, const void* w_packed,
+                               const float* w_scale, int N, const void* bias_bf16, void* y_bf16,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- int8_tensorwise ([QIE] intro "stock int8_tensorwise"; [REB] "Mixed
  *      formats": no group constraint) -------------------------------------- */

@@ -25,7 +25,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A4", "INT8TW", "W4A8", "INT8ROT", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
+    "W4A4", "INT8TW", "W4A8", "INT8ROT", "W4A4_G64", "W4A4_G16", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
     "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8", "pack_weight_int8rot",
     "linear_w4a4", "linear_int8tw", "linear_w4a8", "linear_int8rot",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
@@ -33,7 +33,9 @@ __all__ = [
     "PackedWeight", "pack_linear", "linear",
 ]
 
-W4A4, INT8TW, W4A8, INT8ROT = 0, 1, 2, 3
+W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16 = 0, 1, 2, 3, 4, 5
+# W4A4 kind of each rotation group size
+W4_GROUP_KIND = {256: W4A4, 64: W4A4_G64, 16: W4A4_G16}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.so")
 _LIB = None
 
@@ -46,6 +48,7 @@ EXPORTS = [
     "cr_status_str", "cr_last_error", "cr_dbg_quant_act", "cr_dbg_unpack_weight",
     "cr_dbg_linear_acc", "cr_quantize_activations", "cr_gemm_quantized",
     "cr_pack_weight_int8rot", "cr_linear_int8rot",
+    "cr_pack_weight_w4_group", "cr_linear_w4a4_group",
 ]
 
 
@@ -75,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "cr_pack_weight_w4a8": (i, [vp, vp, vp, i, i, vp, vp]),
         "cr_pack_weight_int8rot": (i, [vp, i, i, vp, vp, vp]),
         "cr_linear_int8rot": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_pack_weight_w4_group": (i, [vp, i, i, i, vp, vp, vp]),
+        "cr_linear_w4a4_group": (i, [vp, i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
@@ -132,8 +137,9 @@ def _empty_u8(n: int, device) -> torch.Tensor:
 # Weight preparation (offline)
 # ---------------------------------------------------------------------------
 
-def pack_weight_w4(w: torch.Tensor):
-    """bf16 [N,K] -> (packed uint8, scale float32[1]) in the W4A4 format."""
+def pack_weight_w4(w: torch.Tensor, group: int = 256):
+    """bf16 [N,K] -> (packed uint8, scale float32[1]) in the W4A4 format,
+    rotated in groups of ``group`` (256, 64 or 16)."""
     _dev(w, "w", torch.bfloat16)
     N, K = w.shape
     nb = packed_bytes(W4A4, N, K)
@@ -141,7 +147,10 @@ def pack_weight_w4(w: torch.Tensor):
         _check(lib().cr_pack_weight_w4(_ptr(w), N, K, None, None, None) or 2)
     out = _empty_u8(nb, w.device)
     scale = torch.empty(4, dtype=torch.float32, device=w.device)
-    _check(lib().cr_pack_weight_w4(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
+    if group == 256:
+        _check(lib().cr_pack_weight_w4(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
+    else:
+        _check(lib().cr_pack_weight_w4_group(_ptr(w), N, K, group, _ptr(out), _ptr(scale), _stream()))
     return out, scale
 
 
@@ -192,7 +201,7 @@ def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Ten
 # Linears
 # ---------------------------------------------------------------------------
 
-def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace):
+def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace, group=None):
     _dev(x, "x", torch.bfloat16)
     _dev(packed, "packed", torch.uint8)
     _dev(scale, "scale", torch.float32)
@@ -217,14 +226,19 @@ def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace):
     else:
         _dev(workspace, "workspace", torch.uint8)
     fn = getattr(lib(), fn_name)
-    _check(fn(_ptr(x), M, K, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
+    lead = (_ptr(x), M, K) if group is None else (_ptr(x), M, K, group)
+    _check(fn(*lead, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
               _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
-def linear_w4a4(x, packed, scale, N, bias=None, out=None, workspace=None):
-    """y = ConvRot W4A4 linear (x bf16 [M,K], K % 256 == 0)."""
-    return _linear("cr_linear_w4a4", W4A4, x, packed, scale, N, bias, out, workspace)
+def linear_w4a4(x, packed, scale, N, bias=None, out=None, workspace=None, group: int = 256):
+    """y = ConvRot W4A4 linear (x bf16 [M,K], K % 256 == 0), rotation groups
+    of ``group`` (the group the weight was packed with)."""
+    if group == 256:
+        return _linear("cr_linear_w4a4", W4A4, x, packed, scale, N, bias, out, workspace)
+    return _linear("cr_linear_w4a4_group", W4_GROUP_KIND.get(group, W4A4), x, packed, scale, N, bias, out,
+                   workspace, group=group)
 
 
 def linear_int8tw(x, packed, scale, N, bias=None, out=None, workspace=None):
@@ -322,22 +336,27 @@ class PackedWeight:
     bias: Optional[torch.Tensor] = None
 
 
-def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None, int8: bool = False) -> PackedWeight:
+def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None, int8: bool = False,
+                group: int = 256) -> PackedWeight:
     """Pack a bf16 [N,K] weight: W4A4 ConvRot when K % 256 == 0 (ConvRot INT8
     row-scaled instead with ``int8=True``, the format [Q3N] gives attention
-    projections), otherwise int8_tensorwise ([REB] "Mixed formats where the
+    projections; ``group`` picks the W4A4 rotation group: 256, 64 or 16),
+    otherwise int8_tensorwise ([REB] "Mixed formats where the
     kernel demands it")."""
     N, K = w.shape
     if K % 256 == 0 and int8:
         p, s = pack_weight_int8rot(w)
         return PackedWeight(INT8ROT, N, K, p, s, bias)
     if K % 256 == 0:
-        p, s = pack_weight_w4(w)
-        return PackedWeight(W4A4, N, K, p, s, bias)
+        p, s = pack_weight_w4(w, group)
+        return PackedWeight(W4_GROUP_KIND.get(group, W4A4), N, K, p, s, bias)
     p, s = pack_weight_int8tw(w)
     return PackedWeight(INT8TW, N, K, p, s, bias)
 
 
 def linear(x: torch.Tensor, pw: PackedWeight, out=None, workspace=None) -> torch.Tensor:
+    if pw.kind in (W4A4_G64, W4A4_G16):
+        group = 64 if pw.kind == W4A4_G64 else 16
+        return linear_w4a4(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace, group=group)
     fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8, INT8ROT: linear_int8rot}[pw.kind]
     return fn(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace)

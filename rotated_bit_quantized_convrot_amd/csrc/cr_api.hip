@@ -48,13 +48,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t a256(size_t v) { return (v + 255) / 256 * 256; }
 
-bool rotated(int kind) { return kind == CR_W4A4 || kind == CR_W4A8 || kind == CR_INT8ROT; }
+bool rotated(int kind) { return kind != CR_INT8TW; }
 
 cr_status check_kind(int kind) {
-    if (kind != CR_W4A4 && kind != CR_INT8TW && kind != CR_W4A8 && kind != CR_INT8ROT)
-        return fail(CR_ERR_KIND, "unknown kind %d", kind);
+    if (kind < CR_W4A4 || kind > CR_W4A4_G16) return fail(CR_ERR_KIND, "unknown kind %d", kind);
     return CR_OK;
 }
+
+// Rotation group of a kind (the W4A4 group variants; 256 for the others).
+int group_of(int kind) { return kind == CR_W4A4_G64 ? 64 : (kind == CR_W4A4_G16 ? 16 : 256); }
 
 cr_status check_nk(int kind, int N, int K) {
     if (N < 1 || K < 1 || N > CR_MAX_DIM || K > CR_MAX_DIM)
@@ -70,7 +72,9 @@ cr_status check_nk(int kind, int N, int K) {
 
 size_t packed_bytes(int kind, int N, int K) {
     switch (kind) {
-        case CR_W4A4: return cr::w4a4_bytes(N, K);
+        case CR_W4A4:
+        case CR_W4A4_G64:
+        case CR_W4A4_G16: return cr::w4a4_bytes(N, K);
         case CR_INT8TW: return cr::i8_bytes(N, K);
         case CR_W4A8: return cr::w4a8_bytes(N, K);
         case CR_INT8ROT: return cr::i8_bytes(N, K);
@@ -82,7 +86,9 @@ int kp_of(int kind, int K) { return kind == CR_INT8TW ? cr::round_up(K, 64) : K;
 
 int wkind(int kind) {
     switch (kind) {
-        case CR_W4A4: return cr::WK_W4;
+        case CR_W4A4:
+        case CR_W4A4_G64:
+        case CR_W4A4_G16: return cr::WK_W4;
         case CR_INT8TW: return cr::WK_I8;
         case CR_INT8ROT: return cr::WK_I8R;
         default: return cr::WK_W4A8;
@@ -129,7 +135,8 @@ cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t
     if (ws_bytes < l.quant_end)
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.quant_end);
     char* w = static_cast<char*>(ws);
-    hipError_t e = cr::launch_quant_act(wkind(kind), static_cast<const uint16_t*>(x), M, K, kp_of(kind, K),
+    hipError_t e = cr::launch_quant_act(wkind(kind), group_of(kind), static_cast<const uint16_t*>(x), M, K,
+                                        kp_of(kind, K),
                                         reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
                                         reinterpret_cast<int32_t*>(w + l.ra), cr::act_packed(wkind(kind)), st);
     return launch_err(e, "activation quantisation");
@@ -221,9 +228,39 @@ cr_status cr_pack_weight_w4(const void* w_bf16, int N, int K, void* w_packed, fl
                             hipStream_t stream) {
     cr_status s = pack_common_checks(CR_W4A4, w_bf16, N, K, w_packed, w_scale);
     if (s != CR_OK) return s;
-    return launch_err(cr::launch_pack_w4(static_cast<const uint16_t*>(w_bf16), N, K,
+    return launch_err(cr::launch_pack_w4(static_cast<const uint16_t*>(w_bf16), N, K, 256,
                                          static_cast<uint8_t*>(w_packed), w_scale, stream),
                       "W4 weight packing");
+}
+
+static cr_status w4_group_kind(int group, int* kind) {
+    switch (group) {
+        case 256: *kind = CR_W4A4; return CR_OK;
+        case 64: *kind = CR_W4A4_G64; return CR_OK;
+        case 16: *kind = CR_W4A4_G16; return CR_OK;
+        default: return fail(CR_ERR_GROUP, "rotation group %d is not one of 256, 64, 16", group);
+    }
+}
+
+cr_status cr_pack_weight_w4_group(const void* w_bf16, int N, int K, int group, void* w_packed, float* w_scale,
+                                  hipStream_t stream) {
+    int kind = 0;
+    cr_status s = w4_group_kind(group, &kind);
+    if (s != CR_OK) return s;
+    if ((s = pack_common_checks(kind, w_bf16, N, K, w_packed, w_scale)) != CR_OK) return s;
+    return launch_err(cr::launch_pack_w4(static_cast<const uint16_t*>(w_bf16), N, K, group,
+                                         static_cast<uint8_t*>(w_packed), w_scale, stream),
+                      "W4 weight packing");
+}
+
+cr_status cr_linear_w4a4_group(const void* x_bf16, int M, int K, int group, const void* w_packed,
+                               const float* w_scale, int N, const void* bias_bf16, void* y_bf16, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    int kind = 0;
+    const cr_status s = w4_group_kind(group, &kind);
+    if (s != CR_OK) return s;
+    return run_linear(kind, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, ws_bytes,
+                      stream);
 }
 
 cr_status cr_pack_weight_int8tw(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
@@ -338,7 +375,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if (!aligned16(x_bf16) || !aligned16(codes)) return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
     if ((s = check_device()) != CR_OK) return s;
     const int wk = wkind(kind);
-    return launch_err(cr::launch_quant_act(wk, static_cast<const uint16_t*>(x_bf16), M, K, K,
+    return launch_err(cr::launch_quant_act(wk, group_of(kind), static_cast<const uint16_t*>(x_bf16), M, K, K,
                                            static_cast<int8_t*>(codes), scales, nullptr, false, stream),
                       "activation quantisation");
 }

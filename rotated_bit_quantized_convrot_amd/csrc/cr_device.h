@@ -71,11 +71,21 @@ __device__ __forceinline__ void fwht_cross(float (&v)[8], int lane32) {
     }
 }
 
-// Rotation of one 256-block held by the 32 lanes of a half-wave, lane j
-// holding elements 8j..8j+7 in v[0..7]: strides 1, 2, 4 inside the lane,
-// then 8, 16, 32, 64, 128 across lanes (lane bits 0..4), then x 1/16.
-// All 32 lanes of the half-wave must be active.
-__device__ __forceinline__ void fwht256(float (&v)[8], int lane32) {
+// 1 / sqrt(GS) for the rotation group sizes 16, 64 and 256 (powers of two,
+// so the normalisation is exact outside the subnormal range).
+template <int GS>
+__device__ __forceinline__ constexpr float rot_norm() {
+    static_assert(GS == 16 || GS == 64 || GS == 256, "rotation group size");
+    return GS == 256 ? 0.0625f : (GS == 64 ? 0.125f : 0.25f);
+}
+
+// Rotation of a 256-block held by the 32 lanes of a half-wave, lane j
+// holding elements 8j..8j+7 in v[0..7], as 256 / GS independent GS-groups:
+// strides 1, 2, 4 inside the lane, then 8, 16, ..., GS / 2 across lanes
+// (lane bits 0 .. log2(GS / 8) - 1), then x 1/sqrt(GS).  All 32 lanes of
+// the half-wave must be active.
+template <int GS>
+__device__ __forceinline__ void fwht8(float (&v)[8], int lane32) {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -88,18 +98,23 @@ __device__ __forceinline__ void fwht256(float (&v)[8], int lane32) {
         }
     }
     fwht_cross<1>(v, lane32);
-    fwht_cross<2>(v, lane32);
-    fwht_cross<4>(v, lane32);
-    fwht_cross<8>(v, lane32);
-    fwht_cross<16>(v, lane32);
+    if constexpr (GS >= 64) {
+        fwht_cross<2>(v, lane32);
+        fwht_cross<4>(v, lane32);
+    }
+    if constexpr (GS >= 256) {
+        fwht_cross<8>(v, lane32);
+        fwht_cross<16>(v, lane32);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] * 0.0625f;
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * rot_norm<GS>();
 }
 
-// Rotation of one 256-block held by 16 lanes, lane j holding elements
-// 16j..16j+15 in v[0..15]: strides 1, 2, 4, 8 inside the lane, then 16, 32,
-// 64, 128 across lanes (lane bits 0..3), with no final 1/16 (the caller
-// folds it into the scale).
+// Rotation of a 256-block held by 16 lanes, lane j holding elements
+// 16j..16j+15 in v[0..15], as 256 / GS independent GS-groups: strides 1, 2,
+// 4, 8 inside the lane, then 16, ..., GS / 2 across lanes (lane bits 0 ..
+// log2(GS / 16) - 1), with no final 1/sqrt(GS) (the caller folds it into
+// the scale).
 //
 // Cross-lane stages keep a per-lane sign: a lane holds sigma * (true value)
 // with sigma = (-1)^(number of cross stages in which it was the upper lane).
@@ -109,8 +124,8 @@ __device__ __forceinline__ void fwht256(float (&v)[8], int lane32) {
 // -sigma (a - b)): one instruction per value and stage, and since rounding
 // is symmetric the magnitudes are bitwise those of the plain butterflies
 // (a zero may carry the other sign, which no later add can tell apart).
-// On return sigma = (-1)^popcount(lane & 15).  All 16 lanes of each row
-// must be active.
+// On return sigma = (-1)^popcount(lane & (GS / 16 - 1)).  All 16 lanes of
+// each row must be active.
 #define CR_FMAC_DPP16(CTRL)                                                                   \
     asm("s_nop 1\n\t"                                                                           \
         "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                    \
@@ -156,7 +171,8 @@ __device__ __forceinline__ void fwht_cross16(float (&v)[16], int lane) {
     }
 }
 
-__device__ __forceinline__ void fwht256_x16_signed(float (&v)[16], int lane) {
+template <int GS>
+__device__ __forceinline__ void fwht16_signed(float (&v)[16], int lane) {
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -168,15 +184,20 @@ __device__ __forceinline__ void fwht256_x16_signed(float (&v)[16], int lane) {
             }
         }
     }
-    fwht_cross16<1>(v, lane);
-    fwht_cross16<2>(v, lane);
-    fwht_cross16<4>(v, lane);
-    fwht_cross16<8>(v, lane);
+    if constexpr (GS >= 64) {
+        fwht_cross16<1>(v, lane);
+        fwht_cross16<2>(v, lane);
+    }
+    if constexpr (GS >= 256) {
+        fwht_cross16<4>(v, lane);
+        fwht_cross16<8>(v, lane);
+    }
 }
 
-// The sign sigma that fwht256_x16_signed leaves in a lane.
-__device__ __forceinline__ float fwht_x16_sign(int lane) {
-    return (__builtin_popcount(lane & 15) & 1) ? -1.0f : 1.0f;
+// The sign sigma that fwht16_signed<GS> leaves in a lane.
+template <int GS>
+__device__ __forceinline__ float fwht16_sign(int lane) {
+    return (__builtin_popcount(lane & (GS / 16 - 1)) & 1) ? -1.0f : 1.0f;
 }
 
 // Symmetric code of v with scale s (IEEE division, round half to even).

@@ -53,11 +53,13 @@ __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_o
 // and scales [M]; with `packed` (W4A4 only) the codes go out 4-bit in the
 // 4-bit tile layout with rows = m (round_up(M, 32) rows, rows >= M left
 // untouched), in the activation nibble forms, and ra [M] (the sums of the
-// codes in high nibbles) beside them.
-hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
+// codes in high nibbles) beside them.  `group` is the W4A4 rotation group
+// (256, 64 or 16; the other kinds rotate, if at all, in groups of 256).
+hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
                             float* sx, int32_t* ra, bool packed, hipStream_t st);
 
-hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
+// W4 weight with rotation group `group` (256, 64 or 16).
+hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* out, float* scale,
                           hipStream_t st);
 hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
                           hipStream_t st);

@@ -11,10 +11,11 @@
 namespace cr {
 
 // ---------------------------------------------------------------------------
-// Rows rotated group by group.  One block per row; half-wave h handles groups
-// h, h + NHW, ... (at most GPL of them), each lane 8 consecutive values.
+// Rows rotated 256-block by 256-block (each block as 256 / GS rotation
+// groups of GS).  One block per row; half-wave h handles 256-blocks h,
+// h + NHW, ... (at most GPL of them), each lane 8 consecutive values.
 // ---------------------------------------------------------------------------
-template <int GPL>
+template <int GPL, int GS = 256>
 struct RotRow {
     float v[GPL][8];
 
@@ -31,7 +32,7 @@ struct RotRow {
                 v[i][2] = bf16_lo(raw.y); v[i][3] = bf16_hi(raw.y);
                 v[i][4] = bf16_lo(raw.z); v[i][5] = bf16_hi(raw.z);
                 v[i][6] = bf16_lo(raw.w); v[i][7] = bf16_hi(raw.w);
-                fwht256(v[i], lane32);
+                fwht8<GS>(v[i], lane32);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
             }
@@ -83,7 +84,7 @@ __device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
 }
 
 // Codes of a lane's 16 rotated values (unscaled, sign-tracked), see below.
-template <int QMAX, int LO, int HI>
+template <int QMAX, int LO, int HI, int GS>
 __device__ __forceinline__ void codes16(const float (&v)[16], bool fast, float rinv, float sigma, float s_u,
                                         float s, float (&r)[16]) {
     if (fast) {
@@ -103,7 +104,7 @@ __device__ __forceinline__ void codes16(const float (&v)[16], bool fast, float r
         }
     } else {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[t]) * 0.0625f, s);
+        for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[t]) * rot_norm<GS>(), s);
     }
 }
 
@@ -135,13 +136,14 @@ __device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
 // lanes, 256 / 2^seg_log2 rows per block; seg_log2 < 0: one row per block
 // (GPL groups per lane, strided by the block's group count).
 //
+// Rotation groups of GS = 256, 64 or 16 (a 256-block is 256 / GS groups).
 // The butterflies run on the unscaled values (sign-tracked, see
-// fwht256_x16_signed); the 1/16 of the rotation is folded into the scale.
-// With amax_u the row's max |value| before the 1/16, the stored scale is
-// s = fl(fl(amax_u / 16) / QMAX), and for 2^-100 <= amax_u <= 2^100 the code
-// fl(v/16 / s) equals fl(v / s_u), s_u = fl(amax_u / QMAX): scaling by 2^-4
-// commutes with rounding away from the subnormal range, and values too small
-// for that have code 0 either way.  That quotient is taken as v * fl(1/s_u):
+// fwht16_signed); the 1/sqrt(GS) = 2^-e of the rotation is folded into the
+// scale.  With amax_u the row's max |value| before the 2^-e, the stored
+// scale is s = fl(fl(amax_u 2^-e) / QMAX), and for 2^-100 <= amax_u <= 2^100
+// the code fl(v 2^-e / s) equals fl(v / s_u), s_u = fl(amax_u / QMAX):
+// scaling by a power of two commutes with rounding away from the subnormal
+// range, and values too small for that have code 0 either way.  That quotient is taken as v * fl(1/s_u):
 // the product is within QMAX * 2^-22.9 of v / s_u and the correctly rounded
 // quotient within half an ulp (< QMAX * 2^-23), so both round to the same
 // integer unless v / s_u lies within QMAX * 2^-20 of a half-integer; a lane
@@ -151,7 +153,7 @@ __device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
 //
 // PACKED (W4A4): codes in the 4-bit tile layout, activation nibble forms,
 // and ra[m] = the sum of the row's codes held in high nibbles (k % 8 >= 4).
-template <int GPL, int QMAX, int LO, int HI, bool PACKED>
+template <int GPL, int QMAX, int LO, int HI, bool PACKED, int GS>
 __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
                                                         int seg_log2, int8_t* __restrict__ qx,
                                                         float* __restrict__ sx, int32_t* __restrict__ ra) {
@@ -185,7 +187,7 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
                 v[i][2 * t] = bf16_lo(w[t]);
                 v[i][2 * t + 1] = bf16_hi(w[t]);
             }
-            fwht256_x16_signed(v[i], l);
+            fwht16_signed<GS>(v[i], l);
 #pragma unroll
             for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
         }
@@ -200,9 +202,9 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
     }
     if (!row_ok) return;
 
-    const float s = (amax * 0.0625f) / (float)QMAX;
+    const float s = (amax * rot_norm<GS>()) / (float)QMAX;
     if (l == 0) sx[m] = s;
-    const float sigma = fwht_x16_sign(l);
+    const float sigma = fwht16_sign<GS>(l);
     const bool fast = amax >= 0x1p-100f && amax <= 0x1p100f;
     const float s_u = amax / (float)QMAX;
     const float rinv = sigma * (1.0f / s_u);          // undoes the lane's sign too
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
         const int g = gslot + i * gstride;
         if (g < G) {
             float r[16];
-            codes16<QMAX, LO, HI>(v[i], fast, rinv, sigma, s_u, s, r);
+            codes16<QMAX, LO, HI, GS>(v[i], fast, rinv, sigma, s_u, s, r);
             if constexpr (PACKED) {
                 const size_t off = act4_offset(m, g * 256 + j * 16, K);
                 hsum += (int)(r[4] + r[5] + r[6] + r[7] + r[12] + r[13] + r[14] + r[15]);
@@ -248,7 +250,7 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
 // most), so that each store instruction writes, for every 64-k chunk it
 // touches, the four rows' 32-byte pieces: one whole 128-byte line of the
 // 4-bit tile.  Same arithmetic as k_quant_act_rot (PACKED).
-template <int GPL>
+template <int GPL, int GS>
 __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, int M, int K,
                                                          int8_t* __restrict__ qx, float* __restrict__ sx,
                                                          int32_t* __restrict__ ra) {
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
                 v[i][2 * t] = bf16_lo(w[t]);
                 v[i][2 * t + 1] = bf16_hi(w[t]);
             }
-            fwht256_x16_signed(v[i], j);
+            fwht16_signed<GS>(v[i], j);
 #pragma unroll
             for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
         }
@@ -286,8 +288,8 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
     amax = 0.0f;
     for (int w = 0; w < nw; ++w) amax = fmaxf(amax, redm[w][r]);
 
-    const float s = (amax * 0.0625f) / 7.0f;
-    const float sigma = fwht_x16_sign(j);
+    const float s = (amax * rot_norm<GS>()) / 7.0f;
+    const float sigma = fwht16_sign<GS>(j);
     const bool fast = amax >= 0x1p-100f && amax <= 0x1p100f;
     const float s_u = amax / 7.0f;
     const float rinv = sigma * (1.0f / s_u);
@@ -297,7 +299,7 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
         const int g = wave + i * nw;
         if (row_ok && g < G) {
             float c[16];
-            codes16<7, -8, 7>(v[i], fast, rinv, sigma, s_u, s, c);
+            codes16<7, -8, 7, GS>(v[i], fast, rinv, sigma, s_u, s, c);
             hsum += (int)(c[4] + c[5] + c[6] + c[7] + c[12] + c[13] + c[14] + c[15]);
             *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + act4_offset(m, g * 256 + j * 16, K)) =
                 pack_act16(c);
@@ -365,14 +367,14 @@ static int rot_threads(int G, int* gpl) {
     return round_up(nhw * 32, 64);      // whole waves (half-waves past G idle)
 }
 
-template <int QMAX, int LO, int HI, bool PACKED>
+template <int QMAX, int LO, int HI, bool PACKED, int GS = 256>
 static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, int32_t* ra, hipStream_t st) {
     const int T = K / 16;              // lanes per row
     if (T <= 64) {
         int lg = 4;
         while ((1 << lg) < T) ++lg;
         const int rows = 256 >> lg;
-        k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx, ra);
+        k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx, ra);
         return hipGetLastError();
     }
     int gpl = 1;
@@ -385,40 +387,52 @@ static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float*
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_quant_act(int kind, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
+// W4A4 activations with rotation group GS.
+template <int GS>
+static hipError_t launch_w4_act(const uint16_t* x, int M, int K, int8_t* qx, float* sx, int32_t* ra, bool packed,
+                                hipStream_t st) {
+    const int G = K >> 8;
+    // four rows per block where there are rows enough to fill the chip
+    // with such blocks (at smaller M one row per block keeps more lanes busy)
+    if (packed && G <= 64 && M >= 2048) {
+        int gpl = 1;
+        while ((G + gpl - 1) / gpl > 16) gpl <<= 1;
+        // two 256-blocks per lane from K = 2048 up: half as many waves, so
+        // the whole grid is resident at once instead of a thin last round
+        // (DiT W1: 11.1 -> 9.7 us)
+        if (gpl == 1 && G >= 8) gpl = 2;
+        const int nw = (G + gpl - 1) / gpl;
+        const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
+        switch (gpl) {
+            case 1: k_quant_w4_rows4<1, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+            case 2: k_quant_w4_rows4<2, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+            case 4: k_quant_w4_rows4<4, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    return packed ? launch_rot<7, -8, 7, true, GS>(x, M, K, qx, sx, ra, st)
+                  : launch_rot<7, -8, 7, false, GS>(x, M, K, qx, sx, nullptr, st);
+}
+
+hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
                             float* sx, int32_t* ra, bool packed, hipStream_t st) {
     if (kind == WK_W4) {
         if (packed && ra == nullptr) return hipErrorInvalidValue;
-        const int G = K >> 8;
-        // four rows per block where there are rows enough to fill the chip
-        // with such blocks (at smaller M one row per block keeps more lanes busy)
-        if (packed && G <= 64 && M >= 2048) {
-            int gpl = 1;
-            while ((G + gpl - 1) / gpl > 16) gpl <<= 1;
-            // two groups per lane from K = 2048 up: half as many waves, so the
-            // whole grid is resident at once instead of a thin last round
-            // (DiT W1: 11.1 -> 9.7 us)
-            if (gpl == 1 && G >= 8) gpl = 2;
-            const int nw = (G + gpl - 1) / gpl;
-            const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
-            switch (gpl) {
-                case 1: k_quant_w4_rows4<1><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
-                case 2: k_quant_w4_rows4<2><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
-                case 4: k_quant_w4_rows4<4><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
-                default: return hipErrorInvalidValue;
-            }
-            return hipGetLastError();
+        switch (group) {
+            case 256: return launch_w4_act<256>(x, M, K, qx, sx, ra, packed, st);
+            case 64: return launch_w4_act<64>(x, M, K, qx, sx, ra, packed, st);
+            case 16: return launch_w4_act<16>(x, M, K, qx, sx, ra, packed, st);
+            default: return hipErrorInvalidValue;
         }
-        return packed ? launch_rot<7, -8, 7, true>(x, M, K, qx, sx, ra, st)
-                      : launch_rot<7, -8, 7, false>(x, M, K, qx, sx, nullptr, st);
     }
     // W4A8 and ConvRot INT8: rotated, per-row int8
     if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
@@ -436,13 +450,13 @@ __global__ void k_set_zero(uint32_t* p) { *p = 0u; }
 
 __global__ void k_finalize_scale(float* p, float q) { p[0] = p[0] / q; }
 
-template <int GPL>
+template <int GPL, int GS>
 __global__ void __launch_bounds__(512) k_absmax_rot_rows(const uint16_t* __restrict__ w, int K,
                                                          uint32_t* __restrict__ amax_bits) {
     __shared__ float red[16];
     const int n = blockIdx.x;
     const int hw = threadIdx.x >> 5, nhw = blockDim.x >> 5, lane32 = threadIdx.x & 31;
-    RotRow<GPL> r;
+    RotRow<GPL, GS> r;
     const float a = block_max(r.load_rotate(w + (size_t)n * K, K >> 8, hw, nhw, lane32), red);
     if (threadIdx.x == 0) atomicMax(amax_bits, __float_as_uint(a));
 }
@@ -465,7 +479,7 @@ __device__ __forceinline__ size_t w4_dword_offset(int n, int k0, int K) {
 
 // One block per row (padding rows: zero codes); also cw[n], the sum of the
 // row's codes held in high nibbles (k % 8 < 4).
-template <int GPL>
+template <int GPL, int GS>
 __global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w, int N, int K,
                                                  const float* __restrict__ amax_slot,
                                                  uint8_t* __restrict__ out) {
@@ -484,7 +498,7 @@ __global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w,
     }
     if (threadIdx.x == 0) tot = 0;
     const float s = amax_slot[0] / 7.0f;
-    RotRow<GPL> r;
+    RotRow<GPL, GS> r;
     r.load_rotate(w + (size_t)n * K, G, hw, nhw, lane32);
     int hsum = 0;
 #pragma unroll
@@ -504,8 +518,8 @@ __global__ void __launch_bounds__(512) k_pack_w4(const uint16_t* __restrict__ w,
     if (threadIdx.x == 0) cw[n] = tot;
 }
 
-hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* scale,
-                          hipStream_t st) {
+template <int GS>
+static hipError_t launch_pack_w4_gs(const uint16_t* w, int N, int K, uint8_t* out, float* scale, hipStream_t st) {
     const int Np = round_up(N, 32);
     int gpl = 1;
     const int threads = rot_threads(K >> 8, &gpl);
@@ -514,8 +528,8 @@ hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* 
     switch (gpl) {
 #define CR_PACK_CASE(G_)                                                                 \
     case G_:                                                                             \
-        k_absmax_rot_rows<G_><<<dim3(N), dim3(threads), 0, st>>>(w, K, bits);            \
-        k_pack_w4<G_><<<dim3(Np), dim3(threads), 0, st>>>(w, N, K, scale, out);          \
+        k_absmax_rot_rows<G_, GS><<<dim3(N), dim3(threads), 0, st>>>(w, K, bits);        \
+        k_pack_w4<G_, GS><<<dim3(Np), dim3(threads), 0, st>>>(w, N, K, scale, out);      \
         break;
         CR_PACK_CASE(1) CR_PACK_CASE(2) CR_PACK_CASE(4) CR_PACK_CASE(8) CR_PACK_CASE(16)
 #undef CR_PACK_CASE
@@ -523,6 +537,16 @@ hipError_t launch_pack_w4(const uint16_t* w, int N, int K, uint8_t* out, float* 
     }
     k_finalize_scale<<<1, 1, 0, st>>>(scale, 7.0f);
     return hipGetLastError();
+}
+
+hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* out, float* scale,
+                          hipStream_t st) {
+    switch (group) {
+        case 256: return launch_pack_w4_gs<256>(w, N, K, out, scale, st);
+        case 64: return launch_pack_w4_gs<64>(w, N, K, out, scale, st);
+        case 16: return launch_pack_w4_gs<16>(w, N, K, out, scale, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // --- int8_tensorwise ------------------------------------------------------
