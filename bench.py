@@ -22,7 +22,8 @@ calls and timing it with HIP events on the launch stream:
     more than twice the 256 MB last-level cache) and M=1220, the
     int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer, and the
     ConvRot INT8 row-scaled format on a square text-encoder projection
-    (K=N=2560) at M=76 and M=1220.
+    (K=N=2560) at M=76 and M=1220, and the DiT W1 layer with W4A4 rotation
+    groups of 64 and 16.
 The CPU oracle (NumPy) is timed on a row sample of the headline layer.
 
 Prints one JSON line.
@@ -68,6 +69,8 @@ def row_specs():
     return {
         "dit_w1": dict(kind=0, gen=lambda: si.dit_w1(), cold=False),
         "dit_w2": dict(kind=0, gen=lambda: si.dit_w2(), cold=False),
+        "dit_w1_group64": dict(kind=4, gen=lambda: si.dit_w1(), cold=False),
+        "dit_w1_group16": dict(kind=5, gen=lambda: si.dit_w1(), cold=False),
         "te_gate_up_M76": dict(kind=0, gen=lambda: si.te_gate_up(76), cold=True),
         "te_down_M76": dict(kind=0, gen=lambda: si.te_down(76), cold=True),
         "te_gate_up_M1220": dict(kind=0, gen=lambda: si.te_gate_up(1220), cold=False),
@@ -99,13 +102,18 @@ class Layer:
             s = torch.from_numpy(s_ch).to(dev)
         else:
             w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
-            p, s = {0: crp.pack_weight_w4, 1: crp.pack_weight_int8tw, 3: crp.pack_weight_int8rot}[kind](w)
+            p, s = {0: crp.pack_weight_w4, 1: crp.pack_weight_int8tw, 3: crp.pack_weight_int8rot,
+                    4: lambda t: crp.pack_weight_w4(t, group=64),
+                    5: lambda t: crp.pack_weight_w4(t, group=16)}[kind](w)
             del w
         self.packed = [p] + [p.clone() for _ in range(copies - 1)]
         self.scale = s
         self.y = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
         self.ws = torch.empty(crp.workspace_bytes(kind, L.M, L.N, L.K), dtype=torch.uint8, device=dev)
-        self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8, 3: crp.linear_int8rot}[kind]
+        self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8, 3: crp.linear_int8rot,
+                   4: lambda *a: crp.linear_w4a4(*a, group=64),
+                   5: lambda *a: crp.linear_w4a4(*a, group=16)}[kind]
+        self.w4 = kind in (0, 4, 5)
 
     def linear(self, i=0):
         return self.fn(self.x, self.packed[i], self.scale, self.N, self.bias, self.y, self.ws)
@@ -122,7 +130,7 @@ class Layer:
         return 2.0 * self.M * self.N * self.K
 
     def weight_bytes(self):
-        if self.kind == 0:
+        if self.w4:
             return self.N * self.K / 2
         if self.kind == 1:
             return self.N * self.K
@@ -131,13 +139,13 @@ class Layer:
         return self.N * self.K / 2 + self.N * self.K / 16 + 4 * self.N
 
     def gemm_bytes(self):
-        qx = self.M * self.K / 2 if self.kind == 0 else self.M * self.K    # activation codes
+        qx = self.M * self.K / 2 if self.w4 else self.M * self.K    # activation codes
         y = self.M * self.N * 2
         b = self.N * 2 if self.bias is not None else 0
         return qx + self.weight_bytes() + y + b + 4 * self.M
 
     def quant_bytes(self):
-        if self.kind == 0:      # 4-bit codes, scale and correction sum per row
+        if self.w4:             # 4-bit codes, scale and correction sum per row
             return self.M * self.K * 2 + self.M * self.K / 2 + 8 * self.M
         return self.M * self.K * 2 + self.M * self.K + 4 * self.M
 

@@ -68,6 +68,13 @@ R12 ConvRot INT8 row-scaled ([Q3N] file table: INT8 with group-256 Hadamard
     clip(rint(W~ / s_w[n]), -128, 127); the activations are rotated online
     and quantised per row as in R8; one int32 accumulation over the full K;
     the epilogue takes s_w[n] per output column (as s_channel in R8).
+R13 Smaller rotation groups ([ZIT] "Where Z-Image sits": the sweep over
+    group sizes 256, 64 and 16): the same butterflies as R2 over groups of
+    G = 64 or 16 consecutive k (strides 1 .. G/2 ascending), i.e. a
+    block-diagonal rotation, then one multiply by 1/sqrt(G) (0.125 or
+    0.25, exact); everything after the rotation is R3-R6 unchanged.  K
+    stays a multiple of 256 (the layer eligibility rule of [REB] "Mixed
+    formats" is kept whatever the group).
 
 Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
 codebooks are correct and the GPU consumes whatever codebook it is given; its
