@@ -15,17 +15,24 @@ namespace cr {
 //
 // Operand roles: weights are the A operand (16 rows = n), activations the B
 // operand (16 columns = m).  Lane l supplies row/column l % 16 and 16 k
-// values of the 64-k chunk, k = kb(l / 16) + 0..15 with kb(g) =
-// 32 (g & 1) + 16 (g >> 1); both operands use the same k order, which is all
-// the dot product needs.  The result leaves lane l with column m = l % 16 and
-// rows n = 4 (l / 16) + r in register r.  In the packed 4-bit layouts the
-// 8 bytes a lane needs are contiguous (row r at r * 32, kb(g) at byte 8 g);
-// in the int8 layouts the 16 bytes are (weights) at 16 g of the row's 64 or
-// (activations [M, Kp]) at kb(g).
+// values; both operands use the same k order, which is all the dot product
+// needs.  The result leaves lane l with column m = l % 16 and rows
+// n = 4 (l / 16) + r in register r.
+//
+// int8 layouts: a step is one 64-k chunk, lane group g = l / 16 takes
+// k = kb(g) + 0..15 with kb(g) = 32 (g & 1) + 16 (g >> 1): 16 bytes at 16 g
+// of the weight row's 64, and at kb(g) of the activation row [M, Kp].
+// Packed 4-bit layouts (W4A4 and the W4A8 indices): in a chunk row r holds
+// 32 bytes at r * 32, k = 32 t + 16 h + 0..15 in the 8 bytes at 16 h + 8 t.
+// W4A4 steps over two chunks c, c + 1 with 16-byte loads: lane group g reads
+// the 16 bytes at 16 (g & 1) of chunk c + (g >> 1), and MFMA t of the step
+// takes their t-th 8 bytes, i.e. k = 64 (c + (g >> 1)) + 32 t + 16 (g & 1)
+// + 0..15 on both operands (the two MFMAs cover the 128 k once).  W4A8 steps
+// over one chunk, lane group g reading the 8 bytes at 8 g (k = kb(g) + ..).
 //
 // Block = 8 waves over NT 16-row weight tiles and a range of 64-k chunks
 // (the whole K, or one of `splits` slices); wave w takes a contiguous run of
-// the range's chunks (run lengths differ by at most one), issues every load
+// the range's steps (run lengths differ by at most one), issues every load
 // of its run up front, then runs NT x MT MFMAs per chunk.  The eight waves'
 // int32 sums meet in LDS and each wave adds up and finishes a share of the
 // NT x MT output tiles: epilogue when the block covers all of K, else an
@@ -36,12 +43,14 @@ constexpr int SM_W = 8;   // waves per block
 
 // Loads of one chunk: NT weight fragments + MT activation fragments.
 template <int WK> struct SmW;
-template <> struct SmW<WK_W4> { v2i a; };
+template <> struct SmW<WK_W4> { v4i a; };
 template <> struct SmW<WK_I8> { v4i a; };
 template <> struct SmW<WK_I8R> { v4i a; };
 template <> struct SmW<WK_W4A8> { v2i a; int c; };
-template <int WK> struct SmA { v4i a; };             // int8 activations
-template <> struct SmA<WK_W4> { v2i a; };            // packed 4-bit activations
+template <int WK> struct SmA { v4i a; };             // int8 activations; W4A4: two 8-byte pieces
+
+// 64-k chunks per step of a wave's run.
+__host__ __device__ constexpr int small_ck(int wk) { return wk == WK_W4 ? 2 : 1; }
 
 template <int WK, int MT, int NT, int CPW>
 __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int cps, int acc_mode) {
@@ -57,8 +66,9 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     const int nt16 = (p.N + 15) >> 4;
     const int s = blockIdx.y;
     const int kc0 = s * cps;
-    const int kcs = min(nkc - kc0, cps);                              // chunks of this block (>= 1)
-    // this wave's run: [kc0 + b0, kc0 + b0 + len)
+    constexpr int CK = small_ck(WK);
+    const int kcs = min(nkc - kc0, cps) / CK;                         // steps of this block (>= 1)
+    // this wave's run: steps [b0, b0 + len) from chunk kc0
     const int base = kcs / SM_W, extra = kcs % SM_W;
     const int len = base + (wave < extra ? 1 : 0);
     const int b0 = wave * base + min(wave, extra);
@@ -97,7 +107,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     for (int t = 0; t < NT; ++t) {
         const int nt = min((int)blockIdx.x * NT + t, nt16 - 1);
         wvo[t] = (uint32_t)((nt >> 1) - band0) * band_bytes + (uint32_t)(((nt & 1) * 16 + r16) * RB) +
-                 (uint32_t)(wk_i8w(WK) ? 16 * g : 8 * g);
+                 (uint32_t)(wk_i8w(WK) ? 16 * g : (WK == WK_W4 ? 16 * (g & 1) + (g >> 1) * WT : 8 * g));
     }
     __amdgpu_buffer_rsrc_t rs_c = rs_w;                                 // replaced below for W4A8
     uint32_t cvo[NT];
@@ -118,7 +128,8 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
         const int m = j * 16 + r16;
-        if constexpr (WK == WK_W4) avo[j] = (uint32_t)((m >> 5) * nkc) * 1024u + (uint32_t)((m & 31) * 32 + 8 * g);
+        if constexpr (WK == WK_W4)
+            avo[j] = (uint32_t)((m >> 5) * nkc) * 1024u + (uint32_t)((m & 31) * 32 + 16 * (g & 1) + (g >> 1) * 1024);
         else avo[j] = (uint32_t)min(m, p.M - 1) * (uint32_t)p.Kp + (uint32_t)kb;
     }
 
@@ -128,10 +139,10 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
     SmA<WK> ar[CPW][MT];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-        const int kc = kc0 + min(b0 + i, kcs - 1);                      // wave-uniform
+        const int kc = kc0 + CK * min(b0 + i, kcs - 1);                 // wave-uniform
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if constexpr (wk_i8w(WK)) {
+            if constexpr (wk_i8w(WK) || WK == WK_W4) {
                 wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b128(rs_w, wvo[t], kc * WT, 0);
             } else {
                 wr[i][t].a = __builtin_amdgcn_raw_buffer_load_b64(rs_w, wvo[t], kc * WT, 0);
@@ -140,8 +151,7 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
         }
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
-            if constexpr (WK == WK_W4) ar[i][j].a = __builtin_amdgcn_raw_buffer_load_b64(rs_a, avo[j], kc * AT, 0);
-            else ar[i][j].a = __builtin_amdgcn_raw_buffer_load_b128(rs_a, avo[j], kc * AT, 0);
+            ar[i][j].a = __builtin_amdgcn_raw_buffer_load_b128(rs_a, avo[j], kc * AT, 0);
         }
     }
     // keep every load above this point: all of the run is in flight before
@@ -164,30 +174,42 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const bool valid = i < len;
-        v4i b[MT];
+        if constexpr (WK == WK_W4) {
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            if constexpr (WK == WK_W4) {
-                b[j] = unpack_act4((uint32_t)ar[i][j].a.x, (uint32_t)ar[i][j].a.y);
-            } else {
-                b[j] = ar[i][j].a;
+            for (int h = 0; h < 2; ++h) {                                  // the step's two MFMAs
+                v4i b[MT];
+#pragma unroll
+                for (int j = 0; j < MT; ++j)
+                    b[j] = h == 0 ? unpack_act4((uint32_t)ar[i][j].a.x, (uint32_t)ar[i][j].a.y)
+                                  : unpack_act4((uint32_t)ar[i][j].a.z, (uint32_t)ar[i][j].a.w);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    v4i a = h == 0 ? unpack_wt4((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y)
+                                   : unpack_wt4((uint32_t)wr[i][t].a.z, (uint32_t)wr[i][t].a.w);
+                    if (!valid) a = v4i{0, 0, 0, 0};
+#pragma unroll
+                    for (int j = 0; j < MT; ++j)
+                        acc[t][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[t][j], 0, 0, 0);
+                }
             }
-        }
+        } else {
+            v4i b[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            v4i a;
-            if constexpr (WK == WK_W4) {
-                a = unpack_wt4((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y);
-            } else if constexpr (wk_i8w(WK)) {
-                a = wr[i][t].a;
-            } else {
-                const uint32_t code = ((uint32_t)wr[i][t].c >> (8 * (2 * (g & 1) + (g >> 1)))) & 0xFFu;
-                a = decode_w4a8((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y, stab[code]);
+            for (int j = 0; j < MT; ++j) b[j] = ar[i][j].a;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                v4i a;
+                if constexpr (wk_i8w(WK)) {
+                    a = wr[i][t].a;
+                } else {
+                    const uint32_t code = ((uint32_t)wr[i][t].c >> (8 * (2 * (g & 1) + (g >> 1)))) & 0xFFu;
+                    a = decode_w4a8((uint32_t)wr[i][t].a.x, (uint32_t)wr[i][t].a.y, stab[code]);
+                }
+                if (!valid) a = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < MT; ++j)
+                    acc[t][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[t][j], 0, 0, 0);
             }
-            if (!valid) a = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < MT; ++j)
-                acc[t][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[t][j], 0, 0, 0);
         }
     }
 
@@ -286,9 +308,9 @@ __host__ __device__ constexpr int small_nt(int mt) { return mt <= 5 ? 3 : 2; }
 constexpr int SM_CPW_MAX = 8;
 constexpr int SM_MAX_SPLITS = 16;
 
-// VGPRs of one chunk's loads; a wave holds at most 128 of them.
+// VGPRs of one step's loads; a wave holds at most 128 of them.
 __host__ __device__ constexpr int small_regs_per_chunk(int wk, int mt, int nt) {
-    return nt * (wk == WK_W4 ? 2 : (wk_i8w(wk) ? 4 : 3)) + mt * (wk == WK_W4 ? 2 : 4);
+    return nt * (wk == WK_W4A8 ? 3 : 4) + mt * 4;
 }
 constexpr int SM_LOAD_REGS = 128;
 
@@ -297,7 +319,9 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
     sp.use = M > 0 && M <= kSmallMaxM;
     if (!sp.use) return sp;
     const int Kp = wk_i8w(kind) ? round_up(K, 64) : K;
+    const int ck = small_ck(kind);
     const int nkc = Kp / 64;
+    const int nsteps = nkc / ck;                 // W4A4: K % 256 == 0, so nkc is even
     const int nt16 = (N + 15) / 16;
     sp.mt = (M + 15) / 16;
     sp.nt = small_nt(sp.mt);
@@ -306,11 +330,12 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
     const double wbytes = kind == WK_W4 ? 0.5 : (wk_i8w(kind) ? 1.0 : 0.5625);
     const double abytes = kind == WK_W4 ? 0.5 : 1.0;
     double best = 1e30;
-    for (int S = 1; S <= nkc && S <= SM_MAX_SPLITS; ++S) {
-        const int cps = (nkc + S - 1) / S;
-        const int splits = (nkc + cps - 1) / cps;
+    for (int S = 1; S <= nsteps && S <= SM_MAX_SPLITS; ++S) {
+        const int sps = (nsteps + S - 1) / S;    // steps per slice
+        const int splits = (nsteps + sps - 1) / sps;
         if (splits != S) continue;
-        const int cpw = (cps + SM_W - 1) / SM_W;
+        const int cps = sps * ck;
+        const int cpw = (sps + SM_W - 1) / SM_W;
         if (cpw > SM_CPW_MAX || cpw * per_chunk > SM_LOAD_REGS) continue;
         // rough cycle model: per block max(L2->CU bytes at 64 B/clk, MFMA
         // issue of 2 waves per SIMD) + latency, rounds of 256 blocks, and
@@ -318,7 +343,7 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
         const double blocks = (double)nblk * splits;
         const double rounds = std::ceil(blocks / 256.0);
         const double bytes = (double)cps * 64.0 * (sp.nt * 16 * wbytes + sp.mt * 16 * abytes);
-        const double mfma = 2.0 * cpw * sp.nt * sp.mt * 16.0;
+        const double mfma = 2.0 * cpw * ck * sp.nt * sp.mt * 16.0;
         double cost = rounds * (std::max(bytes / 64.0, mfma) + 2000.0);
         if (splits > 1) cost += (double)splits * sp.mt * 16 * N * 8 / 4000.0 + 3000.0;
         if (cost < best) {

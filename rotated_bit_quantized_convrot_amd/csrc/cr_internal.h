@@ -112,7 +112,7 @@ struct SmallPlan {
     int nblk;      // weight blocks
     int splits;    // K slices across blocks
     int cps;       // 64-k chunks per slice
-    int cpw;       // chunks per wave (at most)
+    int cpw;       // steps per wave (at most; a step is two 64-k chunks for W4A4, one otherwise)
     size_t part_bytes;   // int32 partial tiles, [splits][N/16][mt][64 lanes] x int4
     size_t lds;          // dynamic LDS bytes of the GEMM kernel
 };
