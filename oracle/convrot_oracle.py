@@ -75,6 +75,16 @@ R13 Smaller rotation groups ([ZIT] "Where Z-Image sits": the sweep over
     0.25, exact); everything after the rotation is R3-R6 unchanged.  K
     stays a multiple of 256 (the layer eligibility rule of [REB] "Mixed
     formats" is kept whatever the group).
+R14 Regular Hadamard ([QIE] intro: "regular-Hadamard" rotation, no
+    construction given): the group-256 matrix (J - 2I)^(x4) / 16, the fourth
+    Kronecker power of the 4x4 regular Hadamard matrix J - 2I (every row of
+    which sums to 2, so every row of the normalised H sums to 1).  Applied
+    by four radix-4 stages (digit strides 1, 4, 16, 64 ascending); a stage
+    maps the group x0..x3 to t - 2 x_k, t = (x0 + x1) + (x2 + x3), in
+    float32; then one multiply by 0.0625.  Everything after the rotation is
+    R3-R6 unchanged.  An alternative to R1, not the default.  (The other
+    4x4 regular Hadamard matrix, 2I - J = -(J - 2I), gives the same
+    256-matrix: the four sign flips cancel.)
 
 Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
 codebooks are correct and the GPU consumes whatever codebook it is given; its
@@ -162,6 +172,44 @@ def fwht(v: np.ndarray, group: int = GROUP, dtype=np.float32) -> np.ndarray:
     return y.reshape(*lead, K).astype(dtype)
 
 
+def regular_hadamard() -> np.ndarray:
+    """Closed form of the normalised group-256 regular Hadamard matrix of
+    reading R14 (float64): with A = J - 2I the 4x4 matrix of ones less twice
+    the identity (every row sums to 2), H[i, j] = prod_d A[i_d, j_d] / 16 over
+    the four base-4 digits of i and j.  Every row of H sums to 1."""
+    A = np.ones((4, 4)) - 2.0 * np.eye(4)
+    H = A
+    for _ in range(3):
+        H = np.kron(H, A)
+    return H / 16.0
+
+
+def rht(v: np.ndarray, dtype=np.float32) -> np.ndarray:
+    """Group-256 rotation by the regular Hadamard matrix along the last axis.
+
+    Reading R14: four radix-4 stages over the base-4 digits of the index
+    (strides 1, 4, 16, 64 in that order); a stage replaces the four values
+    x0..x3 of a group (index order) by t - 2 x_k with t = (x0 + x1) + (x2 + x3),
+    computed in ``dtype``; then one multiply by 1/16 (exact)."""
+    v = np.asarray(v)
+    K = v.shape[-1]
+    if K % GROUP != 0:
+        raise ValueError(f"K={K} is not a multiple of the rotation group {GROUP}")
+    lead = v.shape[:-1]
+    y = np.array(v, dtype=dtype).reshape(-1, K // GROUP, GROUP)
+    R, G = y.shape[0], y.shape[1]
+    s = 1
+    while s < GROUP:
+        y = y.reshape(R, G, GROUP // (4 * s), 4, s)
+        x = [y[:, :, :, k, :].copy() for k in range(4)]
+        t = (x[0] + x[1]) + (x[2] + x[3])
+        for k in range(4):
+            y[:, :, :, k, :] = t - dtype(2) * x[k]
+        s *= 4
+    y = y.reshape(R, G, GROUP) * dtype(0.0625)
+    return y.reshape(*lead, K).astype(dtype)
+
+
 # ---------------------------------------------------------------------------
 # Symmetric quantisation  [QIE intro: activations "dynamically quantized to
 # INT4"; weights packed signed INT4, tensorwise]
@@ -216,6 +264,16 @@ def quant_weight_w4(w_bits: np.ndarray, group: int = GROUP):
 
 
 # --- int8_tensorwise -------------------------------------------------------
+
+def quant_act_w4a4_regular(x_bits: np.ndarray):
+    """W4A4 activations rotated by the regular Hadamard matrix (R14)."""
+    return quant_rows(rht(bf16_to_f32(x_bits)), 7, -8, 7)
+
+
+def quant_weight_w4_regular(w_bits: np.ndarray):
+    """W4 weight rotated by the regular Hadamard matrix (R14), tensorwise."""
+    return quant_tensor(rht(bf16_to_f32(w_bits)), 7, -8, 7)
+
 
 def quant_act_int8(x_bits: np.ndarray):
     """int8_tensorwise activations: no rotation, per row absmax/127."""
@@ -340,6 +398,15 @@ def linear_w4a4(x_bits, w_bits, bias_bits=None, group: int = GROUP):
     Returns dict with codes, scales, acc and the float32 output."""
     qx, sx = quant_act_w4a4(x_bits, group)
     qw, sw = quant_weight_w4(w_bits, group)
+    acc = int_gemm(qx, qw)
+    return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
+
+
+def linear_w4a4_regular(x_bits, w_bits, bias_bits=None):
+    """W4A4 linear with the regular Hadamard rotation (R14): R3-R6 after the
+    rotation, as in linear_w4a4."""
+    qx, sx = quant_act_w4a4_regular(x_bits)
+    qw, sw = quant_weight_w4_regular(w_bits)
     acc = int_gemm(qx, qw)
     return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
 

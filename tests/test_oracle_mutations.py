@@ -107,6 +107,22 @@ def _fwht_norm_of_256(v, group=256, dtype=np.float32):
     return (_fwht_generic(v, group, dtype, scale=False) * dtype(1.0 / 16.0)).astype(dtype)
 
 
+def _rht_generic(v, dtype=np.float32, order="asc", seq_sum=False, half_weight=False):
+    v = np.asarray(v)
+    K = v.shape[-1]
+    lead = v.shape[:-1]
+    y = np.array(v, dtype=dtype).reshape(-1, K // 256, 256)
+    R, G = y.shape[0], y.shape[1]
+    strides = [1, 4, 16, 64] if order == "asc" else [64, 16, 4, 1]
+    for s in strides:
+        y = y.reshape(R, G, 256 // (4 * s), 4, s)
+        x = [y[:, :, :, k, :].copy() for k in range(4)]
+        t = (((x[0] + x[1]) + x[2]) + x[3]) if seq_sum else ((x[0] + x[1]) + (x[2] + x[3]))
+        for k in range(4):
+            y[:, :, :, k, :] = (t - x[k]) if half_weight else (t - dtype(2) * x[k])
+    return (y.reshape(R, G, 256) * dtype(0.0625)).reshape(*lead, K).astype(dtype)
+
+
 MUTATIONS = {
     "fwht_descending_order": ("fwht", lambda v, group=256, dtype=np.float32:
                               _fwht_generic(v, group, dtype, order="desc")),
@@ -126,6 +142,9 @@ MUTATIONS = {
     "int8rot_weight_unrotated": ("quant_weight_int8rot", _int8rot_weight_unrotated),
     "fwht_group_ignored": ("fwht", _fwht_group_ignored),
     "fwht_group_norm_of_256": ("fwht", _fwht_norm_of_256),
+    "rht_descending_stages": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, order="desc")),
+    "rht_left_to_right_sum": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, seq_sum=True)),
+    "rht_diagonal_weight_1": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, half_weight=True)),
 }
 
 PINS = [
@@ -153,6 +172,12 @@ PINS = [
     lambda: P.test_group_one_hot_row_codes(64),
     lambda: P.test_group_constant_row_codes(16, 0.5),
     lambda: P.test_group_weight_one_hot_codes(16),
+    P.test_rht_unit_vectors_give_rows,
+    P.test_rht_float64_equals_dense_product,
+    P.test_rht_pairwise_sum_fixture,
+    P.test_rht_stage_order_fixture,
+    lambda: P.test_rht_constant_row_stays_constant(0.5),
+    P.test_rht_one_hot_row_codes,
 ]
 
 

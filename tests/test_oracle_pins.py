@@ -533,3 +533,140 @@ def test_group_weight_one_hot_codes(G):
         assert q[n, g0 + k] == -7 * sign
     assert np.all(q[n, :g0] == 0) and np.all(q[n, g0 + G:] == 0)
     assert s == F32(F32(5.0 / np.sqrt(G)) / F32(7))
+
+
+# ---------------------------------------------------------------------------
+# Regular Hadamard rotation (R14; [QIE] intro "regular-Hadamard")
+# ---------------------------------------------------------------------------
+
+def _regular_entry(i, j):
+    """prod over the four base-4 digits of (1 - 2 [i_d == j_d]), written out
+    digit by digit (the entries of (J - 2I) x (J - 2I) x ...)."""
+    e = 1
+    for _ in range(4):
+        e *= -1 if (i % 4) == (j % 4) else 1
+        i //= 4
+        j //= 4
+    return e
+
+
+def _sigma(d):
+    # sign a one-hot group picks up in a radix-4 stage: position 0 of the
+    # group gets t - 2 x0 = -x0, the others t = x0
+    return -1.0 if d == 0 else 1.0
+
+
+def test_regular_hadamard_closed_form_orthonormal_regular():
+    H = O.regular_hadamard()
+    want = np.array([[_regular_entry(i, j) / 16.0 for j in range(256)] for i in range(256)])
+    assert np.array_equal(H, want)
+    assert np.array_equal(H @ H.T, np.eye(256))
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H.sum(axis=1), np.ones(256))      # every row sums to 1 (regular)
+
+
+def test_rht_unit_vectors_give_rows():
+    got = O.rht(np.eye(256, dtype=F32)).astype(np.float64)
+    want = np.array([[_regular_entry(i, j) / 16.0 for j in range(256)] for i in range(256)])
+    assert np.array_equal(got, want)
+
+
+def test_rht_float64_equals_dense_product():
+    rng = np.random.default_rng(14)
+    x = rng.normal(size=(4, 768))
+    got = O.rht(x, dtype=np.float64)
+    H = np.array([[_regular_entry(i, j) / 16.0 for j in range(256)] for i in range(256)])
+    want = (x.reshape(4, 3, 256) @ H).reshape(4, 768)
+    assert np.max(np.abs(got - want)) <= 1e-14 * np.max(np.abs(want))
+
+
+def test_rht_float32_within_error_bound():
+    """Error of the float32 stages against the exact product, u = 2^-24.  An
+    output of a stage, t - 2 x_k with t = (x0 + x1) + (x2 + x3), takes four
+    roundings (the two pair sums, t, the output), together below u times
+    |x0 + x1| + |x2 + x3| + |t| + |t - 2 x_k| <= 5 ||x_4||_1 <= 10 ||x_4||_2
+    over its 4-group (first order in u), so one stage adds an error of L2
+    norm <= 20 u ||x||_2 over the 256-group; the exact stage (J - 2I per
+    digit, (J - 2I)^T (J - 2I) = 4 I) doubles L2 norms, so four stages give
+    <= 20 u (8 + 8 + 8 + 8) ||x||_2 = 640 u ||x||_2, i.e. 40 u ||x_g||_2
+    after the 1/16: a bound on every element's error."""
+    rng = np.random.default_rng(15)
+    x32 = rng.standard_t(3, size=(8, 512)).astype(F32)
+    got = O.rht(x32).astype(np.float64)
+    H = np.array([[_regular_entry(i, j) / 16.0 for j in range(256)] for i in range(256)])
+    want = (x32.astype(np.float64).reshape(8, 2, 256) @ H).reshape(8, 512)
+    l2 = np.sqrt((x32.astype(np.float64).reshape(8, 2, 256) ** 2).sum(-1))
+    err = np.abs(got - want).reshape(8, 2, 256)
+    assert np.all(err <= (40 * 2.0 ** -24 * l2)[:, :, None])
+    assert np.max(err) > 0                                   # float32 arithmetic really ran
+
+
+def test_rht_pairwise_sum_fixture():
+    """x0 = 1, x2 = x3 = e = 2^-24 (bf16 values): the first stage's sum is
+    (1 + 0) + (e + e) = 1 + 2^-23 exactly (a left-to-right sum would round
+    1 + e to 1 twice), so that group becomes (t - 2, t, t - 2e, t) =
+    (-1 + 2^-23, 1 + 2^-23, 1, 1); the later stages see one non-zero value
+    per group and only apply the signs sigma(d)."""
+    e = 2.0 ** -24
+    x = np.zeros(256, F32)
+    x[0], x[2], x[3] = 1.0, e, e
+    w = [-1 + 2.0 ** -23, 1 + 2.0 ** -23, 1.0, 1.0]
+    want = np.array([w[i % 4] * _sigma((i // 4) % 4) * _sigma((i // 16) % 4) * _sigma(i // 64) / 16
+                     for i in range(256)], np.float64).astype(F32)
+    assert np.array_equal(O.rht(x).view(np.uint32), want.view(np.uint32))
+
+
+def test_rht_stage_order_fixture():
+    """x0 = 1, x5 = e = 2^-24 with the stages in ascending stride order.
+    Stride 1: (1,0,0,0) -> (-1,1,1,1) at 0..3 and (0,e,0,0) -> (e,-e,e,e) at
+    4..7.  Stride 4, groups (r, 4+r, 8+r, 12+r) holding (P0[r], P1[r], 0, 0),
+    t = P0[r] + P1[r]:
+      r=0: t = -1 + e (exact) -> (t+2, t-2e, t, t) = (1, -1, -1+e, -1+e)
+           (1 + e and -1 - e are ties that round to the even 1 and -1);
+      r=1: t = 1 - e -> (t-2, t+2e, t, t) = (-1, 1, 1-e, 1-e);
+      r=2, 3: t = 1 + e rounds to 1 -> (-1, 1 - 2e, 1, 1).
+    Strides 16 and 64 then apply sigma(d2) sigma(d3).  Descending strides
+    would meet 1 and e only in the last stage and give -(1 - e) at 2, 3."""
+    e = 2.0 ** -24
+    x = np.zeros(256, F32)
+    x[0], x[5] = 1.0, e
+    u = np.zeros(16)
+    u[[0, 4, 8, 12]] = [1, -1, -1 + e, -1 + e]
+    u[[1, 5, 9, 13]] = [-1, 1, 1 - e, 1 - e]
+    for r in (2, 3):
+        u[[r, 4 + r, 8 + r, 12 + r]] = [-1, 1 - 2 * e, 1, 1]
+    want = np.array([u[i % 16] * _sigma((i // 16) % 4) * _sigma(i // 64) / 16 for i in range(256)],
+                    np.float64).astype(F32)
+    assert np.array_equal(O.rht(x).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("c", [0.5, -3.0])
+def test_rht_constant_row_stays_constant(c):
+    """Every row of the regular matrix sums to 1, so a constant row rotates to
+    itself (each stage maps (c,c,c,c) to (2c,...): 16c, then x 1/16): codes
+    +-7 everywhere, scale fl(|c| / 7) - unlike the Sylvester rotation, which
+    moves it all to the first k of each group."""
+    K = 512
+    x = np.full((1, K), c, F32)
+    q, s = O.quant_act_w4a4_regular(si.f32_to_bf16_bits(x))
+    assert np.all(q[0] == (7 if c > 0 else -7))
+    assert s[0] == F32(F32(abs(c)) / F32(7))
+
+
+def test_rht_one_hot_row_codes():
+    j, g = 201, 1
+    x = np.zeros((1, 512), F32)
+    x[0, 256 * g + j] = -2.0
+    q, s = O.quant_act_w4a4_regular(si.f32_to_bf16_bits(x))
+    want = np.array([-7 * _regular_entry(j, k) for k in range(256)], np.int8)
+    assert np.array_equal(q[0, 256 * g:], want) and np.all(q[0, :256] == 0)
+    assert s[0] == F32(F32(2.0 / 16) / F32(7))
+
+
+def test_rht_exact_identity_before_quantisation():
+    L = si.tiny()
+    x = O.bf16_to_f32(L.x).astype(np.float64)
+    w = O.bf16_to_f32(L.w).astype(np.float64)
+    lhs = O.rht(x, dtype=np.float64) @ O.rht(w, dtype=np.float64).T
+    rhs = x @ w.T
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
