@@ -23,7 +23,7 @@ calls and timing it with HIP events on the launch stream:
     int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer, and the
     ConvRot INT8 row-scaled format on a square text-encoder projection
     (K=N=2560) at M=76 and M=1220, and the DiT W1 layer with W4A4 rotation
-    groups of 64 and 16.
+    groups of 64 and 16 and with the group-256 regular Hadamard.
 The CPU oracle (NumPy) is timed on a row sample of the headline layer.
 
 Prints one JSON line.
@@ -71,6 +71,7 @@ def row_specs():
         "dit_w2": dict(kind=0, gen=lambda: si.dit_w2(), cold=False),
         "dit_w1_group64": dict(kind=4, gen=lambda: si.dit_w1(), cold=False),
         "dit_w1_group16": dict(kind=5, gen=lambda: si.dit_w1(), cold=False),
+        "dit_w1_regular": dict(kind=6, gen=lambda: si.dit_w1(), cold=False),
         "te_gate_up_M76": dict(kind=0, gen=lambda: si.te_gate_up(76), cold=True),
         "te_down_M76": dict(kind=0, gen=lambda: si.te_down(76), cold=True),
         "te_gate_up_M1220": dict(kind=0, gen=lambda: si.te_gate_up(1220), cold=False),
@@ -104,7 +105,7 @@ class Layer:
             w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
             p, s = {0: crp.pack_weight_w4, 1: crp.pack_weight_int8tw, 3: crp.pack_weight_int8rot,
                     4: lambda t: crp.pack_weight_w4(t, group=64),
-                    5: lambda t: crp.pack_weight_w4(t, group=16)}[kind](w)
+                    5: lambda t: crp.pack_weight_w4(t, group=16), 6: crp.pack_weight_w4_regular}[kind](w)
             del w
         self.packed = [p] + [p.clone() for _ in range(copies - 1)]
         self.scale = s
@@ -112,8 +113,8 @@ class Layer:
         self.ws = torch.empty(crp.workspace_bytes(kind, L.M, L.N, L.K), dtype=torch.uint8, device=dev)
         self.fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8, 3: crp.linear_int8rot,
                    4: lambda *a: crp.linear_w4a4(*a, group=64),
-                   5: lambda *a: crp.linear_w4a4(*a, group=16)}[kind]
-        self.w4 = kind in (0, 4, 5)
+                   5: lambda *a: crp.linear_w4a4(*a, group=16), 6: crp.linear_w4a4_regular}[kind]
+        self.w4 = kind in (0, 4, 5, 6)
 
     def linear(self, i=0):
         return self.fn(self.x, self.packed[i], self.scale, self.N, self.bias, self.y, self.ws)

@@ -77,6 +77,7 @@ typedef enum {
                         output row), rotated int8 activations */
 #define CR_W4A4_G64 4 /* ConvRot W4A4 with rotation groups of 64 (layout as CR_W4A4) */
 #define CR_W4A4_G16 5 /* ConvRot W4A4 with rotation groups of 16 (layout as CR_W4A4) */
+#define CR_W4A4_RH 6  /* ConvRot W4A4 with the group-256 regular Hadamard (layout as CR_W4A4) */
 
 /* Limits: 1 <= N, K <= CR_MAX_DIM; 0 <= M <= CR_MAX_DIM. */
 #define CR_MAX_DIM (1 << 20)
@@ -133,6 +134,24 @@ cr_status cr_pack_weight_w4_group(const void* w_bf16, int N, int K, int group, v
 cr_status cr_linear_w4a4_group(const void* x_bf16, int M, int K, int group, const void* w_packed,
                                const float* w_scale, int N, const void* bias_bf16, void* y_bf16,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- W4A4 with the regular Hadamard ([QIE] intro: "regular-Hadamard"
+ *      rotation; the construction is this library's reading) -------------
+ * As cr_pack_weight_w4 / cr_linear_w4a4 with each 256-block rotated by
+ * H = (J - 2I)^(x4) / 16 in place of the Sylvester matrix: J - 2I is the 4x4
+ * matrix of ones less twice the identity, the power is the Kronecker power,
+ * H is symmetric and orthonormal and every row sums to 1.  Applied as four
+ * radix-4 stages over the base-4 digits of k (strides 1, 4, 16, 64), each
+ * mapping the group x0..x3 to t - 2 x_k with t = (x0 + x1) + (x2 + x3) in
+ * float32, then x 1/16.  Same packed layout and sizes as CR_W4A4; the
+ * generic calls take the kind CR_W4A4_RH.  A weight must be used with the
+ * rotation it was packed with: nothing in the packed bytes records it. */
+cr_status cr_pack_weight_w4_regular(const void* w_bf16, int N, int K, void* w_packed,
+                                    float* w_scale, hipStream_t stream);
+
+cr_status cr_linear_w4a4_regular(const void* x_bf16, int M, int K, const void* w_packed,
+                                 const float* w_scale, int N, const void* bias_bf16,
+                                 void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- int8_tensorwise ([QIE] intro "stock int8_tensorwise"; [REB] "Mixed
  *      formats": no group constraint) -------------------------------------- */

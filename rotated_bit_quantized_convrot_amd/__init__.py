@@ -25,15 +25,16 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A4", "INT8TW", "W4A8", "INT8ROT", "W4A4_G64", "W4A4_G16", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
+    "W4A4", "INT8TW", "W4A8", "INT8ROT", "W4A4_G64", "W4A4_G16", "W4A4_RH", "ConvRotError", "lib", "packed_bytes", "workspace_bytes",
     "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8", "pack_weight_int8rot",
     "linear_w4a4", "linear_int8tw", "linear_w4a8", "linear_int8rot",
+    "pack_weight_w4_regular", "linear_w4a4_regular",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
 ]
 
-W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16 = 0, 1, 2, 3, 4, 5
+W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
 # W4A4 kind of each rotation group size
 W4_GROUP_KIND = {256: W4A4, 64: W4A4_G64, 16: W4A4_G16}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvrot.so")
@@ -49,6 +50,7 @@ EXPORTS = [
     "cr_dbg_linear_acc", "cr_quantize_activations", "cr_gemm_quantized",
     "cr_pack_weight_int8rot", "cr_linear_int8rot",
     "cr_pack_weight_w4_group", "cr_linear_w4a4_group",
+    "cr_pack_weight_w4_regular", "cr_linear_w4a4_regular",
 ]
 
 
@@ -80,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "cr_linear_int8rot": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_pack_weight_w4_group": (i, [vp, i, i, i, vp, vp, vp]),
         "cr_linear_w4a4_group": (i, [vp, i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_pack_weight_w4_regular": (i, [vp, i, i, vp, vp, vp]),
+        "cr_linear_w4a4_regular": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
@@ -151,6 +155,20 @@ def pack_weight_w4(w: torch.Tensor, group: int = 256):
         _check(lib().cr_pack_weight_w4(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
     else:
         _check(lib().cr_pack_weight_w4_group(_ptr(w), N, K, group, _ptr(out), _ptr(scale), _stream()))
+    return out, scale
+
+
+def pack_weight_w4_regular(w: torch.Tensor):
+    """bf16 [N,K] -> (packed uint8, scale float32[1]) in the W4A4 format with
+    the group-256 regular Hadamard rotation."""
+    _dev(w, "w", torch.bfloat16)
+    N, K = w.shape
+    nb = packed_bytes(W4A4_RH, N, K)
+    if nb == 0:
+        _check(lib().cr_pack_weight_w4_regular(_ptr(w), N, K, None, None, None) or 2)
+    out = _empty_u8(nb, w.device)
+    scale = torch.empty(4, dtype=torch.float32, device=w.device)
+    _check(lib().cr_pack_weight_w4_regular(_ptr(w), N, K, _ptr(out), _ptr(scale), _stream()))
     return out, scale
 
 
@@ -239,6 +257,12 @@ def linear_w4a4(x, packed, scale, N, bias=None, out=None, workspace=None, group:
         return _linear("cr_linear_w4a4", W4A4, x, packed, scale, N, bias, out, workspace)
     return _linear("cr_linear_w4a4_group", W4_GROUP_KIND.get(group, W4A4), x, packed, scale, N, bias, out,
                    workspace, group=group)
+
+
+def linear_w4a4_regular(x, packed, scale, N, bias=None, out=None, workspace=None):
+    """y = W4A4 linear with the group-256 regular Hadamard rotation (weight from
+    pack_weight_w4_regular)."""
+    return _linear("cr_linear_w4a4_regular", W4A4_RH, x, packed, scale, N, bias, out, workspace)
 
 
 def linear_int8tw(x, packed, scale, N, bias=None, out=None, workspace=None):
@@ -337,16 +361,20 @@ class PackedWeight:
 
 
 def pack_linear(w: torch.Tensor, bias: Optional[torch.Tensor] = None, int8: bool = False,
-                group: int = 256) -> PackedWeight:
+                group: int = 256, regular: bool = False) -> PackedWeight:
     """Pack a bf16 [N,K] weight: W4A4 ConvRot when K % 256 == 0 (ConvRot INT8
     row-scaled instead with ``int8=True``, the format [Q3N] gives attention
-    projections; ``group`` picks the W4A4 rotation group: 256, 64 or 16),
+    projections; ``group`` picks the W4A4 rotation group: 256, 64 or 16, and
+    ``regular=True`` the group-256 regular Hadamard),
     otherwise int8_tensorwise ([REB] "Mixed formats where the
     kernel demands it")."""
     N, K = w.shape
     if K % 256 == 0 and int8:
         p, s = pack_weight_int8rot(w)
         return PackedWeight(INT8ROT, N, K, p, s, bias)
+    if K % 256 == 0 and regular:
+        p, s = pack_weight_w4_regular(w)
+        return PackedWeight(W4A4_RH, N, K, p, s, bias)
     if K % 256 == 0:
         p, s = pack_weight_w4(w, group)
         return PackedWeight(W4_GROUP_KIND.get(group, W4A4), N, K, p, s, bias)
@@ -358,5 +386,6 @@ def linear(x: torch.Tensor, pw: PackedWeight, out=None, workspace=None) -> torch
     if pw.kind in (W4A4_G64, W4A4_G16):
         group = 64 if pw.kind == W4A4_G64 else 16
         return linear_w4a4(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace, group=group)
-    fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8, INT8ROT: linear_int8rot}[pw.kind]
+    fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8, INT8ROT: linear_int8rot,
+          W4A4_RH: linear_w4a4_regular}[pw.kind]
     return fn(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace)

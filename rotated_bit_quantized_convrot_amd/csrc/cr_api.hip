@@ -51,12 +51,19 @@ size_t a256(size_t v) { return (v + 255) / 256 * 256; }
 bool rotated(int kind) { return kind != CR_INT8TW; }
 
 cr_status check_kind(int kind) {
-    if (kind < CR_W4A4 || kind > CR_W4A4_G16) return fail(CR_ERR_KIND, "unknown kind %d", kind);
+    if (kind < CR_W4A4 || kind > CR_W4A4_RH) return fail(CR_ERR_KIND, "unknown kind %d", kind);
     return CR_OK;
 }
 
-// Rotation group of a kind (the W4A4 group variants; 256 for the others).
-int group_of(int kind) { return kind == CR_W4A4_G64 ? 64 : (kind == CR_W4A4_G16 ? 16 : 256); }
+// Rotation selector of a kind (the W4A4 variants; 256 for the others).
+int group_of(int kind) {
+    switch (kind) {
+        case CR_W4A4_G64: return 64;
+        case CR_W4A4_G16: return 16;
+        case CR_W4A4_RH: return cr::kRotRegular;
+        default: return 256;
+    }
+}
 
 cr_status check_nk(int kind, int N, int K) {
     if (N < 1 || K < 1 || N > CR_MAX_DIM || K > CR_MAX_DIM)
@@ -74,7 +81,8 @@ size_t packed_bytes(int kind, int N, int K) {
     switch (kind) {
         case CR_W4A4:
         case CR_W4A4_G64:
-        case CR_W4A4_G16: return cr::w4a4_bytes(N, K);
+        case CR_W4A4_G16:
+        case CR_W4A4_RH: return cr::w4a4_bytes(N, K);
         case CR_INT8TW: return cr::i8_bytes(N, K);
         case CR_W4A8: return cr::w4a8_bytes(N, K);
         case CR_INT8ROT: return cr::i8_bytes(N, K);
@@ -88,7 +96,8 @@ int wkind(int kind) {
     switch (kind) {
         case CR_W4A4:
         case CR_W4A4_G64:
-        case CR_W4A4_G16: return cr::WK_W4;
+        case CR_W4A4_G16:
+        case CR_W4A4_RH: return cr::WK_W4;
         case CR_INT8TW: return cr::WK_I8;
         case CR_INT8ROT: return cr::WK_I8R;
         default: return cr::WK_W4A8;
@@ -260,6 +269,22 @@ cr_status cr_linear_w4a4_group(const void* x_bf16, int M, int K, int group, cons
     const cr_status s = w4_group_kind(group, &kind);
     if (s != CR_OK) return s;
     return run_linear(kind, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, ws_bytes,
+                      stream);
+}
+
+cr_status cr_pack_weight_w4_regular(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
+                                    hipStream_t stream) {
+    cr_status s = pack_common_checks(CR_W4A4_RH, w_bf16, N, K, w_packed, w_scale);
+    if (s != CR_OK) return s;
+    return launch_err(cr::launch_pack_w4(static_cast<const uint16_t*>(w_bf16), N, K, cr::kRotRegular,
+                                         static_cast<uint8_t*>(w_packed), w_scale, stream),
+                      "W4 weight packing (regular Hadamard)");
+}
+
+cr_status cr_linear_w4a4_regular(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
+                                 int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    return run_linear(CR_W4A4_RH, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, ws_bytes,
                       stream);
 }
 

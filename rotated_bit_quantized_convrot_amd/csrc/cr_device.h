@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cr_internal.h"
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -71,12 +73,36 @@ __device__ __forceinline__ void fwht_cross(float (&v)[8], int lane32) {
     }
 }
 
-// 1 / sqrt(GS) for the rotation group sizes 16, 64 and 256 (powers of two,
-// so the normalisation is exact outside the subnormal range).
+// Rotation selector GS: the Sylvester Hadamard over groups of 256, 64 or 16,
+// or kRotRegular (cr_internal.h), the group-256 regular Hadamard.
+
+// The rotation's normalisation, 1 / sqrt(group) (a power of two, so exact
+// outside the subnormal range).
 template <int GS>
 __device__ __forceinline__ constexpr float rot_norm() {
-    static_assert(GS == 16 || GS == 64 || GS == 256, "rotation group size");
-    return GS == 256 ? 0.0625f : (GS == 64 ? 0.125f : 0.25f);
+    static_assert(GS == 16 || GS == 64 || GS == 256 || GS == kRotRegular, "rotation selector");
+    return (GS == 256 || GS == kRotRegular) ? 0.0625f : (GS == 64 ? 0.125f : 0.25f);
+}
+
+// One radix-4 stage of the regular rotation on the group a0..a3 (index
+// order): a_k <- t - 2 a_k with t = (a0 + a1) + (a2 + a3).
+__device__ __forceinline__ void rh4(float& a0, float& a1, float& a2, float& a3) {
+    const float t = (a0 + a1) + (a2 + a3);
+    a0 = t - 2.0f * a0;
+    a1 = t - 2.0f * a1;
+    a2 = t - 2.0f * a2;
+    a3 = t - 2.0f * a3;
+}
+
+// The same stage when the group's four values sit in the lanes that differ
+// in lane bits M1 (the low bit of the group index) and M2: the lane pair sum
+// with the M1 partner, then t with the M2 partner's pair sum (each lane
+// forms the same t: addition is commutative).
+template <int M1, int M2>
+__device__ __forceinline__ float rh4_cross(float v) {
+    const float p = v + lane_xor<M1>(v);
+    const float t = p + lane_xor<M2>(p);
+    return t - 2.0f * v;
 }
 
 // Rotation of a 256-block held by the 32 lanes of a half-wave, lane j
@@ -86,6 +112,24 @@ __device__ __forceinline__ constexpr float rot_norm() {
 // the half-wave must be active.
 template <int GS>
 __device__ __forceinline__ void fwht8(float (&v)[8], int lane32) {
+    if constexpr (GS == kRotRegular) {
+        // strides 1 (inside the lane), 4 (this lane's pair (r, r + 4) and the
+        // lane ^ 1 pair (r + 8, r + 12)), 16 (lane bits 1, 2), 64 (bits 3, 4)
+        rh4(v[0], v[1], v[2], v[3]);
+        rh4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = v[r] + v[r + 4];
+            const float t = p + lane_xor<1>(p);
+            v[r] = t - 2.0f * v[r];
+            v[r + 4] = t - 2.0f * v[r + 4];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = rh4_cross<2, 4>(v[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = rh4_cross<8, 16>(v[i]) * 0.0625f;
+        return;
+    }
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -173,6 +217,19 @@ __device__ __forceinline__ void fwht_cross16(float (&v)[16], int lane) {
 
 template <int GS>
 __device__ __forceinline__ void fwht16_signed(float (&v)[16], int lane) {
+    if constexpr (GS == kRotRegular) {
+        // the regular rotation keeps no sign: strides 1 and 4 inside the
+        // lane, 16 across lane bits 0, 1 and 64 across lane bits 2, 3
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rh4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rh4(v[r], v[r + 4], v[r + 8], v[r + 12]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = rh4_cross<1, 2>(v[i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = rh4_cross<4, 8>(v[i]);
+        return;
+    }
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -197,7 +254,8 @@ __device__ __forceinline__ void fwht16_signed(float (&v)[16], int lane) {
 // The sign sigma that fwht16_signed<GS> leaves in a lane.
 template <int GS>
 __device__ __forceinline__ float fwht16_sign(int lane) {
-    return (__builtin_popcount(lane & (GS / 16 - 1)) & 1) ? -1.0f : 1.0f;
+    if constexpr (GS == kRotRegular) return 1.0f;
+    else return (__builtin_popcount(lane & (GS / 16 - 1)) & 1) ? -1.0f : 1.0f;
 }
 
 // Symmetric code of v with scale s (IEEE division, round half to even).

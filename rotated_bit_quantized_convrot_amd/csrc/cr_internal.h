@@ -6,6 +6,11 @@
 
 namespace cr {
 
+// W4A4 rotation selector for the group-256 regular Hadamard (J - 2I)^(x4) / 16,
+// J - 2I the 4x4 matrix of ones less twice the identity; the other values
+// (256, 64, 16) select the Sylvester Hadamard over groups of that size.
+constexpr int kRotRegular = 1;
+
 enum WKind { WK_W4 = 0, WK_I8 = 1, WK_W4A8 = 2, WK_I8R = 3 };
 
 // int8 weights in the int8 tile layout (int8_tensorwise; ConvRot INT8,
@@ -53,12 +58,14 @@ __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_o
 // and scales [M]; with `packed` (W4A4 only) the codes go out 4-bit in the
 // 4-bit tile layout with rows = m (round_up(M, 32) rows, rows >= M left
 // untouched), in the activation nibble forms, and ra [M] (the sums of the
-// codes in high nibbles) beside them.  `group` is the W4A4 rotation group
-// (256, 64 or 16; the other kinds rotate, if at all, in groups of 256).
+// codes in high nibbles) beside them.  `group` is the W4A4 rotation: the
+// Sylvester Hadamard over groups of 256, 64 or 16, or kRotRegular (1) for the
+// group-256 regular Hadamard; the other kinds rotate, if at all, with the
+// group-256 Sylvester matrix.
 hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
                             float* sx, int32_t* ra, bool packed, hipStream_t st);
 
-// W4 weight with rotation group `group` (256, 64 or 16).
+// W4 weight with the rotation `group` (as for launch_quant_act).
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* out, float* scale,
                           hipStream_t st);
 hipError_t launch_pack_i8(const uint16_t* w, int N, int K, uint8_t* out, float* scale,

@@ -136,9 +136,10 @@ __device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
 // lanes, 256 / 2^seg_log2 rows per block; seg_log2 < 0: one row per block
 // (GPL groups per lane, strided by the block's group count).
 //
-// Rotation groups of GS = 256, 64 or 16 (a 256-block is 256 / GS groups).
-// The butterflies run on the unscaled values (sign-tracked, see
-// fwht16_signed); the 1/sqrt(GS) = 2^-e of the rotation is folded into the
+// Rotation GS: Sylvester groups of 256, 64 or 16 (a 256-block is 256 / GS
+// groups), or the group-256 regular Hadamard (GS = kRotRegular).  The
+// butterflies run on the unscaled values (sign-tracked, see fwht16_signed);
+// the normalisation 2^-e of the rotation is folded into the
 // scale.  With amax_u the row's max |value| before the 2^-e, the stored
 // scale is s = fl(fl(amax_u 2^-e) / QMAX), and for 2^-100 <= amax_u <= 2^100
 // the code fl(v 2^-e / s) equals fl(v / s_u), s_u = fl(amax_u / QMAX):
@@ -431,6 +432,7 @@ hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K
             case 256: return launch_w4_act<256>(x, M, K, qx, sx, ra, packed, st);
             case 64: return launch_w4_act<64>(x, M, K, qx, sx, ra, packed, st);
             case 16: return launch_w4_act<16>(x, M, K, qx, sx, ra, packed, st);
+            case kRotRegular: return launch_w4_act<kRotRegular>(x, M, K, qx, sx, ra, packed, st);
             default: return hipErrorInvalidValue;
         }
     }
@@ -545,6 +547,7 @@ hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* o
         case 256: return launch_pack_w4_gs<256>(w, N, K, out, scale, st);
         case 64: return launch_pack_w4_gs<64>(w, N, K, out, scale, st);
         case 16: return launch_pack_w4_gs<16>(w, N, K, out, scale, st);
+        case kRotRegular: return launch_pack_w4_gs<kRotRegular>(w, N, K, out, scale, st);
         default: return hipErrorInvalidValue;
     }
 }

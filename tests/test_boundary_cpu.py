@@ -130,15 +130,16 @@ def test_int8rot_sizes_and_group(L):
     assert L.cr_packed_bytes(3, 100, 512) == 128 * 512
     assert L.cr_packed_bytes(3, 64, 2688) == 0
     assert L.cr_workspace_bytes(3, 1220, 2560, 2560) >= 1220 * 2560 + 1220 * 4
-    assert L.cr_packed_bytes(6, 64, 256) == 0
+    assert L.cr_packed_bytes(7, 64, 256) == 0
     vp = ctypes.c_void_p(16)
     assert L.cr_pack_weight_int8rot(vp, 64, 2688, vp, vp, None) == CR["GROUP"]
     assert L.cr_linear_int8rot(vp, 8, 300, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]
 
 
 def test_w4_group_kinds_sizes_and_errors(L):
-    # W4A4 with rotation groups 64 / 16 (kinds 4 / 5): the CR_W4A4 layout
-    for kind in (4, 5):
+    # W4A4 with rotation groups 64 / 16 (kinds 4 / 5) and the regular
+    # Hadamard (kind 6): the CR_W4A4 layout
+    for kind in (4, 5, 6):
         for N, K in ((2560, 2560), (100, 512), (33, 256)):
             assert L.cr_packed_bytes(kind, N, K) == L.cr_packed_bytes(0, N, K)
             for M in (1, 76, 4096):
@@ -152,3 +153,11 @@ def test_w4_group_kinds_sizes_and_errors(L):
         assert L.cr_pack_weight_w4_group(vp, 64, 300, g, vp, vp, None) == CR["GROUP"]
         assert L.cr_linear_w4a4_group(vp, 8, 300, g, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]
         assert L.cr_pack_weight_w4_group(None, 64, 512, g, vp, vp, None) == CR["NULL"]
+
+
+def test_w4_regular_argument_errors(L):
+    vp = ctypes.c_void_p(16)
+    assert L.cr_pack_weight_w4_regular(vp, 64, 300, vp, vp, None) == CR["GROUP"]
+    assert L.cr_linear_w4a4_regular(vp, 8, 300, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]
+    assert L.cr_pack_weight_w4_regular(None, 64, 512, vp, vp, None) == CR["NULL"]
+    assert L.cr_linear_w4a4_regular(vp, 8, 512, vp, vp, 64, None, vp, vp, 16, None) == CR["WORKSPACE"]
