@@ -75,6 +75,14 @@ R13 Smaller rotation groups ([ZIT] "Where Z-Image sits": the sweep over
     0.25, exact); everything after the rotation is R3-R6 unchanged.  K
     stays a multiple of 256 (the layer eligibility rule of [REB] "Mixed
     formats" is kept whatever the group).
+R15 Text-encoder MLP block ([Q3N] file table and the "qwen3vl_4b" page:
+    the decoder blocks' gate_proj, up_proj and down_proj Linears; the
+    pages do not state the activation): the gated MLP of this model family,
+    h = silu(gate(x)) * up(x), silu(v) = v / (1 + exp(-v)), then
+    y = down(h).  Each Linear is the W4A4 linear of R1-R6 (bf16 out, no
+    bias); h is computed from the bf16 g and u in float64, rounded to
+    float32 and then to bf16 (round to nearest even), and enters the down
+    linear as its bf16 input.
 R14 Regular Hadamard ([QIE] intro: "regular-Hadamard" rotation, no
     construction given): the group-256 matrix (J - 2I)^(x4) / 16, the fourth
     Kronecker power of the 4x4 regular Hadamard matrix J - 2I (every row of
@@ -409,6 +417,32 @@ def linear_w4a4_regular(x_bits, w_bits, bias_bits=None):
     qw, sw = quant_weight_w4_regular(w_bits)
     acc = int_gemm(qx, qw)
     return dict(qx=qx, sx=sx, qw=qw, sw=sw, acc=acc, y=epilogue(acc, sx, sw, bias_bits))
+
+
+# --- Text-encoder MLP block  [Q3N / "qwen3vl_4b" pages: the decoder
+# blocks' {gate,up,down}_proj Linears, all W4A4 ConvRot in the W4A4 file]
+
+def silu_mul_bf16(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u of two bf16 tensors (reading R15): in float64,
+    silu(v) = v / (1 + exp(-v)), the product rounded to float32 and then to
+    bf16 (both round to nearest even).  Returns bf16 bits."""
+    g = bf16_to_f32(g_bits).astype(np.float64)
+    u = bf16_to_f32(u_bits).astype(np.float64)
+    with np.errstate(over="ignore"):
+        h = g / (1.0 + np.exp(-g)) * u
+    return f32_to_bf16_rne(h.astype(F32))
+
+
+def mlp_w4a4(x_bits, wg_bits, wu_bits, wd_bits, group: int = GROUP):
+    """Gated MLP block of W4A4 ConvRot linears (reading R15): g and u the bf16
+    outputs of the gate and up linears of x, h = silu_mul_bf16(g, u), y the
+    W4A4 linear of h with the down weight (no biases).  Returns the
+    intermediates and the float32 output of the down linear."""
+    g = f32_to_bf16_rne(linear_w4a4(x_bits, wg_bits, None, group)["y"])
+    u = f32_to_bf16_rne(linear_w4a4(x_bits, wu_bits, None, group)["y"])
+    h = silu_mul_bf16(g, u)
+    d = linear_w4a4(h, wd_bits, None, group)
+    return dict(g=g, u=u, h=h, qh=d["qx"], sh=d["sx"], acc=d["acc"], y=d["y"])
 
 
 def linear_int8tw(x_bits, w_bits, bias_bits=None):

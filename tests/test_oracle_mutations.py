@@ -123,6 +123,17 @@ def _rht_generic(v, dtype=np.float32, order="asc", seq_sum=False, half_weight=Fa
     return (y.reshape(R, G, 256) * dtype(0.0625)).reshape(*lead, K).astype(dtype)
 
 
+def _silu_mul_sigmoid(g_bits, u_bits):
+    g = O.bf16_to_f32(g_bits).astype(np.float64)
+    u = O.bf16_to_f32(u_bits).astype(np.float64)
+    return O.f32_to_bf16_rne((1.0 / (1.0 + np.exp(-g)) * u).astype(F32))
+
+
+def _silu_no_up(g_bits, u_bits):
+    g = O.bf16_to_f32(g_bits).astype(np.float64)
+    return O.f32_to_bf16_rne((g / (1.0 + np.exp(-g))).astype(F32))
+
+
 MUTATIONS = {
     "fwht_descending_order": ("fwht", lambda v, group=256, dtype=np.float32:
                               _fwht_generic(v, group, dtype, order="desc")),
@@ -145,6 +156,8 @@ MUTATIONS = {
     "rht_descending_stages": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, order="desc")),
     "rht_left_to_right_sum": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, seq_sum=True)),
     "rht_diagonal_weight_1": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, half_weight=True)),
+    "mlp_sigmoid_not_silu": ("silu_mul_bf16", _silu_mul_sigmoid),
+    "mlp_gate_without_up": ("silu_mul_bf16", _silu_no_up),
 }
 
 PINS = [
@@ -178,6 +191,9 @@ PINS = [
     P.test_rht_stage_order_fixture,
     lambda: P.test_rht_constant_row_stays_constant(0.5),
     P.test_rht_one_hot_row_codes,
+    P.test_silu_mul_matches_library_logistic,
+    P.test_silu_mul_special_values,
+    P.test_mlp_block_close_to_float_mlp,
 ]
 
 

@@ -670,3 +670,72 @@ def test_rht_exact_identity_before_quantisation():
     lhs = O.rht(x, dtype=np.float64) @ O.rht(w, dtype=np.float64).T
     rhs = x @ w.T
     assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
+
+
+# ---------------------------------------------------------------------------
+# Text-encoder MLP block (R15)
+# ---------------------------------------------------------------------------
+
+def test_silu_mul_matches_library_logistic():
+    """silu(g) * u against scipy's logistic function (an independent
+    implementation): g * expit(g) * u in float64, rounded to float32, then
+    bf16.  The two float64 values differ by an ulp or so; a bf16 rounding
+    could only differ within ~1e-16 of a boundary, which 2e5 random values
+    do not hit."""
+    from scipy.special import expit
+    rng = np.random.default_rng(16)
+    g = si.f32_to_bf16_bits((rng.standard_t(3, size=200_000) * 2).astype(F32))
+    u = si.f32_to_bf16_bits(rng.standard_normal(200_000).astype(F32))
+    g64 = O.bf16_to_f32(g).astype(np.float64)
+    u64 = O.bf16_to_f32(u).astype(np.float64)
+    want = O.f32_to_bf16_rne((g64 * expit(g64) * u64).astype(F32))
+    assert np.array_equal(O.silu_mul_bf16(g, u), want)
+
+
+def test_silu_mul_special_values():
+    bits = lambda a: si.f32_to_bf16_bits(np.array(a, F32))
+    f = lambda h: O.bf16_to_f32(h)
+    # silu(0) = 0; u = 0 gives 0
+    assert np.all(f(O.silu_mul_bf16(bits([0.0, 0.0]), bits([3.0, -1.0]))) == 0)
+    assert np.all(f(O.silu_mul_bf16(bits([2.5, -7.0]), bits([0.0, 0.0]))) == 0)
+    # large positive g: silu(g) = g to float32 precision; large negative: 0
+    h = f(O.silu_mul_bf16(bits([96.0, -200.0, -1000.0]), bits([0.5, 1.0, 1.0])))
+    assert h[0] == 48.0 and h[1] == 0 and h[2] == 0
+    # silu(1) = 1 / (1 + e^-1) = 0.7310585786...; bf16 nearest is 0.73046875
+    assert f(O.silu_mul_bf16(bits([1.0]), bits([1.0])))[0] == np.float32(0.73046875)
+
+
+def test_silu_odd_part_identity():
+    """silu(v) - silu(-v) = v exactly in real arithmetic: with u = 1 the bf16
+    results satisfy it within two bf16 roundings."""
+    v = np.linspace(-8, 8, 1601).astype(F32)
+    vb = si.f32_to_bf16_bits(v)
+    nb = si.f32_to_bf16_bits(-O.bf16_to_f32(vb))
+    one = si.f32_to_bf16_bits(np.ones_like(v))
+    hp = O.bf16_to_f32(O.silu_mul_bf16(vb, one)).astype(np.float64)
+    hn = O.bf16_to_f32(O.silu_mul_bf16(nb, one)).astype(np.float64)
+    vv = O.bf16_to_f32(vb).astype(np.float64)
+    assert np.all(np.abs((hp - hn) - vv) <= 2.0 ** -8 * (np.abs(hp) + np.abs(hn)) + 1e-30)
+
+
+def test_mlp_block_close_to_float_mlp():
+    """The W4A4 MLP block against the float64 gated MLP of the same bf16
+    inputs: the error of three 4-bit linears, and the intermediates are the
+    bf16 outputs of the gate and up linears."""
+    rng = np.random.default_rng(17)
+    M, K, F, N = 24, 512, 768, 512
+    x = si.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    wg = si.f32_to_bf16_bits((rng.standard_normal((F, K)) * 0.05).astype(F32))
+    wu = si.f32_to_bf16_bits((rng.standard_normal((F, K)) * 0.05).astype(F32))
+    wd = si.f32_to_bf16_bits((rng.standard_normal((N, F)) * 0.05).astype(F32))
+    r = O.mlp_w4a4(x, wg, wu, wd)
+    assert np.array_equal(r["g"], O.f32_to_bf16_rne(O.linear_w4a4(x, wg)["y"]))
+    x64 = O.bf16_to_f32(x).astype(np.float64)
+    g = x64 @ O.bf16_to_f32(wg).astype(np.float64).T
+    u = x64 @ O.bf16_to_f32(wu).astype(np.float64).T
+    h = g / (1 + np.exp(-g)) * u
+    ref = h @ O.bf16_to_f32(wd).astype(np.float64).T
+    rel = np.linalg.norm(r["y"] - ref) / np.linalg.norm(ref)
+    # three 4-bit linears in a row (about 0.43 here; the "qwen3vl_4b" page
+    # reports ~0.5 relative RMSE for the whole W4A4 encoder at 76 tokens)
+    assert 0.1 < rel < 0.6
