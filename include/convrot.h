@@ -235,6 +235,27 @@ cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const 
                             int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* ---- text-encoder MLP block ([Q3N] file table and the "qwen3vl_4b" page:
+ *      the decoder blocks' gate_proj, up_proj, down_proj Linears, W4A4
+ *      ConvRot; the gated-SiLU form is this library's reading) ------------
+ * y = down(h), h = silu(g) * u, g = gate(x), u = up(x): three W4A4 linears
+ * (packed with cr_pack_weight_w4, group-256 Sylvester rotation, no biases)
+ * and, between them, one kernel that forms h and quantises it for the down
+ * projection.  g and u are the bf16 outputs cr_linear_w4a4 gives; h =
+ * bf16(float(g / (1 + exp(-g)) * u)) with the quotient and products in
+ * float64 (both roundings to nearest even).  x is quantised once for the
+ * gate and up GEMMs.  All launches go on `stream`, none allocates.
+ *   x_bf16 [M,K]; wg, wu: [F,K] packed + tensor scale; wd: [N,F] packed +
+ *   tensor scale; y_bf16 [M,N] (out); ws / ws_bytes: at least
+ *   cr_mlp_workspace_bytes(M,K,F,N) (g and u live there).
+ * K and F must be multiples of 256 (CR_ERR_GROUP otherwise). */
+size_t cr_mlp_workspace_bytes(int M, int K, int F, int N);
+
+cr_status cr_mlp_w4a4(const void* x_bf16, int M, int K, const void* wg_packed, const float* wg_scale,
+                      const void* wu_packed, const float* wu_scale, int F, const void* wd_packed,
+                      const float* wd_scale, int N, void* y_bf16, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* ---- status ----------------------------------------------------------- */
 const char* cr_status_str(cr_status s);
 const char* cr_last_error(void);   /* thread-local detail of the last failure */
@@ -252,6 +273,12 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K,
  * decoded int8 w8). */
 cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K,
                                void* codes, hipStream_t stream);
+
+/* The down projection's input codes [M,K] (one per byte, [-8,7]) and scales
+ * [M] of the MLP block, formed from bf16 g, u [M,K] by the same kernel as in
+ * cr_mlp_w4a4. */
+cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int K,
+                              void* codes, float* scales, hipStream_t stream);
 
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */

@@ -29,6 +29,7 @@ __all__ = [
     "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8", "pack_weight_int8rot",
     "linear_w4a4", "linear_int8tw", "linear_w4a8", "linear_int8rot",
     "pack_weight_w4_regular", "linear_w4a4_regular",
+    "mlp_workspace_bytes", "mlp_w4a4", "dbg_quant_swiglu",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
@@ -51,6 +52,7 @@ EXPORTS = [
     "cr_pack_weight_int8rot", "cr_linear_int8rot",
     "cr_pack_weight_w4_group", "cr_linear_w4a4_group",
     "cr_pack_weight_w4_regular", "cr_linear_w4a4_regular",
+    "cr_mlp_workspace_bytes", "cr_mlp_w4a4", "cr_dbg_quant_swiglu",
 ]
 
 
@@ -84,6 +86,9 @@ def lib() -> ctypes.CDLL:
         "cr_linear_w4a4_group": (i, [vp, i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_pack_weight_w4_regular": (i, [vp, i, i, vp, vp, vp]),
         "cr_linear_w4a4_regular": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_mlp_workspace_bytes": (sz, [i, i, i, i]),
+        "cr_mlp_w4a4": (i, [vp, i, i, vp, vp, vp, vp, i, vp, vp, i, vp, vp, sz, vp]),
+        "cr_dbg_quant_swiglu": (i, [vp, vp, i, i, vp, vp, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
@@ -278,6 +283,51 @@ def linear_int8rot(x, packed, scale, N, bias=None, out=None, workspace=None):
 def linear_w4a8(x, packed, s_channel, N, bias=None, out=None, workspace=None):
     """y = asym W4A8 codebook linear; s_channel float32 [N]."""
     return _linear("cr_linear_w4a8", W4A8, x, packed, s_channel, N, bias, out, workspace)
+
+
+# ---------------------------------------------------------------------------
+# Text-encoder MLP block
+# ---------------------------------------------------------------------------
+
+def mlp_workspace_bytes(M: int, K: int, F: int, N: int) -> int:
+    return int(lib().cr_mlp_workspace_bytes(M, K, F, N))
+
+
+def mlp_w4a4(x, wg, sg, wu, su, F, wd, sd, N, out=None, workspace=None):
+    """y = down(silu(gate(x)) * up(x)) with W4A4 ConvRot linears (weights from
+    pack_weight_w4: gate and up [F,K], down [N,F]; no biases)."""
+    _dev(x, "x", torch.bfloat16)
+    for t, n in ((wg, "wg"), (wu, "wu"), (wd, "wd")):
+        _dev(t, n, torch.uint8)
+    for t, n in ((sg, "sg"), (su, "su"), (sd, "sd")):
+        _dev(t, n, torch.float32)
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    need = max(mlp_workspace_bytes(M, K, F, N), 256)
+    if workspace is None:
+        workspace = _empty_u8(need, x.device)
+    else:
+        _dev(workspace, "workspace", torch.uint8)
+    _check(lib().cr_mlp_w4a4(_ptr(x), M, K, _ptr(wg), _ptr(sg), _ptr(wu), _ptr(su), F, _ptr(wd), _ptr(sd), N,
+                             _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def dbg_quant_swiglu(g: torch.Tensor, u: torch.Tensor):
+    """Codes int8 [M,K] and scales [M] of h = silu(g) * u, as the MLP block
+    quantises the down projection's input."""
+    _dev(g, "g", torch.bfloat16)
+    _dev(u, "u", torch.bfloat16)
+    M, K = g.shape
+    codes = torch.empty((M, K), dtype=torch.int8, device=g.device)
+    scales = torch.empty(max(M, 1), dtype=torch.float32, device=g.device)
+    _check(lib().cr_dbg_quant_swiglu(_ptr(g), _ptr(u), M, K, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales[:M]
 
 
 # ---------------------------------------------------------------------------

@@ -211,9 +211,86 @@ cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, cons
     return gemm_phase(kind, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
 }
 
+// Gated MLP block workspace: [x codes + gate/up partials | g | u | h codes +
+// down partials], each region at a 256-byte boundary.
+struct MlpLayout {
+    size_t g, u, b, total;
+};
+
+MlpLayout mlp_layout(int M, int K, int F, int N) {
+    MlpLayout l{};
+    l.g = a256(ws_layout(CR_W4A4, M, F, K).total);
+    l.u = l.g + a256((size_t)M * F * 2);
+    l.b = l.u + a256((size_t)M * F * 2);
+    l.total = l.b + ws_layout(CR_W4A4, M, N, F).total;
+    return l;
+}
+
+cr_status check_mlp_shape(int M, int K, int F, int N) {
+    cr_status s;
+    if ((s = check_m(M)) != CR_OK) return s;
+    if ((s = check_nk(CR_W4A4, F, K)) != CR_OK) return s;
+    return check_nk(CR_W4A4, N, F);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t cr_mlp_workspace_bytes(int M, int K, int F, int N) {
+    if (check_mlp_shape(M, K, F, N) != CR_OK) return 0;
+    return mlp_layout(M, K, F, N).total;
+}
+
+cr_status cr_mlp_w4a4(const void* x_bf16, int M, int K, const void* wg_packed, const float* wg_scale,
+                      const void* wu_packed, const float* wu_scale, int F, const void* wd_packed,
+                      const float* wd_scale, int N, void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream) {
+    cr_status s;
+    if ((s = check_mlp_shape(M, K, F, N)) != CR_OK) return s;
+    if (!wg_packed || !wg_scale || !wu_packed || !wu_scale || !wd_packed || !wd_scale)
+        return fail(CR_ERR_NULL, "packed weight or scale is NULL");
+    if (!aligned16(wg_packed) || !aligned16(wu_packed) || !aligned16(wd_packed))
+        return fail(CR_ERR_ALIGN, "packed weight not 16-byte aligned");
+    if (M == 0) return ok();
+    if (!x_bf16 || !y_bf16 || !ws) return fail(CR_ERR_NULL, "x, y or workspace is NULL");
+    if (!aligned16(x_bf16) || !aligned16(y_bf16) || !aligned16(ws))
+        return fail(CR_ERR_ALIGN, "x, y or workspace not 16-byte aligned");
+    const MlpLayout l = mlp_layout(M, K, F, N);
+    if (ws_bytes < l.total) return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    if ((s = check_device()) != CR_OK) return s;
+    char* w = static_cast<char*>(ws);
+    // x quantised once for the gate and up GEMMs
+    if ((s = quantize_phase(CR_W4A4, x_bf16, M, K, w, l.g, stream)) != CR_OK) return s;
+    if ((s = gemm_phase(CR_W4A4, M, K, wg_packed, wg_scale, F, nullptr, w + l.g, nullptr, w, l.g, stream)) != CR_OK)
+        return s;
+    if ((s = gemm_phase(CR_W4A4, M, K, wu_packed, wu_scale, F, nullptr, w + l.u, nullptr, w, l.g, stream)) != CR_OK)
+        return s;
+    // h = silu(g) * u, rotated and quantised for the down GEMM
+    const WsLayout lb = ws_layout(CR_W4A4, M, N, F);
+    char* wb = w + l.b;
+    s = launch_err(cr::launch_quant_swiglu(reinterpret_cast<const uint16_t*>(w + l.g),
+                                           reinterpret_cast<const uint16_t*>(w + l.u), M, F,
+                                           reinterpret_cast<int8_t*>(wb + lb.qx), reinterpret_cast<float*>(wb + lb.sx),
+                                           reinterpret_cast<int32_t*>(wb + lb.ra), true, stream),
+                   "MLP activation quantisation");
+    if (s != CR_OK) return s;
+    return gemm_phase(CR_W4A4, M, F, wd_packed, wd_scale, N, nullptr, y_bf16, nullptr, wb, lb.total, stream);
+}
+
+cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int K, void* codes, float* scales,
+                              hipStream_t stream) {
+    cr_status s;
+    if (M < 0 || M > CR_MAX_DIM) return fail(CR_ERR_SHAPE, "bad M=%d", M);
+    if ((s = check_nk(CR_W4A4, 1, K)) != CR_OK) return s;
+    if (M == 0) return ok();
+    if (!g_bf16 || !u_bf16 || !codes || !scales) return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(g_bf16) || !aligned16(u_bf16) || !aligned16(codes))
+        return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::launch_quant_swiglu(static_cast<const uint16_t*>(g_bf16), static_cast<const uint16_t*>(u_bf16),
+                                              M, K, static_cast<int8_t*>(codes), scales, nullptr, false, stream),
+                      "MLP activation quantisation");
+}
 
 size_t cr_packed_bytes(int kind, int N, int K) {
     if (check_kind(kind) != CR_OK || check_nk(kind, N, K) != CR_OK) return 0;

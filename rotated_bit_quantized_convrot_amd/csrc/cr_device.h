@@ -35,6 +35,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// h = silu(g) * u of two bf16 values: float64 g / (1 + exp(-g)) * u, rounded
+// to float32 and then to bf16 (round to nearest even); returned as float.
+__device__ __forceinline__ float silu_mul_bf16(float g, float u) {
+    const double gd = (double)g;
+    const double h = gd / (1.0 + exp(-gd)) * (double)u;
+    return __uint_as_float(f32_to_bf16_rne((float)h) << 16);
+}
+
 // ---------------------------------------------------------------------------
 // Lane exchange v <- v[lane ^ MASK] inside each 32-lane half of the wave.
 //   MASK 1, 2 : DPP quad_perm;  MASK 8 : DPP row_ror:8 (a 16-lane row rotated

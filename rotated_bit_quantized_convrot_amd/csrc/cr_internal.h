@@ -65,6 +65,12 @@ __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_o
 hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
                             float* sx, int32_t* ra, bool packed, hipStream_t st);
 
+// W4A4 activations (group-256 Sylvester rotation) of h = silu(g) * u, the
+// gated MLP's input to its down projection, from the bf16 gate and up
+// outputs g, u [M, K]; outputs as launch_quant_act(WK_W4, 256, ...).
+hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
+                               int32_t* ra, bool packed, hipStream_t st);
+
 // W4 weight with the rotation `group` (as for launch_quant_act).
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* out, float* scale,
                           hipStream_t st);

@@ -129,6 +129,33 @@ __device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
     return ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
 }
 
+// The 16 values of x at x + off (16-byte aligned), as float; with GLU, x is
+// the gate output g, u the up output, and the values are silu(g) * u
+// rounded to bf16 (silu_mul_bf16).
+template <bool GLU>
+__device__ __forceinline__ void load16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u, size_t off,
+                                       float (&v)[16]) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + off);
+    const uint4 r0 = src[0], r1 = src[1];
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    if constexpr (GLU) {
+        const uint4* su = reinterpret_cast<const uint4*>(u + off);
+        const uint4 q0 = su[0], q1 = su[1];
+        const uint32_t z[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            v[2 * t] = silu_mul_bf16(bf16_lo(w[t]), bf16_lo(z[t]));
+            v[2 * t + 1] = silu_mul_bf16(bf16_hi(w[t]), bf16_hi(z[t]));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            v[2 * t] = bf16_lo(w[t]);
+            v[2 * t + 1] = bf16_hi(w[t]);
+        }
+    }
+}
+
 // Rotated activations: codes [M, K] int8 (natural order) and scales [M].
 //
 // Each row is handled by a segment of lanes: 16 lanes per 256-group, each
@@ -154,9 +181,10 @@ __device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
 //
 // PACKED (W4A4): codes in the 4-bit tile layout, activation nibble forms,
 // and ra[m] = the sum of the row's codes held in high nibbles (k % 8 >= 4).
-template <int GPL, int QMAX, int LO, int HI, bool PACKED, int GS>
-__global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, int M, int K,
-                                                        int seg_log2, int8_t* __restrict__ qx,
+// GLU: the row is silu(g) * u of the gate and up outputs x = g and u.
+template <int GPL, int QMAX, int LO, int HI, bool PACKED, int GS, bool GLU>
+__global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
+                                                        int M, int K, int seg_log2, int8_t* __restrict__ qx,
                                                         float* __restrict__ sx, int32_t* __restrict__ ra) {
     __shared__ float red[16];
     __shared__ int ired[16];
@@ -180,14 +208,7 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
     for (int i = 0; i < GPL; ++i) {
         const int g = gslot + i * gstride;
         if (row_ok && g < G) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)g * 256 + j * 16);
-            const uint4 r0 = src[0], r1 = src[1];
-            const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                v[i][2 * t] = bf16_lo(w[t]);
-                v[i][2 * t + 1] = bf16_hi(w[t]);
-            }
+            load16<GLU>(x, u, (size_t)m * K + (size_t)g * 256 + j * 16, v[i]);
             fwht16_signed<GS>(v[i], l);
 #pragma unroll
             for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
@@ -251,9 +272,9 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
 // most), so that each store instruction writes, for every 64-k chunk it
 // touches, the four rows' 32-byte pieces: one whole 128-byte line of the
 // 4-bit tile.  Same arithmetic as k_quant_act_rot (PACKED).
-template <int GPL, int GS>
-__global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, int M, int K,
-                                                         int8_t* __restrict__ qx, float* __restrict__ sx,
+template <int GPL, int GS, bool GLU>
+__global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
+                                                         int M, int K, int8_t* __restrict__ qx, float* __restrict__ sx,
                                                          int32_t* __restrict__ ra) {
     __shared__ float redm[16][4];
     __shared__ int reds[16][4];
@@ -270,14 +291,7 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
     for (int i = 0; i < GPL; ++i) {
         const int g = wave + i * nw;
         if (row_ok && g < G) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)g * 256 + j * 16);
-            const uint4 r0 = src[0], r1 = src[1];
-            const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                v[i][2 * t] = bf16_lo(w[t]);
-                v[i][2 * t + 1] = bf16_hi(w[t]);
-            }
+            load16<GLU>(x, u, (size_t)m * K + (size_t)g * 256 + j * 16, v[i]);
             fwht16_signed<GS>(v[i], j);
 #pragma unroll
             for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(v[i][t]));
@@ -368,14 +382,15 @@ static int rot_threads(int G, int* gpl) {
     return round_up(nhw * 32, 64);      // whole waves (half-waves past G idle)
 }
 
-template <int QMAX, int LO, int HI, bool PACKED, int GS = 256>
-static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float* sx, int32_t* ra, hipStream_t st) {
+template <int QMAX, int LO, int HI, bool PACKED, int GS = 256, bool GLU = false>
+static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K, int8_t* qx, float* sx, int32_t* ra,
+                             hipStream_t st) {
     const int T = K / 16;              // lanes per row
     if (T <= 64) {
         int lg = 4;
         while ((1 << lg) < T) ++lg;
         const int rows = 256 >> lg;
-        k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, M, K, lg, qx, sx, ra);
+        k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, u, M, K, lg, qx, sx, ra);
         return hipGetLastError();
     }
     int gpl = 1;
@@ -388,18 +403,18 @@ static hipError_t launch_rot(const uint16_t* x, int M, int K, int8_t* qx, float*
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED, GS><<<grid, block, 0, st>>>(x, M, K, -1, qx, sx, ra); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-// W4A4 activations with rotation group GS.
-template <int GS>
-static hipError_t launch_w4_act(const uint16_t* x, int M, int K, int8_t* qx, float* sx, int32_t* ra, bool packed,
-                                hipStream_t st) {
+// W4A4 activations with rotation GS (GLU: of silu(x) * u).
+template <int GS, bool GLU = false>
+static hipError_t launch_w4_act(const uint16_t* x, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
+                                int32_t* ra, bool packed, hipStream_t st) {
     const int G = K >> 8;
     // four rows per block where there are rows enough to fill the chip
     // with such blocks (at smaller M one row per block keeps more lanes busy)
@@ -413,15 +428,15 @@ static hipError_t launch_w4_act(const uint16_t* x, int M, int K, int8_t* qx, flo
         const int nw = (G + gpl - 1) / gpl;
         const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
         switch (gpl) {
-            case 1: k_quant_w4_rows4<1, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
-            case 2: k_quant_w4_rows4<2, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
-            case 4: k_quant_w4_rows4<4, GS><<<grid, block, 0, st>>>(x, M, K, qx, sx, ra); break;
+            case 1: k_quant_w4_rows4<1, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
+            case 2: k_quant_w4_rows4<2, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
+            case 4: k_quant_w4_rows4<4, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
-    return packed ? launch_rot<7, -8, 7, true, GS>(x, M, K, qx, sx, ra, st)
-                  : launch_rot<7, -8, 7, false, GS>(x, M, K, qx, sx, nullptr, st);
+    return packed ? launch_rot<7, -8, 7, true, GS, GLU>(x, u, M, K, qx, sx, ra, st)
+                  : launch_rot<7, -8, 7, false, GS, GLU>(x, u, M, K, qx, sx, nullptr, st);
 }
 
 hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
@@ -429,18 +444,24 @@ hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K
     if (kind == WK_W4) {
         if (packed && ra == nullptr) return hipErrorInvalidValue;
         switch (group) {
-            case 256: return launch_w4_act<256>(x, M, K, qx, sx, ra, packed, st);
-            case 64: return launch_w4_act<64>(x, M, K, qx, sx, ra, packed, st);
-            case 16: return launch_w4_act<16>(x, M, K, qx, sx, ra, packed, st);
-            case kRotRegular: return launch_w4_act<kRotRegular>(x, M, K, qx, sx, ra, packed, st);
+            case 256: return launch_w4_act<256>(x, nullptr, M, K, qx, sx, ra, packed, st);
+            case 64: return launch_w4_act<64>(x, nullptr, M, K, qx, sx, ra, packed, st);
+            case 16: return launch_w4_act<16>(x, nullptr, M, K, qx, sx, ra, packed, st);
+            case kRotRegular: return launch_w4_act<kRotRegular>(x, nullptr, M, K, qx, sx, ra, packed, st);
             default: return hipErrorInvalidValue;
         }
     }
     // W4A8 and ConvRot INT8: rotated, per-row int8
-    if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, M, K, qx, sx, nullptr, st);
+    if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, nullptr, M, K, qx, sx, nullptr, st);
     // two waves per row when four per row would exceed what the chip holds at once
     k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx);
     return hipGetLastError();
+}
+
+hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
+                               int32_t* ra, bool packed, hipStream_t st) {
+    if (packed && ra == nullptr) return hipErrorInvalidValue;
+    return launch_w4_act<256, true>(g, u, M, K, qx, sx, ra, packed, st);
 }
 
 // ---------------------------------------------------------------------------

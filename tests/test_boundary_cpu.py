@@ -161,3 +161,17 @@ def test_w4_regular_argument_errors(L):
     assert L.cr_linear_w4a4_regular(vp, 8, 300, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["GROUP"]
     assert L.cr_pack_weight_w4_regular(None, 64, 512, vp, vp, None) == CR["NULL"]
     assert L.cr_linear_w4a4_regular(vp, 8, 512, vp, vp, 64, None, vp, vp, 16, None) == CR["WORKSPACE"]
+
+
+def test_mlp_sizes_and_errors(L):
+    # workspace: x codes + gate/up partials, g and u (bf16), h codes + down partials
+    M, K, F, N = 76, 2560, 9728, 2560
+    need = L.cr_mlp_workspace_bytes(M, K, F, N)
+    assert need >= L.cr_workspace_bytes(0, M, F, K) + 2 * M * F * 2 + L.cr_workspace_bytes(0, M, N, F) - 1024
+    assert L.cr_mlp_workspace_bytes(M, 300, F, N) == 0 and L.cr_mlp_workspace_bytes(M, K, 1000, N) == 0
+    vp = ctypes.c_void_p(16)
+    assert L.cr_mlp_w4a4(vp, M, 300, vp, vp, vp, vp, F, vp, vp, N, vp, vp, 1 << 30, None) == CR["GROUP"]
+    assert L.cr_mlp_w4a4(vp, M, K, vp, vp, vp, vp, 1000, vp, vp, N, vp, vp, 1 << 30, None) == CR["GROUP"]
+    assert L.cr_mlp_w4a4(vp, M, K, None, vp, vp, vp, F, vp, vp, N, vp, vp, 1 << 30, None) == CR["NULL"]
+    assert L.cr_mlp_w4a4(vp, M, K, vp, vp, vp, vp, F, vp, vp, N, vp, vp, 16, None) == CR["WORKSPACE"]
+    assert L.cr_dbg_quant_swiglu(vp, vp, 4, 300, vp, vp, None) == CR["GROUP"]
