@@ -23,7 +23,9 @@ calls and timing it with HIP events on the launch stream:
     int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer, and the
     ConvRot INT8 row-scaled format on a square text-encoder projection
     (K=N=2560) at M=76 and M=1220, and the DiT W1 layer with W4A4 rotation
-    groups of 64 and 16 and with the group-256 regular Hadamard.
+    groups of 64 and 16 and with the group-256 regular Hadamard;
+  * the text-encoder MLP block (cr_mlp_w4a4: gate and up 2560 -> 9728,
+    silu(g) * u, down 9728 -> 2560) at M=76 (cold weights) and M=1220.
 The CPU oracle (NumPy) is timed on a row sample of the headline layer.
 
 Prints one JSON line.
@@ -207,6 +209,39 @@ def measure_row(torch, lay: Layer, cold: bool, reps: int):
     return out
 
 
+def measure_mlp(torch, crp, M: int, cold: bool, reps: int):
+    """The text-encoder MLP block (K=2560, F=9728, N=2560) through
+    cr_mlp_w4a4, by graph replay; cold: the three packed weights cycled
+    through enough copies to exceed the last-level cache."""
+    import synthetic_inputs as si
+    K, F, N = 2560, 9728, 2560
+    Lg, Ld = si.te_gate_up(M), si.te_down(M)
+    dev = "cuda"
+    x = torch.from_numpy(Lg.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    rng = np.random.default_rng(7)
+    wu = si.f32_to_bf16_bits((rng.standard_normal((F, K)) * 0.02).astype(np.float32))
+    packs = []
+    for w in (Lg.w, wu, Ld.w):
+        t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
+        packs.append(crp.pack_weight_w4(t))
+        del t
+    copies = max(1, COLD_COPIES // 3) if cold else 1
+    sets = [[(p.clone(), s) for (p, s) in packs] for _ in range(copies - 1)] + [packs]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(crp.mlp_workspace_bytes(M, K, F, N), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        (pg, sg), (pu, su), (pd, sd) = sets[i % len(sets)]
+        crp.mlp_w4a4(x, pg, sg, pu, su, F, pd, sd, N, out=y, workspace=ws)
+
+    calls = max(reps, len(sets))
+    us = graph_time_us(torch, [lambda i=i: call(i) for i in range(calls)])
+    ops = 2.0 * M * K * F * 2 + 2.0 * M * F * N
+    wbytes = (2 * F * K + N * F) / 2
+    return {"mlp_us": us, "tops": ops / (us * 1e-6) / 1e12, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
+            "cold_weights": bool(cold), "shape": {"M": M, "K": K, "F": F, "N": N}, "launches": 5}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a row sample of the headline layer
 # ---------------------------------------------------------------------------
@@ -361,7 +396,7 @@ def main():
     rows = {"dit_w1": hrow}
     wanted = [] if args.rows == "none" else (
         [r for r in specs if r != "dit_w1"] if args.rows == "all" else
-        [r for r in args.rows.split(",") if r != "dit_w1"])
+        [r for r in args.rows.split(",") if r != "dit_w1" and r in specs])
     for name in wanted:
         sp = specs[name]
         _log(f"row {name}")
@@ -372,6 +407,14 @@ def main():
              f"({r['gemm_tops']:.0f} TOPS, weights {r['weight_gbs']:.0f} GB/s), quant {r['quant_us']:.2f} us")
         del lay
         torch.cuda.empty_cache()
+
+    for name, M, cold in (("te_mlp_M76", 76, True), ("te_mlp_M1220", 1220, False)):
+        if args.rows == "all" or name in args.rows.split(","):
+            _log(f"row {name}")
+            rows[name] = measure_mlp(torch, crp, M, cold, args.repeat)
+            _log(f"  MLP block {rows[name]['mlp_us']:.2f} us ({rows[name]['tops']:.0f} TOPS, "
+                 f"weights {rows[name]['weight_gbs']:.0f} GB/s)")
+            torch.cuda.empty_cache()
 
     achieved = head.ops() / (step_gemm_us * 1e-6) / 1e12
     roofline = {
