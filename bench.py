@@ -210,18 +210,17 @@ def measure_row(torch, lay: Layer, cold: bool, reps: int):
 
 
 def measure_mlp(torch, crp, M: int, cold: bool, reps: int):
-    """The text-encoder MLP block (K=2560, F=9728, N=2560) through
-    cr_mlp_w4a4, by graph replay; cold: the three packed weights cycled
-    through enough copies to exceed the last-level cache."""
+    """The text-encoder MLP block (K=2560, F=9728, N=2560; inputs
+    synthetic_inputs.te_mlp) through cr_mlp_w4a4, by graph replay; cold: the
+    three packed weights cycled through enough copies to exceed the
+    last-level cache."""
     import synthetic_inputs as si
     K, F, N = 2560, 9728, 2560
-    Lg, Ld = si.te_gate_up(M), si.te_down(M)
+    xb, wg, wu, wd = si.te_mlp(M)
     dev = "cuda"
-    x = torch.from_numpy(Lg.x.view(np.int16)).view(torch.bfloat16).to(dev)
-    rng = np.random.default_rng(7)
-    wu = si.f32_to_bf16_bits((rng.standard_normal((F, K)) * 0.02).astype(np.float32))
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
     packs = []
-    for w in (Lg.w, wu, Ld.w):
+    for w in (wg, wu, wd):
         t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
         packs.append(crp.pack_weight_w4(t))
         del t

@@ -122,6 +122,15 @@ def te_attn_proj(M: int = 76, seed: int = 2) -> LayerInputs:
                       outlier_frac=0.005, outlier_scale=40.0)
 
 
+def te_mlp(M: int = 76):
+    """Text-encoder MLP block inputs (hidden 2560, intermediate 9728): x and the
+    gate weight from te_gate_up(M), the up weight from te_gate_up(M, seed=3),
+    the down weight from te_down(M).  Returns (x, w_gate, w_up, w_down) as bf16
+    bit patterns."""
+    g = te_gate_up(M)
+    return g.x, g.w, te_gate_up(M, seed=3).w, te_down(M).w
+
+
 def dit_w1(M: int = 4096, seed: int = 0) -> LayerInputs:
     return make_layer(f"dit_w1_M{M}", M, 3072, 12288, seed=seed, x_dist="student_t",
                       outlier_frac=0.01, outlier_scale=50.0, bias_std=0.01)

@@ -123,3 +123,59 @@ def test_w4a8_full_size(crp):
     qx, sx = O.quant_act_w4a8(L.x[rows])
     ref_acc = O.int_gemm(qx, w8)
     _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, enc["s_channel"], None))
+
+
+W4_VARIANTS = {"dit_w1_group64": 4, "dit_w1_group16": 5, "dit_w1_regular": 6}
+
+
+@pytest.mark.parametrize("name", list(W4_VARIANTS))
+def test_w4a4_rotation_variants_full_size(crp, name):
+    """DiT W1 with the other rotations, as the benchmark rows run them."""
+    print(f"[fullsize] {name}", flush=True)
+    kind = W4_VARIANTS[name]
+    L = si.dit_w1()
+    x = to_dev_bf16(L.x)
+    w = to_dev_bf16(L.w)
+    if kind == 6:
+        p, s = crp.pack_weight_w4_regular(w)
+        y = crp.linear_w4a4_regular(x, p, s, L.N, to_dev_bf16(L.bias))
+        qw, sw = O.quant_weight_w4_regular(L.w)
+        qx, sx = O.quant_act_w4a4_regular(L.x[_rows(L.M)])
+    else:
+        G = 64 if kind == 4 else 16
+        p, s = crp.pack_weight_w4(w, group=G)
+        y = crp.linear_w4a4(x, p, s, L.N, to_dev_bf16(L.bias), group=G)
+        qw, sw = O.quant_weight_w4(L.w, G)
+        qx, sx = O.quant_act_w4a4(L.x[_rows(L.M)], G)
+    acc = crp.dbg_linear_acc(kind, x, p, L.N)
+    torch.cuda.synchronize()
+    assert s.cpu().numpy()[:1].view(np.uint32)[0] == np.float32(sw).view(np.uint32)
+    ref_acc = O.int_gemm(qx, qw)
+    _check(y, acc, _rows(L.M), ref_acc, O.epilogue(ref_acc, sx, sw, L.bias))
+
+
+@pytest.mark.parametrize("M", [76, 1220])
+def test_mlp_block_full_size(crp, M):
+    """The text-encoder MLP block at the benchmark's shapes: the GPU runs the
+    whole block, the oracle follows sampled rows through it (rows are
+    independent given the three tensorwise weight scales) and the bf16
+    outputs must be equal."""
+    print(f"[fullsize] te_mlp_M{M}", flush=True)
+    xb, wg, wu, wd = si.te_mlp(M)
+    F, N = wg.shape[0], wd.shape[0]
+    packs = [crp.pack_weight_w4(to_dev_bf16(w)) for w in (wg, wu, wd)]
+    (pg, sg), (pu, su), (pd, sd) = packs
+    y = crp.mlp_w4a4(to_dev_bf16(xb), pg, sg, pu, su, F, pd, sd, N)
+    torch.cuda.synchronize()
+    rows = _rows(M)
+    qg, s_g = O.quant_weight_w4(wg)
+    qu, s_u = O.quant_weight_w4(wu)
+    qd, s_d = O.quant_weight_w4(wd)
+    qx, sx = O.quant_act_w4a4(xb[rows])
+    g = O.f32_to_bf16_rne(O.epilogue(O.int_gemm(qx, qg), sx, s_g, None))
+    u = O.f32_to_bf16_rne(O.epilogue(O.int_gemm(qx, qu), sx, s_u, None))
+    qh, sh = O.quant_act_w4a4(O.silu_mul_bf16(g, u))
+    ref_y = O.epilogue(O.int_gemm(qh, qd), sh, s_d, None)
+    got = y.index_select(0, torch.from_numpy(rows).cuda())
+    assert max_rel_err(bf16_dev_to_f32(got), ref_y) <= TOL
+    assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(ref_y))

@@ -35,3 +35,40 @@ def test_graph_replays_match_eager(M, K, N):
         torch.cuda.synchronize()
         assert torch.equal(y, ref), f"replay {i}"
         assert not torch.equal(other, ref)
+
+
+def test_graph_mlp_block_and_rotation_variants():
+    """The MLP block (five launches, workspace-resident g and u) and the group /
+    regular-Hadamard linears under capture: every replay equals eager."""
+    import rotated_bit_quantized_convrot_amd as crp
+    M, K, F, N = 76, 512, 768, 256
+    xb, _, _, _ = si.te_mlp(M)
+    L = si.random_layer(M, K, N, seed=9)
+    rng = np.random.default_rng(10)
+    ws_ = [si.f32_to_bf16_bits((rng.standard_normal(s) * 0.02).astype(np.float32)) for s in ((F, K), (F, K), (N, F))]
+    x = to_dev_bf16(L.x)
+    (pg, sg), (pu, su), (pd, sd) = [crp.pack_weight_w4(to_dev_bf16(w)) for w in ws_]
+    p64, s64 = crp.pack_weight_w4(to_dev_bf16(L.w), group=64)
+    prh, srh = crp.pack_weight_w4_regular(to_dev_bf16(L.w))
+    wsm = torch.empty(crp.mlp_workspace_bytes(M, K, F, N), dtype=torch.uint8, device="cuda")
+    wsl = torch.empty(crp.workspace_bytes(0, M, N, K), dtype=torch.uint8, device="cuda")
+    ym = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y64 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yrh = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ref = [crp.mlp_w4a4(x, pg, sg, pu, su, F, pd, sd, N).clone(),
+           crp.linear_w4a4(x, p64, s64, N, group=64).clone(),
+           crp.linear_w4a4_regular(x, prh, srh, N).clone()]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        crp.mlp_w4a4(x, pg, sg, pu, su, F, pd, sd, N, out=ym, workspace=wsm)
+        crp.linear_w4a4(x, p64, s64, N, out=y64, workspace=wsl, group=64)
+        crp.linear_w4a4_regular(x, prh, srh, N, out=yrh, workspace=wsl)
+    for i in range(4):
+        for t in (ym, y64, yrh):
+            t.zero_()
+        crp.linear_w4a4(x, p64, s64, N)           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ym, ref[0]) and torch.equal(y64, ref[1]) and torch.equal(yrh, ref[2]), f"replay {i}"
