@@ -417,8 +417,10 @@ static hipError_t launch_w4_act(const uint16_t* x, const uint16_t* u, int M, int
                                 int32_t* ra, bool packed, hipStream_t st) {
     const int G = K >> 8;
     // four rows per block where there are rows enough to fill the chip
-    // with such blocks (at smaller M one row per block keeps more lanes busy)
-    if (packed && G <= 64 && M >= 2048) {
+    // with such blocks (at smaller M one row per block keeps more lanes busy;
+    // past 32 groups a row's own block has more loads in flight: DiT W2,
+    // K = 12288, 36.1 -> 31.8 us)
+    if (packed && G <= 32 && M >= 2048) {
         int gpl = 1;
         while ((G + gpl - 1) / gpl > 16) gpl <<= 1;
         // two 256-blocks per lane from K = 2048 up: half as many waves, so

@@ -47,6 +47,8 @@ ACT_CASES = [
     # grids larger than the chip holds at once: two groups per lane (rotated)
     # or two waves per row (int8_tensorwise)
     (2, 2100, 3840), (0, 1100, 8192), (1, 2100, 640),
+    # M >= 2048 with more than 32 groups per row: one row per block
+    (0, 2050, 9216),
     (3, 76, 2560), (3, 300, 512), (3, 5, 9728),
 ]
 
