@@ -221,15 +221,16 @@ cr_status cr_linear_w4a8(const void* x_bf16, int M, int K, const void* w_packed,
  * two kernels on one stream (rotation + quantisation need the whole row for
  * its scale before any code can be used). */
 
-/* Rotation (W4A4, W4A8) and per-row quantisation of x [M,K] into `ws`.
+/* Rotation (the W4A4 kinds, W4A8, ConvRot INT8) and per-row quantisation of
+ * x [M,K] into `ws`.
  * ws_bytes >= cr_workspace_bytes(kind, M, 1, K). */
 cr_status cr_quantize_activations(int kind, const void* x_bf16, int M, int K, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
 /* GEMM + rank-one epilogue from a workspace filled by
  * cr_quantize_activations(kind, x, M, K, ...).  w_scale is the tensor scale
- * (W4A4, int8_tensorwise), s_channel [N] (W4A8) or the row scales [N]
- * (ConvRot INT8).
+ * (the W4A4 kinds, int8_tensorwise), s_channel [N] (W4A8) or the row scales
+ * [N] (ConvRot INT8).
  * ws_bytes >= cr_workspace_bytes(kind, M, N, K). */
 cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const float* w_scale,
                             int N, const void* bias_bf16, void* y_bf16, void* ws, size_t ws_bytes,
