@@ -281,6 +281,11 @@ cr_status cr_dbg_unpack_weight(int kind, const void* w_packed, int N, int K,
 cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int K,
                               void* codes, float* scales, hipStream_t stream);
 
+/* h = silu(g) * u of n bf16 pairs (bf16 out), computed as the MLP block's
+ * quantiser computes it. */
+cr_status cr_dbg_silu_mul(const void* g_bf16, const void* u_bf16, size_t n, void* h_bf16,
+                          hipStream_t stream);
+
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */
 cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K,

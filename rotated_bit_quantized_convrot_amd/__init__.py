@@ -29,7 +29,7 @@ __all__ = [
     "pack_weight_w4", "pack_weight_int8tw", "pack_weight_w4a8", "pack_weight_int8rot",
     "linear_w4a4", "linear_int8tw", "linear_w4a8", "linear_int8rot",
     "pack_weight_w4_regular", "linear_w4a4_regular",
-    "mlp_workspace_bytes", "mlp_w4a4", "dbg_quant_swiglu",
+    "mlp_workspace_bytes", "mlp_w4a4", "dbg_quant_swiglu", "dbg_silu_mul",
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
@@ -52,7 +52,7 @@ EXPORTS = [
     "cr_pack_weight_int8rot", "cr_linear_int8rot",
     "cr_pack_weight_w4_group", "cr_linear_w4a4_group",
     "cr_pack_weight_w4_regular", "cr_linear_w4a4_regular",
-    "cr_mlp_workspace_bytes", "cr_mlp_w4a4", "cr_dbg_quant_swiglu",
+    "cr_mlp_workspace_bytes", "cr_mlp_w4a4", "cr_dbg_quant_swiglu", "cr_dbg_silu_mul",
 ]
 
 
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
         "cr_mlp_workspace_bytes": (sz, [i, i, i, i]),
         "cr_mlp_w4a4": (i, [vp, i, i, vp, vp, vp, vp, i, vp, vp, i, vp, vp, sz, vp]),
         "cr_dbg_quant_swiglu": (i, [vp, vp, i, i, vp, vp, vp]),
+        "cr_dbg_silu_mul": (i, [vp, vp, sz, vp, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
@@ -328,6 +329,17 @@ def dbg_quant_swiglu(g: torch.Tensor, u: torch.Tensor):
     scales = torch.empty(max(M, 1), dtype=torch.float32, device=g.device)
     _check(lib().cr_dbg_quant_swiglu(_ptr(g), _ptr(u), M, K, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales[:M]
+
+
+def dbg_silu_mul(g: torch.Tensor, u: torch.Tensor) -> torch.Tensor:
+    """h = silu(g) * u (bf16, same shape), as the MLP block forms it."""
+    _dev(g, "g", torch.bfloat16)
+    _dev(u, "u", torch.bfloat16)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    h = torch.empty_like(g)
+    _check(lib().cr_dbg_silu_mul(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream()))
+    return h
 
 
 # ---------------------------------------------------------------------------

@@ -277,6 +277,17 @@ cr_status cr_mlp_w4a4(const void* x_bf16, int M, int K, const void* wg_packed, c
     return gemm_phase(CR_W4A4, M, F, wd_packed, wd_scale, N, nullptr, y_bf16, nullptr, wb, lb.total, stream);
 }
 
+cr_status cr_dbg_silu_mul(const void* g_bf16, const void* u_bf16, size_t n, void* h_bf16, hipStream_t stream) {
+    if (n == 0) return ok();
+    if (!g_bf16 || !u_bf16 || !h_bf16) return fail(CR_ERR_NULL, "NULL argument");
+    if (n > ((size_t)1 << 40)) return fail(CR_ERR_SHAPE, "n=%zu too large", n);
+    cr_status s;
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::launch_silu_mul(static_cast<const uint16_t*>(g_bf16), static_cast<const uint16_t*>(u_bf16), n,
+                                          static_cast<uint16_t*>(h_bf16), stream),
+                      "silu product");
+}
+
 cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int K, void* codes, float* scales,
                               hipStream_t stream) {
     cr_status s;

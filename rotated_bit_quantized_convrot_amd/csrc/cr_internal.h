@@ -71,6 +71,9 @@ hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K
 hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
                                int32_t* ra, bool packed, hipStream_t st);
 
+// h = silu(g) * u of n bf16 pairs, as launch_quant_swiglu forms it.
+hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, size_t n, uint16_t* h, hipStream_t st);
+
 // W4 weight with the rotation `group` (as for launch_quant_act).
 hipError_t launch_pack_w4(const uint16_t* w, int N, int K, int group, uint8_t* out, float* scale,
                           hipStream_t st);

@@ -460,6 +460,20 @@ hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K
     return hipGetLastError();
 }
 
+// h = silu(g) * u element by element (bf16 in, bf16 out), the values the
+// MLP block's quantiser forms (inspection).
+__global__ void __launch_bounds__(256) k_silu_mul(const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
+                                                  size_t n, uint16_t* __restrict__ h) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) h[i] = (uint16_t)(__float_as_uint(silu_mul_bf16(bf16_to_f32(g[i]), bf16_to_f32(u[i]))) >> 16);
+}
+
+hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, size_t n, uint16_t* h, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    k_silu_mul<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(g, u, n, h);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
                                int32_t* ra, bool packed, hipStream_t st) {
     if (packed && ra == nullptr) return hipErrorInvalidValue;

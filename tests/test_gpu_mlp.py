@@ -89,3 +89,30 @@ def test_mlp_block_repeat_and_m_zero(crp):
     y0 = crp.mlp_w4a4(x[:0], pg, sg, pu, su, F, pd, sd, N)
     _sync()
     assert torch.equal(y1, y2) and y0.shape == (0, N)
+
+
+def test_silu_mul_bits_including_fallback_cases(crp):
+    """h = silu(g) * u bit-exact against the oracle, on random values and on
+    the hard ones: values whose float64 result lies near a bf16 rounding
+    midpoint (picked from 4e6 random pairs by the oracle's own value), |g|
+    beyond the float32 range of exp(-g), and tiny results."""
+    rng = np.random.default_rng(23)
+    g = si.f32_to_bf16_bits((rng.standard_t(3, size=4_000_000) * 3).astype(np.float32))
+    u = si.f32_to_bf16_bits(rng.standard_normal(4_000_000).astype(np.float32))
+    g64 = O.bf16_to_f32(g).astype(np.float64)
+    u64 = O.bf16_to_f32(u).astype(np.float64)
+    with np.errstate(over="ignore"):
+        h32 = (g64 / (1.0 + np.exp(-g64)) * u64).astype(np.float32)
+    lo = h32.view(np.uint32) & 0xFFFF
+    # within 2048 float32 ulps of a bf16 rounding midpoint
+    near = np.nonzero(np.abs(lo.astype(np.int64) - 0x8000) <= 2048)[0][:100_000]
+    big = si.f32_to_bf16_bits(np.array([65.0, -65.0, 88.0, -88.5, -90.0, -100.0, -103.0, -150.0, 300.0, -800.0],
+                                       np.float32))
+    tiny_u = si.f32_to_bf16_bits(np.array([1e-30, -3e-38, 1e-39, 2.0, 0.5, -1.0, 1e-38, 7.0, 1.0, 1.0], np.float32))
+    gs = np.concatenate([g[:200_000], g[near], big, big])
+    us = np.concatenate([u[:200_000], u[near], tiny_u, u[:10]])
+    assert len(near) > 1000
+    h = crp.dbg_silu_mul(to_dev_bf16(gs), to_dev_bf16(us))
+    _sync()
+    got = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, O.silu_mul_bf16(gs, us))
