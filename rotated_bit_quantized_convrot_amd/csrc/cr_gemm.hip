@@ -743,15 +743,14 @@ static hipError_t launch_big_bn(const GemmArgs& a, const BigPlan& bp, hipStream_
     using C = BigCfg<WK, BIG_NW, NS, BN>;
     const int tiles_m = (a.M + BIG_BM - 1) / BIG_BM, tiles_n = (a.N + BN - 1) / BN;
     if (bp.splits > 1 && a.part == nullptr) return hipErrorInvalidValue;
-    // opt in to more than 64 KiB of dynamic LDS (once per process and kernel)
-    static bool attr_set[2] = {false, false};
+    // opt in to more than 64 KiB of dynamic LDS (once per device and kernel)
+    static std::atomic<uint64_t> lds_done[2];
     const bool split = bp.splits > 1;
-    if (!attr_set[split]) {
+    {
         const void* k = split ? reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, BN, ACC, true>)
                               : reinterpret_cast<const void*>(&k_gemm_big<WK, BIG_NW, NS, BN, ACC, false>);
-        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+        hipError_t e = opt_in_lds(k, (int)C::LDS, lds_done[split]);
         if (e != hipSuccess) return e;
-        attr_set[split] = true;
     }
     const int units = tiles_m * tiles_n * bp.splits;
     const int grid = min(units, num_cus());

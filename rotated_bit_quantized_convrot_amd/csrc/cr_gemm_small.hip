@@ -370,13 +370,11 @@ static hipError_t launch_small_c(const GemmArgs& a, const SmallPlan& sp, hipStre
         return hipErrorInvalidValue;            // never planned
     } else {
     auto kern = &k_gemm_small<WK, MT, NT, CPW>;
-    static bool attr_set = false;
-    if (!attr_set) {
+    static std::atomic<uint64_t> lds_done;
+    {
         const int lds = SM_W * NT * MT * 1024 + (WK == WK_W4A8 ? 4096 : 0);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipError_t e = opt_in_lds(reinterpret_cast<const void*>(kern), lds, lds_done);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int acc_mode = a.acc_out != nullptr ? 1 : 0;
     kern<<<dim3(sp.nblk, sp.splits), dim3(64 * SM_W), sp.lds, st>>>(a, sp.splits, sp.cps, acc_mode);

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace cr {
 
 // W4A4 rotation selector for the group-256 regular Hadamard (J - 2I)^(x4) / 16,
@@ -145,5 +147,19 @@ inline size_t act_bytes(int kind, int M, int K) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+// Opts `kernel` in to `bytes` of dynamic LDS (beyond the default 64 KiB) on
+// the current device, once per device: `done` holds one bit per device id
+// (ids past 63 set the attribute on every call).
+inline hipError_t opt_in_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_relaxed) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
 
 }  // namespace cr

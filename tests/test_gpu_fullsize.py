@@ -179,3 +179,22 @@ def test_mlp_block_full_size(crp, M):
     got = y.index_select(0, torch.from_numpy(rows).cuda())
     assert max_rel_err(bf16_dev_to_f32(got), ref_y) <= TOL
     assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(ref_y))
+
+
+def test_w4a4_very_large_m(crp):
+    """M = 131071 (512 row tiles, ragged last one): workspace and tile
+    arithmetic far past the benchmark shapes; sampled rows checked."""
+    print("[fullsize] very large M", flush=True)
+    M, K, N = 131071, 256, 96
+    L = si.random_layer(M, K, N, seed=77, bias=True, outlier_count=4)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    ws = torch.empty(crp.workspace_bytes(0, M, N, K), dtype=torch.uint8, device="cuda")
+    y = crp.linear_w4a4(x, p, s, N, to_dev_bf16(L.bias), workspace=ws)
+    acc = crp.dbg_linear_acc(0, x, p, N, workspace=ws)
+    torch.cuda.synchronize()
+    rows = _rows(M, n=48, seed=3)
+    qw, sw = O.quant_weight_w4(L.w)
+    qx, sx = O.quant_act_w4a4(L.x[rows])
+    ref_acc = O.int_gemm(qx, qw)
+    _check(y, acc, rows, ref_acc, O.epilogue(ref_acc, sx, sw, L.bias))
