@@ -225,6 +225,18 @@ def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Ten
 # Linears
 # ---------------------------------------------------------------------------
 
+def _check_weight(kind: int, packed, scale, N: int, K: int):
+    """Refuse packed weights and scales smaller than the layout of (kind, N,
+    K) needs: the kernels would read past their end.  (Shapes the library
+    rejects give 0 bytes here and are left to its own error.)"""
+    need = packed_bytes(kind, N, K)
+    if need and packed.numel() < need:
+        raise ValueError(f"packed weight has {packed.numel()} bytes, kind {kind} N={N} K={K} needs {need}")
+    per_row = kind in (W4A8, INT8ROT)
+    if scale is not None and scale.numel() < (N if per_row else 1):
+        raise ValueError(f"scale has {scale.numel()} values, needs {N if per_row else 1}")
+
+
 def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace, group=None):
     _dev(x, "x", torch.bfloat16)
     _dev(packed, "packed", torch.uint8)
@@ -232,6 +244,7 @@ def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace, 
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
     M, K = x.shape
+    _check_weight(kind, packed, scale, N, K)
     if bias is not None:
         _dev(bias, "bias", torch.bfloat16)
         if bias.numel() != N:
@@ -303,6 +316,9 @@ def mlp_w4a4(x, wg, sg, wu, su, F, wd, sd, N, out=None, workspace=None):
     for t, n in ((sg, "sg"), (su, "su"), (sd, "sd")):
         _dev(t, n, torch.float32)
     M, K = x.shape
+    _check_weight(W4A4, wg, sg, F, K)
+    _check_weight(W4A4, wu, su, F, K)
+    _check_weight(W4A4, wd, sd, N, F)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     else:
@@ -359,6 +375,7 @@ def gemm_quantized(kind: int, M: int, K: int, packed, scale, N: int, workspace, 
     """GEMM + epilogue from a workspace filled by :func:`quantize_activations`."""
     _dev(packed, "packed", torch.uint8)
     _dev(scale, "scale", torch.float32)
+    _check_weight(kind, packed, scale, N, K)
     _dev(workspace, "workspace", torch.uint8)
     if bias is not None:
         _dev(bias, "bias", torch.bfloat16)
@@ -388,6 +405,7 @@ def dbg_quant_act(kind: int, x: torch.Tensor):
 def dbg_unpack_weight(kind: int, packed: torch.Tensor, N: int, K: int):
     """Canonical int8 weight codes [N,K] held by a packed weight."""
     _dev(packed, "packed", torch.uint8)
+    _check_weight(kind, packed, None, N, K)
     codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
     _check(lib().cr_dbg_unpack_weight(kind, _ptr(packed), N, K, _ptr(codes), _stream()))
     return codes
@@ -397,6 +415,7 @@ def dbg_linear_acc(kind: int, x: torch.Tensor, packed: torch.Tensor, N: int, wor
     """int32 accumulators [M,N] of the linear `kind`."""
     _dev(x, "x", torch.bfloat16)
     _dev(packed, "packed", torch.uint8)
+    _check_weight(kind, packed, None, N, x.shape[1])
     M, K = x.shape
     acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
     need = max(workspace_bytes(kind, M, N, K), 256)

@@ -444,3 +444,24 @@ def test_two_phase_large_m(crp):
     y2 = crp.gemm_quantized(1, M, K, p, s, N, ws)
     _sync()
     assert torch.equal(y, y2)
+
+
+def test_short_packed_weight_or_scale_raises(crp):
+    """The binding refuses packed weights and scales smaller than the layout
+    needs, before anything is launched."""
+    M, K, N = 8, 512, 64
+    L = si.random_layer(M, K, N, seed=12)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    with pytest.raises(ValueError, match="packed weight"):
+        crp.linear_w4a4(x, p[:-16], s, N)
+    with pytest.raises(ValueError, match="packed weight"):
+        crp.linear_w4a4(x, p, s, N + 32)
+    pr, sr = crp.pack_weight_int8rot(to_dev_bf16(L.w))
+    with pytest.raises(ValueError, match="scale"):
+        crp.linear_int8rot(x, pr, sr[: N // 2], N)
+    ws = torch.empty(crp.workspace_bytes(0, M, N, K), dtype=torch.uint8, device="cuda")
+    crp.quantize_activations(0, x, ws)
+    with pytest.raises(ValueError, match="packed weight"):
+        crp.gemm_quantized(0, M, K, p[:100], s, N, ws)
+    _sync()
