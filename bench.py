@@ -308,7 +308,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(the linear would shard by rows with no communication); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
