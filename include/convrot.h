@@ -5,7 +5,7 @@
  *   [QIE] "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4 (+ConvRot, mixed int8
  *         fallback)", intro and "Speed" table: weights stored as packed signed
  *         INT4, two per byte, rotated offline with a group-256 Hadamard
- *         (ConvRot); activations rotated online and quantised to INT4
+ *         (ConvRot); the activations are rotated and quantised to INT4 at run time
  *         dynamically inside the kernel; integer MMA with a rank-one rescale.
  *   [REB] "Rebels_w4a8s", "What's inside a file" and "Mixed formats where the
  *         kernel demands it": the W4A8 codebook format (int4 codebook indices,
@@ -93,7 +93,7 @@ size_t cr_packed_bytes(int kind, int N, int K);
  * need no initialisation and are meaningless after the call. */
 size_t cr_workspace_bytes(int kind, int M, int N, int K);
 
-/* ---- W4A4 ConvRot ([QIE] intro; "Speed": fused ConvRot + rank-one s4 MMA) */
+/* ---- W4A4 ConvRot ([QIE] intro; "Speed": one kernel for the rotation, the s4 MMA and the rank-one rescale) */
 
 /* Offline weight preparation: rotate each 256-block of every row of W,
  * s_w = absmax(rotated W) / 7, codes = clamp(rint(v / s_w), -8, 7), written

@@ -12,18 +12,20 @@ reordered.
 Sources (web pages; cited by title and section):
 
 * [QIE]  "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4 (+ConvRot, mixed int8
-         fallback)" model card: intro paragraph (packed signed INT4, 2/byte,
-         group-256 regular-Hadamard ConvRot, online activation rotation,
-         dynamic INT4 activations, calibration-free); "Speed" table (fused
-         ConvRot + rank-one s4 MMA kernel; int8_tensorwise kernels).
+         fallback)" model card: intro paragraph (signed 4-bit weight codes
+         two to a byte, a group-256 Hadamard rotation named "regular",
+         activations rotated and quantised to 4 bits per row at run time,
+         no calibration); "Speed" table (one kernel for the rotation, the
+         s4 MMA and the rank-one rescale; int8_tensorwise kernels).
 * [Q3N]  "qwen3-4b-nvfp4-convrot" asset page: file table and converter
          flags (ConvRot INT8 row-scaled, group size 256).
 * [QVL]  "Qwen3-VL-4B-W4A8-ConvRot" model page: file table
          (asym_w4a8_int8, group 16, convrot_groupsize 256).
-* [REB]  "Rebels_w4a8s" collection page: "What's inside a file" table (int4
-         codes two per byte, fp8 scale per group of 16, one scale per output
-         channel, 16 Lloyd-Max levels); "Mixed formats where the kernel
-         demands it" (group exactly 256, int8_tensorwise for other widths);
+* [REB]  "Rebels_w4a8s" collection page: "What's inside a file" table (4-bit
+         codebook indices two to a byte, an fp8 scale for each 16 weights, a
+         scale for each output row, a 16-level Lloyd-Max codebook); "Mixed
+         formats where the kernel demands it" (the W4 kernel takes only
+         groups of 256, int8_tensorwise covers other widths);
          "Why W4A8 instead of GGUF" (int8 GEMM, ~0.56 B/param, ~7% weight
          error).
 * [ZIT]  "Z-Image-Turbo-W4A4-ConvRot" model card: "Where Z-Image sits"
@@ -528,8 +530,9 @@ def w4a8_decode(idx: np.ndarray, s_rel: np.ndarray, codebook: np.ndarray) -> np.
 
 def linear_w4a8(x_bits, idx_packed, s_rel, codebook, s_channel, bias_bits=None,
                 group: int = GROUP):
-    """Asym W4A8 codebook linear ([REB] "int8 tensor cores do the work",
-    "keeps compute in int8 end to end"; reading R8)."""
+    """Asym W4A8 codebook linear ([REB] "Why W4A8 instead of GGUF": the GEMM
+    runs on the int8 matrix units with no dequantisation to a float type;
+    reading R8)."""
     qx, sx = quant_act_w4a8(x_bits, group)
     w8 = w4a8_decode(unpack_uint4(idx_packed), s_rel, codebook)
     acc = int_gemm(qx, w8)

@@ -2,7 +2,7 @@
 //
 // acc[m,n] = sum_k qx[m,k] * qw[n,k] (exact int32), then
 // y[m,n] = bf16(fl(fl(float(acc) * s_x[m]) * s_w) + bias[n])
-// ([QIE] model card, "Speed" table: fused ConvRot + rank-one s4 MMA kernel;
+// ([QIE] model card, "Speed" table: one kernel for the rotation, the s4 MMA and the rank-one rescale;
 // [REB] "Why W4A8 instead of GGUF": the W4A8 weights stay 4-bit in memory and
 // the math is int8).  CDNA4 has no int4 MFMA, so 4-bit codes are widened to
 // int8 in registers: W4A4 weights and activations by one AND per dword (two

@@ -2,7 +2,7 @@
 //
 // Rotation + per-row dynamic quantisation of activations, tensorwise weight
 // quantisation and packing ([QIE] model card intro: group-256 Hadamard
-// ConvRot, activations rotated online and quantised to INT4 in the kernel,
+// ConvRot; the activations are rotated and quantised to INT4 at run time inside the kernel,
 // weights packed signed INT4 two per byte; [REB] "What's inside a file" for
 // the W4A8 tensors).
 #include "cr_device.h"
