@@ -89,8 +89,9 @@ size_t cr_packed_bytes(int kind, int N, int K);
 
 /* Bytes of workspace cr_linear_* / cr_dbg_linear_acc need for these sizes
  * (0 on bad args; at least 256 otherwise).  The workspace holds the
- * quantised activations, their scales and split-K partial sums; its contents
- * need no initialisation and are meaningless after the call. */
+ * quantised activations, their scales and split-K partial sums (and, for
+ * W4A8 from M = 2048 on, the weight decoded to int8 for that call); its
+ * contents need no initialisation and are meaningless after the call. */
 size_t cr_workspace_bytes(int kind, int M, int N, int K);
 
 /* ---- W4A4 ConvRot ([QIE] intro; "Speed": one kernel for the rotation, the s4 MMA and the rank-one rescale) */

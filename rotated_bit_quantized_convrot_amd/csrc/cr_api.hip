@@ -110,19 +110,31 @@ int wkind(int kind) {
 // against several weights (with the workspace sized for the largest need
 // over their N).
 struct WsLayout {
-    size_t qx, sx, ra, part, quant_end, total;
+    size_t qx, sx, ra, part, wexp, quant_end, total;
 };
+
+// W4A8 at large M: the GEMM's per-16-weight table decode is the costly part
+// of its inner loop, so the weight is first decoded once into the int8 tile
+// layout (in the workspace) and the int8 GEMM with per-column scales runs on
+// it; the decoded values and so the accumulators are the same.  Pays off
+// from about M = 1300 at the W4A8 layer (K = 3840, N = 10240: 216.7 -> 178.2
+// us for the GEMM, ~10 us for the decode pass); taken from M = 2048 on.
+bool w4a8_expands(int kind, int M) { return kind == CR_W4A8 && M >= 2048; }
+
+// The GEMM kernels' format for this call.
+int gemm_wkind(int kind, int M) { return w4a8_expands(kind, M) ? cr::WK_I8R : wkind(kind); }
 
 WsLayout ws_layout(int kind, int M, int N, int K) {
     WsLayout l{};
-    const int wk = wkind(kind);
+    const int wk = wkind(kind), gk = gemm_wkind(kind, M);
     l.qx = 0;
     l.sx = a256(cr::act_bytes(wk, M, K));
     l.ra = l.sx + a256((size_t)M * 4);
     l.part = l.ra + (cr::act_packed(wk) ? a256((size_t)M * 4) : 0);
     l.quant_end = l.part;
-    const cr::SmallPlan sp = cr::plan_small(wk, M, N, K);
-    l.total = l.part + a256(sp.use ? sp.part_bytes : cr::plan_big(wk, M, N, K).part_bytes);
+    const cr::SmallPlan sp = cr::plan_small(gk, M, N, K);
+    l.wexp = l.part + a256(sp.use ? sp.part_bytes : cr::plan_big(gk, M, N, K).part_bytes);
+    l.total = l.wexp + (w4a8_expands(kind, M) ? a256(cr::i8_bytes(N, K)) : 0);
     if (l.total < 256) l.total = 256;
     if (l.quant_end < 256) l.quant_end = 256;
     return l;
@@ -158,8 +170,15 @@ cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale
     if (ws_bytes < l.total)
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
     char* w = static_cast<char*>(ws);
+    if (w4a8_expands(kind, M)) {
+        cr_status s = launch_err(cr::launch_w4a8_expand(static_cast<const uint8_t*>(wp), N, K,
+                                                        reinterpret_cast<uint8_t*>(w + l.wexp), st),
+                                 "W4A8 weight decode");
+        if (s != CR_OK) return s;
+        wp = w + l.wexp;
+    }
     cr::GemmArgs a{};
-    a.kind = wkind(kind);
+    a.kind = gemm_wkind(kind, M);
     a.qx = reinterpret_cast<const int8_t*>(w + l.qx);
     a.sx = reinterpret_cast<const float*>(w + l.sx);
     a.M = M; a.N = N; a.K = K; a.Kp = kp_of(kind, K); a.Np = cr::round_up(N, 32);

@@ -86,6 +86,9 @@ hipError_t launch_pack_i8rot(const uint16_t* w, int N, int K, uint8_t* out, floa
                              hipStream_t st);
 hipError_t launch_pack_w4a8(const uint8_t* idx, const uint8_t* s_rel, const float* cb, int N,
                             int K, uint8_t* out, hipStream_t st);
+// A packed W4A8 weight decoded into the int8 tile layout (i8_bytes(N, K)
+// bytes at `out`; K % 256 == 0), for the int8 GEMM with per-column scales.
+hipError_t launch_w4a8_expand(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st);
 hipError_t launch_unpack_weight(int kind, const uint8_t* packed, int N, int K, int8_t* out,
                                 hipStream_t st);
 

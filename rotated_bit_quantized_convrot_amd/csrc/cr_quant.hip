@@ -768,6 +768,48 @@ hipError_t launch_pack_w4a8(const uint8_t* idx, const uint8_t* s_rel, const floa
     return hipGetLastError();
 }
 
+// --- W4A8 expanded to the int8 tile layout (per call, large M) ------------
+// One thread per 16-byte segment (row n, 64-k chunk, half h, step t) of the
+// int8 layout: the 16 indices k0 + 0..15 (k0 = 64 kc + 32 t + 16 h) decoded
+// through the decode table with their group's scale code, exactly the
+// values the W4A8 GEMM decodes in registers.  Padding rows get zeros.
+__global__ void __launch_bounds__(256) k_w4a8_expand(const uint8_t* __restrict__ p, int N, int K, size_t codes_off,
+                                                     size_t table_off, uint8_t* __restrict__ out, size_t nseg) {
+    __shared__ uint32_t tab[1024];
+    for (int i = threadIdx.x; i < 1024; i += blockDim.x)
+        tab[i] = reinterpret_cast<const uint32_t*>(p + table_off)[i];
+    __syncthreads();
+    const size_t seg = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (seg >= nseg) return;
+    const size_t tile = seg >> 7;                 // 128 segments of 16 B per 2 KiB tile
+    const int within = (int)(seg & 127);
+    const int r = within >> 2, h = (within >> 1) & 1, t = within & 1;
+    const int nkc = K >> 6;
+    const int n = (int)(tile / nkc) * 32 + r;
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (n < N) {
+        const uint2 src = *reinterpret_cast<const uint2*>(p + tile * 1024 + r * 32 + 16 * h + 8 * t);
+        const uint32_t code = p[codes_off + tile * 128 + r * 4 + 2 * t + h];
+        const uint8_t* row = reinterpret_cast<const uint8_t*>(tab) + code * 16;
+#pragma unroll
+        for (int pp = 0; pp < 16; ++pp) {
+            const int d = pp >> 3, b = pp & 3, hi = (pp >> 2) & 1;
+            const uint32_t word = d ? src.y : src.x;
+            const uint32_t byte = (word >> (8 * b)) & 0xFFu;
+            const uint32_t nib = hi ? (byte >> 4) : (byte & 0xFu);
+            o[pp >> 2] |= (uint32_t)row[nib] << (8 * (pp & 3));
+        }
+    }
+    *reinterpret_cast<uint4*>(out + tile * 2048 + r * 64 + 32 * h + 16 * t) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_w4a8_expand(const uint8_t* packed, int N, int K, uint8_t* out, hipStream_t st) {
+    const size_t nseg = (size_t)round_up(N, 32) * K / 16;
+    k_w4a8_expand<<<dim3((unsigned)((nseg + 255) / 256)), dim3(256), 0, st>>>(
+        packed, N, K, w4a8_codes_offset(N, K), w4a8_table_offset(N, K), out, nseg);
+    return hipGetLastError();
+}
+
 // --- canonical weight codes (inspection) ---------------------------------
 
 __global__ void __launch_bounds__(256) k_unpack_weight(int kind, const uint8_t* __restrict__ p, int N,

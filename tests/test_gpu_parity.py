@@ -257,7 +257,9 @@ def test_int8tw_acc_and_output(crp, M, K, N):
     assert max_rel_err(bf16_dev_to_f32(y), r["y"]) <= TOL
 
 
-@pytest.mark.parametrize("M,K,N", [(64, 512, 256), (76, 768, 96), (200, 512, 160), (3, 256, 33)])
+@pytest.mark.parametrize("M,K,N", [(64, 512, 256), (76, 768, 96), (200, 512, 160), (3, 256, 33),
+                                   # M >= 2048: weight decoded to int8 per call, int8 GEMM
+                                   (2050, 512, 160), (2048, 1024, 300)])
 def test_w4a8_acc_and_output(crp, M, K, N):
     L = si.random_layer(M, K, N, seed=M + K + N * 11, bias=True)
     enc = O.w4a8_encode(L.w)
