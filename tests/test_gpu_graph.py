@@ -72,3 +72,31 @@ def test_graph_mlp_block_and_rotation_variants():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(ym, ref[0]) and torch.equal(y64, ref[1]) and torch.equal(yrh, ref[2]), f"replay {i}"
+
+
+def test_graph_w4a8_large_m_decode_route():
+    """W4A8 at M >= 2048 (weight decoded into the workspace, then the int8
+    GEMM) under capture: every replay equals eager."""
+    import rotated_bit_quantized_convrot_amd as crp
+    from tests._util import to_dev
+    M, K, N = 2048, 512, 320
+    L = si.random_layer(M, K, N, seed=31, bias=True)
+    idx, s_rel, cb, s_ch = si.random_w4a8_format(N, K, seed=5)
+    p = crp.pack_weight_w4a8(to_dev(idx), to_dev(s_rel), to_dev(cb), N, K)
+    sch = to_dev(s_ch)
+    x = to_dev_bf16(L.x)
+    b = to_dev_bf16(L.bias)
+    ws = torch.empty(crp.workspace_bytes(2, M, N, K), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ref = crp.linear_w4a8(x, p, sch, N, b).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        crp.linear_w4a8(x, p, sch, N, b, out=y, workspace=ws)
+    for i in range(4):
+        y.zero_()
+        ws.fill_(0x5A)                                  # the decoded copy must be rebuilt each replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {i}"
