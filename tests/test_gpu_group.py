@@ -164,3 +164,48 @@ def test_group_sizes_differ_and_bad_group_raises(crp):
     p, s = crp.pack_weight_w4(to_dev_bf16(L.w), group=64)
     with pytest.raises(crp.ConvRotError, match="CR_ERR_GROUP"):
         crp.linear_w4a4(x, p, s, 32, group=128)
+
+
+def _subnormal_rows(K, seed):
+    """Rows of the smallest bf16 subnormals (one +-2^-133, all-subnormal
+    random rows, a sparse mix), where the scales are fp32 subnormals too."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for sign in (0x0000, 0x8000):
+        r = np.zeros(K, np.uint16)
+        r[3] = sign | 0x0001
+        rows.append(r)
+    rows.append((rng.integers(1, 128, K) | (rng.integers(0, 2, K) << 15)).astype(np.uint16))
+    r = np.zeros(K, np.uint16)
+    r[::7] = 0x8001
+    r[5] = 0x007F
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("kind", [0, 4, 5, 6])
+@pytest.mark.parametrize("M,K", [(4, 512), (36, 3072), (2052, 512)])
+def test_subnormal_rows_quant_act_bitexact(crp, kind, M, K):
+    """Activation codes and scales of subnormal-only rows, every rotation,
+    across the quantiser's row layouts; the codes stay in [-7, 7]."""
+    base = _subnormal_rows(K, seed=M + K + kind)
+    x = np.tile(base, ((M + 3) // 4, 1))[:M]
+    q, s = crp.dbg_quant_act(kind, to_dev_bf16(x))
+    _sync()
+    q_ref, s_ref = O.quant_act_w4a4_regular(x) if kind == 6 else O.quant_act_w4a4(x, {0: 256, 4: 64, 5: 16}[kind])
+    qn = q.cpu().numpy()
+    assert np.array_equal(qn, q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert qn.min() >= -7 and qn.max() <= 7
+
+
+@pytest.mark.parametrize("G", [256, 64, 16])
+def test_subnormal_weight_pack_bitexact(crp, G):
+    """A weight of subnormal bf16 values only: tensor scale and codes."""
+    w = np.tile(_subnormal_rows(512, seed=G), (9, 1))[:33]
+    p, s = crp.pack_weight_w4(to_dev_bf16(w), group=G)
+    codes = crp.dbg_unpack_weight({256: 0, 64: 4, 16: 5}[G], p, 33, 512)
+    _sync()
+    q_ref, s_ref = O.quant_weight_w4(w, G)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    assert s.cpu().numpy()[:1].view(np.uint32)[0] == np.float32(s_ref).view(np.uint32)

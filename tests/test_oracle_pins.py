@@ -149,6 +149,46 @@ def test_quant_invariants():
     assert np.all(np.max(np.abs(q8.astype(np.int32)), axis=1) == 127)
 
 
+def test_w4_codes_never_reach_minus_8_on_bf16_inputs():
+    """The clip bound -8 is never reached from bf16 inputs, however small.
+
+    A nonzero rotated bf16 value is a multiple of 2^-137 (bf16's smallest
+    subnormal is 2^-133 and every rotation divides by at most 16), so the
+    scale amax / 7 >= 2^-139.8 keeps at least nine significant bits and
+    |v / s| <= 7 (1 + 2^-9) < 7.5 before rounding.  Rows of the smallest
+    bf16 subnormals, with every rotation, stay in [-7, 7]; the same
+    quantiser on raw fp32 subnormals (below that grid) does give -8, so the
+    check is not vacuous."""
+    rng = np.random.default_rng(17)
+    K = 512
+    rows = []
+    for sign in (0x0000, 0x8000):
+        r = np.zeros(K, np.uint16)
+        r[3] = sign | 0x0001                                   # one +-2^-133
+        rows.append(r)
+    rows.append((rng.integers(1, 128, K) | (rng.integers(0, 2, K) << 15)).astype(np.uint16))   # all subnormal
+    r = np.zeros(K, np.uint16)
+    r[::7] = 0x8001
+    r[5] = 0x007F
+    rows.append(r)
+    x = np.stack(rows)
+    cases = [O.quant_act_w4a4(x, g) for g in (256, 64, 16)] + [O.quant_act_w4a4_regular(x)]
+    for q, sc in cases:
+        assert q.min() >= -7 and q.max() <= 7
+        assert np.all(sc > 0)
+    vs = O.fwht(O.bf16_to_f32(x)).astype(np.float64)
+    _, sx = O.quant_act_w4a4(x)
+    assert np.max(np.abs(vs / sx.astype(np.float64)[:, None])) < 7.5
+    for g in (256, 64, 16):
+        qw, sw = O.quant_weight_w4(x, g)
+        assert qw.min() >= -7 and qw.max() <= 7 and sw > 0
+    # raw fp32 subnormals: amax = 10 ulps, s = fl(10/7 ulp) = 1 ulp, v / s = -10
+    tiny = np.zeros((1, 8), np.float32)
+    tiny[0, 2] = -np.float32(10 * 2.0 ** -149)
+    q, sc = O.quant_rows(tiny, 7, -8, 7)
+    assert sc[0] == np.float32(2.0 ** -149) and q[0, 2] == -8
+
+
 def test_pack_roundtrip():
     rng = np.random.default_rng(1)
     q = rng.integers(-8, 8, size=(7, 64)).astype(np.int8)
