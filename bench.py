@@ -305,6 +305,9 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the headline GEMM 5 times and a 512 MiB device copy 5 times "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs), then exit")
+    ap.add_argument("--traffic-row", default="dit_w1",
+                    help="row whose GEMM --traffic-probe launches (a cold row uses a different weight "
+                         "copy for each of the 5 launches)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -328,18 +331,22 @@ def main():
     head = Layer(crp, torch, Lh, 0)
 
     if args.traffic_probe:
-        head.quant()
-        for _ in range(5):
-            head.gemm()
+        probe = head
+        if args.traffic_row != "dit_w1":
+            spec = specs[args.traffic_row]
+            probe = Layer(crp, torch, spec["gen"](), spec["kind"], copies=5 if spec["cold"] else 1)
+        probe.quant()
+        for i in range(5):
+            probe.gemm(i % len(probe.packed))
         torch.cuda.synchronize()
         src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": True, "gemm_launches": 5, "copy_launches": 5,
-                          "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
-                          "gemm_algorithmic_bytes": head.gemm_bytes()}), flush=True)
+        print(json.dumps({"traffic_probe": True, "row": args.traffic_row, "gemm_launches": 5,
+                          "copy_launches": 5, "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                          "gemm_algorithmic_bytes": probe.gemm_bytes()}), flush=True)
         return
 
     # --- headline: K timed steps of the whole linear -----------------------
