@@ -305,7 +305,7 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the headline GEMM 5 times and a 512 MiB device copy 5 times "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs), then exit")
-    ap.add_argument("--traffic-row", default="dit_w1",
+    ap.add_argument("--traffic-row", default="dit_w1", choices=sorted(row_specs()),
                     help="row whose GEMM --traffic-probe launches (a cold row uses a different weight "
                          "copy for each of the 5 launches)")
     args = ap.parse_args()
