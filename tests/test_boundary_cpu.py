@@ -175,3 +175,24 @@ def test_mlp_sizes_and_errors(L):
     assert L.cr_mlp_w4a4(vp, M, K, None, vp, vp, vp, F, vp, vp, N, vp, vp, 1 << 30, None) == CR["NULL"]
     assert L.cr_mlp_w4a4(vp, M, K, vp, vp, vp, vp, F, vp, vp, N, vp, vp, 16, None) == CR["WORKSPACE"]
     assert L.cr_dbg_quant_swiglu(vp, vp, 4, 300, vp, vp, None) == CR["GROUP"]
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises; there is no fallback."""
+    import rotated_bit_quantized_convrot_amd as crp
+    monkeypatch.setattr(crp, "_LIB", None)
+    monkeypatch.setattr(crp, "_LIB_PATH", str(tmp_path / "libconvrot.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        crp.lib()
+
+
+def test_host_tensors_are_refused():
+    """Host (CPU) tensors are rejected before any call: nothing computes on the CPU."""
+    torch = pytest.importorskip("torch")
+    import rotated_bit_quantized_convrot_amd as crp
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    w = torch.zeros((32, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        crp.pack_weight_w4(w)
+    with pytest.raises(ValueError, match="device tensor"):
+        crp.linear_w4a4(x, torch.zeros(1, dtype=torch.uint8), torch.ones(1), 32)
