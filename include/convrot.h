@@ -83,6 +83,10 @@ typedef enum {
 #define CR_MAX_DIM (1 << 20)
 /* Largest K the rotated activation quantiser accepts (W4A4, W4A8, ConvRot INT8). */
 #define CR_MAX_ROT_K 65536
+/* Largest K of int8_tensorwise: its codes reach +-127 on both operands, so
+ * |acc| <= 16129 K, which int32 holds only up to K = 133144 (CR_ERR_SHAPE
+ * beyond this limit). */
+#define CR_MAX_INT8_K 131072
 
 /* Bytes of the packed weight of `kind` for an [N,K] weight (0 on bad args). */
 size_t cr_packed_bytes(int kind, int N, int K);

@@ -32,8 +32,9 @@ Sources (web pages; cited by title and section):
          (convrot_groupsize sweep 256 / 64 / 16; a size-N rotation spreads
          an outlier over N channels).
 
-Readings taken where the pages are silent (each also listed in the design
-notes of the repository):
+Readings taken where the pages are silent (each also listed, under the same
+number, in the design notes of the repository; R11-R16 there concern the
+GPU library's interface and tolerance, not this module's arithmetic):
 
 R1  Hadamard: Sylvester order-256 matrix H[i,j] = (-1)^popcount(i&j), scaled
     by 1/16 so it is orthonormal.  ("regular-Hadamard" read as the standard
@@ -62,30 +63,21 @@ R10 W4A8 encode (offline): s_channel[n] = absmax_k |W~[n,:]| / 127;
     midpoints, levels at the cell means, initialised at the (j+1/2)/16
     quantiles, at most 100 iterations; idx = the cell of u (a value on a
     threshold goes to the lower level).
-R11 Canonical int4 storage: two's complement nibbles, low nibble = even k.
-R12 ConvRot INT8 row-scaled ([Q3N] file table: INT8 with group-256 Hadamard
+R17 ConvRot INT8 row-scaled ([Q3N] file table: INT8 with group-256 Hadamard
     rotation and row-wise scaling; converter flags: int8, row scaling,
     dynamic ConvRot, group 256): the weight is rotated like R2, then
     quantised per output row, s_w[n] = absmax_k |W~[n,k]| / 127, codes
     clip(rint(W~ / s_w[n]), -128, 127); the activations are rotated online
     and quantised per row as in R8; one int32 accumulation over the full K;
     the epilogue takes s_w[n] per output column (as s_channel in R8).
-R13 Smaller rotation groups ([ZIT] "Where Z-Image sits": the sweep over
+R18 Smaller rotation groups ([ZIT] "Where Z-Image sits": the sweep over
     group sizes 256, 64 and 16): the same butterflies as R2 over groups of
     G = 64 or 16 consecutive k (strides 1 .. G/2 ascending), i.e. a
     block-diagonal rotation, then one multiply by 1/sqrt(G) (0.125 or
     0.25, exact); everything after the rotation is R3-R6 unchanged.  K
     stays a multiple of 256 (the layer eligibility rule of [REB] "Mixed
     formats" is kept whatever the group).
-R15 Text-encoder MLP block ([Q3N] file table and the "qwen3vl_4b" page:
-    the decoder blocks' gate_proj, up_proj and down_proj Linears; the
-    pages do not state the activation): the gated MLP of this model family,
-    h = silu(gate(x)) * up(x), silu(v) = v / (1 + exp(-v)), then
-    y = down(h).  Each Linear is the W4A4 linear of R1-R6 (bf16 out, no
-    bias); h is computed from the bf16 g and u in float64, rounded to
-    float32 and then to bf16 (round to nearest even), and enters the down
-    linear as its bf16 input.
-R14 Regular Hadamard ([QIE] intro: "regular-Hadamard" rotation, no
+R19 Regular Hadamard ([QIE] intro: "regular-Hadamard" rotation, no
     construction given): the group-256 matrix (J - 2I)^(x4) / 16, the fourth
     Kronecker power of the 4x4 regular Hadamard matrix J - 2I (every row of
     which sums to 2, so every row of the normalised H sums to 1).  Applied
@@ -95,6 +87,16 @@ R14 Regular Hadamard ([QIE] intro: "regular-Hadamard" rotation, no
     R3-R6 unchanged.  An alternative to R1, not the default.  (The other
     4x4 regular Hadamard matrix, 2I - J = -(J - 2I), gives the same
     256-matrix: the four sign flips cancel.)
+R20 Text-encoder MLP block ([Q3N] file table and the "qwen3vl_4b" page:
+    the decoder blocks' gate_proj, up_proj and down_proj Linears; the
+    pages do not state the activation): the gated MLP of this model family,
+    h = silu(gate(x)) * up(x), silu(v) = v / (1 + exp(-v)), then
+    y = down(h).  Each Linear is the W4A4 linear of R1-R6 (bf16 out, no
+    bias); h is computed from the bf16 g and u in float64, rounded to
+    float32 and then to bf16 (round to nearest even), and enters the down
+    linear as its bf16 input.
+R21 Canonical 4-bit storage: two values per byte, low nibble = even k;
+    signed codes in two's complement, codebook indices unsigned.
 
 Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
 codebooks are correct and the GPU consumes whatever codebook it is given; its
@@ -184,7 +186,7 @@ def fwht(v: np.ndarray, group: int = GROUP, dtype=np.float32) -> np.ndarray:
 
 def regular_hadamard() -> np.ndarray:
     """Closed form of the normalised group-256 regular Hadamard matrix of
-    reading R14 (float64): with A = J - 2I the 4x4 matrix of ones less twice
+    reading R19 (float64): with A = J - 2I the 4x4 matrix of ones less twice
     the identity (every row sums to 2), H[i, j] = prod_d A[i_d, j_d] / 16 over
     the four base-4 digits of i and j.  Every row of H sums to 1."""
     A = np.ones((4, 4)) - 2.0 * np.eye(4)
@@ -197,7 +199,7 @@ def regular_hadamard() -> np.ndarray:
 def rht(v: np.ndarray, dtype=np.float32) -> np.ndarray:
     """Group-256 rotation by the regular Hadamard matrix along the last axis.
 
-    Reading R14: four radix-4 stages over the base-4 digits of the index
+    Reading R19: four radix-4 stages over the base-4 digits of the index
     (strides 1, 4, 16, 64 in that order); a stage replaces the four values
     x0..x3 of a group (index order) by t - 2 x_k with t = (x0 + x1) + (x2 + x3),
     computed in ``dtype``; then one multiply by 1/16 (exact)."""
@@ -276,12 +278,12 @@ def quant_weight_w4(w_bits: np.ndarray, group: int = GROUP):
 # --- int8_tensorwise -------------------------------------------------------
 
 def quant_act_w4a4_regular(x_bits: np.ndarray):
-    """W4A4 activations rotated by the regular Hadamard matrix (R14)."""
+    """W4A4 activations rotated by the regular Hadamard matrix (R19)."""
     return quant_rows(rht(bf16_to_f32(x_bits)), 7, -8, 7)
 
 
 def quant_weight_w4_regular(w_bits: np.ndarray):
-    """W4 weight rotated by the regular Hadamard matrix (R14), tensorwise."""
+    """W4 weight rotated by the regular Hadamard matrix (R19), tensorwise."""
     return quant_tensor(rht(bf16_to_f32(w_bits)), 7, -8, 7)
 
 
@@ -303,7 +305,7 @@ def quant_act_w4a8(x_bits: np.ndarray, group: int = GROUP):
     return quant_rows(xr, 127, -128, 127)
 
 
-# --- ConvRot INT8, row-scaled (reading R12) --------------------------------
+# --- ConvRot INT8, row-scaled (reading R17) --------------------------------
 
 def quant_act_int8rot(x_bits: np.ndarray, group: int = GROUP):
     """ConvRot INT8 activations: group-256 rotation (dynamic ConvRot), then
@@ -320,7 +322,7 @@ def quant_weight_int8rot(w_bits: np.ndarray, group: int = GROUP):
 
 
 # ---------------------------------------------------------------------------
-# Canonical nibble packing (reading R11)
+# Canonical nibble packing (reading R21)
 # ---------------------------------------------------------------------------
 
 def pack_int4(q: np.ndarray) -> np.ndarray:
@@ -413,7 +415,7 @@ def linear_w4a4(x_bits, w_bits, bias_bits=None, group: int = GROUP):
 
 
 def linear_w4a4_regular(x_bits, w_bits, bias_bits=None):
-    """W4A4 linear with the regular Hadamard rotation (R14): R3-R6 after the
+    """W4A4 linear with the regular Hadamard rotation (R19): R3-R6 after the
     rotation, as in linear_w4a4."""
     qx, sx = quant_act_w4a4_regular(x_bits)
     qw, sw = quant_weight_w4_regular(w_bits)
@@ -425,7 +427,7 @@ def linear_w4a4_regular(x_bits, w_bits, bias_bits=None):
 # blocks' {gate,up,down}_proj Linears, all W4A4 ConvRot in the W4A4 file]
 
 def silu_mul_bf16(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
-    """h = silu(g) * u of two bf16 tensors (reading R15): in float64,
+    """h = silu(g) * u of two bf16 tensors (reading R20): in float64,
     silu(v) = v / (1 + exp(-v)), the product rounded to float32 and then to
     bf16 (both round to nearest even).  Returns bf16 bits."""
     g = bf16_to_f32(g_bits).astype(np.float64)
@@ -436,7 +438,7 @@ def silu_mul_bf16(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
 
 
 def mlp_w4a4(x_bits, wg_bits, wu_bits, wd_bits, group: int = GROUP):
-    """Gated MLP block of W4A4 ConvRot linears (reading R15): g and u the bf16
+    """Gated MLP block of W4A4 ConvRot linears (reading R20): g and u the bf16
     outputs of the gate and up linears of x, h = silu_mul_bf16(g, u), y the
     W4A4 linear of h with the down weight (no biases).  Returns the
     intermediates and the float32 output of the down linear."""

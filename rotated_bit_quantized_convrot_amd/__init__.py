@@ -225,6 +225,14 @@ def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Ten
 # Linears
 # ---------------------------------------------------------------------------
 
+def _same_device(first: torch.Tensor, **others):
+    """Every tensor passed must live on ``first``'s device: the kernels take
+    raw pointers and would fault on another GPU's memory."""
+    for name, t in others.items():
+        if t is not None and t.device != first.device:
+            raise ValueError(f"{name} is on {t.device}, expected {first.device}")
+
+
 def _check_weight(kind: int, packed, scale, N: int, K: int):
     """Refuse packed weights and scales smaller than the layout of (kind, N,
     K) needs: the kernels would read past their end.  (Shapes the library
@@ -245,6 +253,7 @@ def _linear(fn_name: str, kind: int, x, packed, scale, N, bias, out, workspace, 
         raise ValueError("x must be [M, K]")
     M, K = x.shape
     _check_weight(kind, packed, scale, N, K)
+    _same_device(x, packed=packed, scale=scale, bias=bias, out=out, workspace=workspace)
     if bias is not None:
         _dev(bias, "bias", torch.bfloat16)
         if bias.numel() != N:
@@ -319,6 +328,9 @@ def mlp_w4a4(x, wg, sg, wu, su, F, wd, sd, N, out=None, workspace=None):
     _check_weight(W4A4, wg, sg, F, K)
     _check_weight(W4A4, wu, su, F, K)
     _check_weight(W4A4, wd, sd, N, F)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    _same_device(x, wg=wg, sg=sg, wu=wu, su=su, wd=wd, sd=sd, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     else:
@@ -340,6 +352,9 @@ def dbg_quant_swiglu(g: torch.Tensor, u: torch.Tensor):
     quantises the down projection's input."""
     _dev(g, "g", torch.bfloat16)
     _dev(u, "u", torch.bfloat16)
+    if g.dim() != 2 or g.shape != u.shape:
+        raise ValueError("g and u must be [M, K] of the same shape")
+    _same_device(g, u=u)
     M, K = g.shape
     codes = torch.empty((M, K), dtype=torch.int8, device=g.device)
     scales = torch.empty(max(M, 1), dtype=torch.float32, device=g.device)
@@ -353,6 +368,7 @@ def dbg_silu_mul(g: torch.Tensor, u: torch.Tensor) -> torch.Tensor:
     _dev(u, "u", torch.bfloat16)
     if g.shape != u.shape:
         raise ValueError("g and u must have the same shape")
+    _same_device(g, u=u)
     h = torch.empty_like(g)
     _check(lib().cr_dbg_silu_mul(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream()))
     return h
@@ -377,12 +393,17 @@ def gemm_quantized(kind: int, M: int, K: int, packed, scale, N: int, workspace, 
     _dev(scale, "scale", torch.float32)
     _check_weight(kind, packed, scale, N, K)
     _dev(workspace, "workspace", torch.uint8)
+    _same_device(packed, scale=scale, workspace=workspace, bias=bias, out=out)
     if bias is not None:
         _dev(bias, "bias", torch.bfloat16)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=packed.device)
     else:
         _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
     _check(lib().cr_gemm_quantized(kind, M, K, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
                                    _ptr(workspace), workspace.numel(), _stream()))
     return out

@@ -68,6 +68,10 @@ int group_of(int kind) {
 cr_status check_nk(int kind, int N, int K) {
     if (N < 1 || K < 1 || N > CR_MAX_DIM || K > CR_MAX_DIM)
         return fail(CR_ERR_SHAPE, "bad shape N=%d K=%d (need 1..%d)", N, K, CR_MAX_DIM);
+    // int8 codes reach +-127 on both sides, so |acc| <= 16129 K: int32 holds
+    // it up to K = 133144; the limit is the power of two below
+    if (kind == CR_INT8TW && K > CR_MAX_INT8_K)
+        return fail(CR_ERR_SHAPE, "K=%d exceeds %d for int8_tensorwise (int32 accumulator range)", K, CR_MAX_INT8_K);
     if (rotated(kind)) {
         if (K % 256 != 0)
             return fail(CR_ERR_GROUP, "K=%d is not a multiple of the 256-wide rotation group; "

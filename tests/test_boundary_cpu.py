@@ -196,3 +196,63 @@ def test_host_tensors_are_refused():
         crp.pack_weight_w4(w)
     with pytest.raises(ValueError, match="device tensor"):
         crp.linear_w4a4(x, torch.zeros(1, dtype=torch.uint8), torch.ones(1), 32)
+
+
+def test_int8tw_k_limit(L):
+    """int8_tensorwise codes reach +-127 on both sides, so |acc| <= 16129 K;
+    K past 131072 would leave int32 and is refused before any launch."""
+    vp = ctypes.c_void_p(16)
+    assert L.cr_packed_bytes(1, 64, 131072) == 64 * 131072
+    assert L.cr_packed_bytes(1, 64, 131073) == 0
+    assert L.cr_linear_int8tw(vp, 4, 131073, vp, vp, 64, None, vp, vp, 1 << 30, None) == CR["SHAPE"]
+    assert b"131072" in L.cr_last_error()
+    assert L.cr_pack_weight_int8tw(vp, 64, 200000, vp, vp, None) == CR["SHAPE"]
+    assert 16129 * 133144 < 2 ** 31 <= 16129 * 133145
+
+
+def _binding_on_host(monkeypatch):
+    """The binding with its device check switched off, so that its shape
+    checks can be exercised on host tensors; they must raise before any
+    library call that would launch."""
+    import rotated_bit_quantized_convrot_amd as crp
+    real = crp._dev
+
+    def host_ok(t, name, dtype=None):
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}")
+
+    monkeypatch.setattr(crp, "_dev", host_ok)
+
+    def no_launch(*a, **k):
+        raise AssertionError("a launching call was reached")
+    return crp, real, no_launch
+
+
+def test_gemm_quantized_checks_out_and_bias(monkeypatch, L):
+    torch = pytest.importorskip("torch")
+    crp, _, no_launch = _binding_on_host(monkeypatch)
+    monkeypatch.setattr(L, "cr_gemm_quantized", no_launch)
+    M, K, N = 4, 256, 64
+    packed = torch.zeros(crp.packed_bytes(crp.W4A4, N, K), dtype=torch.uint8)
+    scale = torch.ones(1)
+    ws = torch.zeros(crp.workspace_bytes(crp.W4A4, M, N, K), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must be"):
+        crp.gemm_quantized(crp.W4A4, M, K, packed, scale, N, ws, out=torch.zeros((M, N - 1), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="bias must have N"):
+        crp.gemm_quantized(crp.W4A4, M, K, packed, scale, N, ws, bias=torch.zeros(N - 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="packed weight has"):
+        crp.gemm_quantized(crp.W4A4, M, K, packed[:-16], scale, N, ws)
+
+
+def test_swiglu_hooks_check_shapes(monkeypatch, L):
+    torch = pytest.importorskip("torch")
+    crp, _, no_launch = _binding_on_host(monkeypatch)
+    monkeypatch.setattr(L, "cr_dbg_quant_swiglu", no_launch)
+    monkeypatch.setattr(L, "cr_dbg_silu_mul", no_launch)
+    g = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="same shape"):
+        crp.dbg_quant_swiglu(g, torch.zeros((3, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="same shape"):
+        crp.dbg_quant_swiglu(torch.zeros(256, dtype=torch.bfloat16), torch.zeros(256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="same shape"):
+        crp.dbg_silu_mul(g, torch.zeros((4, 128), dtype=torch.bfloat16))

@@ -1,5 +1,5 @@
 """Text-encoder MLP block (gate/up -> silu(g) * u -> rotate + quantise ->
-down; the oracle's reading R15) through the C ABI against the oracle.  The
+down; the oracle's reading R20) through the C ABI against the oracle.  The
 fused kernel's codes and scales are compared bit-exactly with the oracle's
 quantisation of silu_mul_bf16(g, u) (h is computed in float64 on both sides
 and rounded to float32, then bf16: the two float64 exp implementations can

@@ -1,6 +1,6 @@
 """W4A4 with the group-256 regular Hadamard rotation ([QIE] intro:
 "regular-Hadamard"; the construction (J - 2I)^(x4) / 16 is the oracle's
-reading R14): the HIP path through the C ABI against the oracle.  Codes,
+reading R19): the HIP path through the C ABI against the oracle.  Codes,
 scales and int32 accumulators bit-exact; bf16 outputs equal to the oracle's
 bf16 rounding.  Cases cover every activation quantiser path and both GEMM
 paths, with ragged M and N, bias and split K."""

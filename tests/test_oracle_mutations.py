@@ -123,6 +123,27 @@ def _rht_generic(v, dtype=np.float32, order="asc", seq_sum=False, half_weight=Fa
     return (y.reshape(R, G, 256) * dtype(0.0625)).reshape(*lead, K).astype(dtype)
 
 
+def _rot_act_unrotated(x_bits, group=256):
+    return O.quant_rows(O.bf16_to_f32(x_bits), 127, -128, 127)
+
+
+def _rot_act_div7(x_bits, group=256):
+    return O.quant_rows(_real_fwht(O.bf16_to_f32(x_bits), group), 7, -8, 7)
+
+
+def _pack_uint4_high_first(idx):
+    idx = np.asarray(idx, dtype=np.uint8)
+    return (idx[:, 1::2] | (idx[:, 0::2] << 4)).astype(np.uint8)
+
+
+def _unpack_uint4_high_first(p):
+    p = np.asarray(p, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 1::2] = p & 0xF
+    out[:, 0::2] = p >> 4
+    return out
+
+
 def _silu_mul_sigmoid(g_bits, u_bits):
     g = O.bf16_to_f32(g_bits).astype(np.float64)
     u = O.bf16_to_f32(u_bits).astype(np.float64)
@@ -158,6 +179,12 @@ MUTATIONS = {
     "rht_diagonal_weight_1": ("rht", lambda v, dtype=np.float32: _rht_generic(v, dtype, half_weight=True)),
     "mlp_sigmoid_not_silu": ("silu_mul_bf16", _silu_mul_sigmoid),
     "mlp_gate_without_up": ("silu_mul_bf16", _silu_no_up),
+    "int8rot_act_unrotated": ("quant_act_int8rot", _rot_act_unrotated),
+    "int8rot_act_div7": ("quant_act_int8rot", _rot_act_div7),
+    "w4a8_act_unrotated": ("quant_act_w4a8", _rot_act_unrotated),
+    "w4a8_act_div7": ("quant_act_w4a8", _rot_act_div7),
+    # both directions swapped consistently: a round trip alone cannot see it
+    "uint4_high_first": [("pack_uint4", _pack_uint4_high_first), ("unpack_uint4", _unpack_uint4_high_first)],
 }
 
 PINS = [
@@ -194,13 +221,20 @@ PINS = [
     P.test_silu_mul_matches_library_logistic,
     P.test_silu_mul_special_values,
     P.test_mlp_block_close_to_float_mlp,
+    lambda: P.test_rotated_int8_act_one_hot_rows("int8rot"),
+    lambda: P.test_rotated_int8_act_one_hot_rows("w4a8"),
+    lambda: P.test_rotated_int8_act_constant_rows("int8rot", 0.75),
+    lambda: P.test_rotated_int8_act_constant_rows("w4a8", -2.0),
+    P.test_linear_int8rot_close_to_float_linear,
+    P.test_uint4_nibble_order_hand_bytes,
 ]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, monkeypatch):
-    attr, bad = MUTATIONS[name]
-    monkeypatch.setattr(O, attr, bad)
+    plants = MUTATIONS[name]
+    for attr, bad in (plants if isinstance(plants, list) else [plants]):
+        monkeypatch.setattr(O, attr, bad)
     caught = []
     for pin in PINS:
         try:
