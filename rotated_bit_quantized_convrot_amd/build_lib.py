@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libconvrot.so")
-SOURCES = ["cr_api.hip", "cr_quant.hip", "cr_gemm.hip", "cr_gemm_small.hip"]
+SOURCES = ["cr_api.hip", "cr_quant.hip", "cr_gemm.hip", "cr_gemm_small.hip", "cr_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -36,7 +36,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Werror=inline-asm",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -61,14 +61,17 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 
 // buffer_load_dwordx4 ... lds: lane i's 16 bytes at offset voff + soff of the
 // resource go to LDS address lds + 16 i.  Issued from inline asm, the load is
-// not seen by the compiler as an LDS write, so it inserts no vmcnt(0) before
-// later LDS reads (the stage ring makes them independent); completion is
-// tracked with explicit wait_vmcnt<> before the barrier that publishes a
-// stage.  The instruction has no register result; M0 (the LDS address) is set
-// in the same block.
+// not seen by the compiler as an LDS write, so it neither inserts waits for it
+// before later LDS reads nor orders those reads after it (the stage ring
+// makes them independent); completion is tracked with explicit wait_vmcnt<>
+// before the barrier that publishes a stage.  The instruction has no register
+// result.  The LDS address goes in M0 through an input operand bound to that
+// register, so the compiler itself sets M0 and knows its value.
+// (The compiler's direct-to-LDS buffer-load builtin gives the same
+// instruction, but with it the int8-weight kernels need ~40 more VGPRs and
+// spill at 256-wide tiles.)
 __device__ __forceinline__ void buf_lds16(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 : : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
 }
 
 template <int V> struct IntC { static constexpr int value = V; };

@@ -1,7 +1,9 @@
 """Full-size parity for every workload, in the launch configuration the
-benchmark times: the GPU computes the whole layer, the oracle recomputes a
-sample of rows (rows are independent given the weight), compared bit-exact on
-the int32 accumulators and within 1e-2 on the bf16 outputs."""
+benchmark times: the GPU computes the whole layer and the oracle recomputes
+every row of it (a few seconds of float64 BLAS per layer), compared bit-exact
+on the int32 accumulators and on the bf16 output bits (the oracle's float32
+epilogue rounded to nearest even), and within 1e-2 relative error.  Only the
+M = 131071 case checks a sample of rows."""
 import numpy as np
 import pytest
 
@@ -20,8 +22,10 @@ def crp():
     return m
 
 
-def _rows(M, n=24, seed=0):
-    if M <= 96:
+def _rows(M, n=None, seed=0):
+    """All rows, or (n given) a seeded sample that keeps the first, middle
+    and last rows."""
+    if n is None or M <= n:
         return np.arange(M)
     rng = np.random.default_rng(seed)
     fixed = [0, 1, M // 2, M - 2, M - 1]
@@ -29,12 +33,22 @@ def _rows(M, n=24, seed=0):
     return np.sort(np.concatenate([fixed, rest]))
 
 
+def _take(t, rows):
+    if len(rows) == t.shape[0]:
+        return t
+    return t.index_select(0, torch.from_numpy(rows).cuda())
+
+
 def _check(y, acc, rows, ref_acc, ref_y):
-    idx = torch.from_numpy(rows).cuda()
-    a = acc.index_select(0, idx).cpu().numpy()
-    assert np.array_equal(a, ref_acc)
-    yd = bf16_dev_to_f32(y.index_select(0, idx))
-    assert max_rel_err(yd, ref_y) <= TOL
+    a = _take(acc, rows).cpu().numpy()
+    bad = np.argwhere(a != ref_acc)
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first at (row, col) {tuple(bad[0])}"
+    yt = _take(y, rows)
+    ybits = yt.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = O.f32_to_bf16_rne(ref_y)
+    nbad = int(np.count_nonzero(ybits != want))
+    assert nbad == 0, f"{nbad} bf16 outputs differ from the oracle's rounding"
+    assert max_rel_err(bf16_dev_to_f32(yt), ref_y) <= TOL
 
 
 W4A4_LAYERS = {
@@ -157,8 +171,7 @@ def test_w4a4_rotation_variants_full_size(crp, name):
 @pytest.mark.parametrize("M", [76, 1220])
 def test_mlp_block_full_size(crp, M):
     """The text-encoder MLP block at the benchmark's shapes: the GPU runs the
-    whole block, the oracle follows sampled rows through it (rows are
-    independent given the three tensorwise weight scales) and the bf16
+    whole block, the oracle follows every row through it and the bf16
     outputs must be equal."""
     print(f"[fullsize] te_mlp_M{M}", flush=True)
     xb, wg, wu, wd = si.te_mlp(M)
@@ -193,7 +206,7 @@ def test_w4a4_very_large_m(crp):
     y = crp.linear_w4a4(x, p, s, N, to_dev_bf16(L.bias), workspace=ws)
     acc = crp.dbg_linear_acc(0, x, p, N, workspace=ws)
     torch.cuda.synchronize()
-    rows = _rows(M, n=48, seed=3)
+    rows = _rows(M, n=4096, seed=3)
     qw, sw = O.quant_weight_w4(L.w)
     qx, sx = O.quant_act_w4a4(L.x[rows])
     ref_acc = O.int_gemm(qx, qw)
