@@ -242,6 +242,95 @@ def measure_mlp(torch, crp, M: int, cold: bool, reps: int):
 
 
 # ---------------------------------------------------------------------------
+# Ceilings of the machine at hand (probe kernels of the library, not the
+# method): int8 matrix-core rate, cold single-kernel read, plain copy; and the
+# shader clock, from the kernels' own cycle and real-time counters
+# ---------------------------------------------------------------------------
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _sclk_mhz(stamps, wall_khz):
+    """Shader clock (MHz) from a probe's cycle and real-time counter stamps."""
+    c0, c1, w0, w1 = [int(v) for v in stamps]
+    if wall_khz <= 0 or w1 <= w0:
+        return None
+    return (c1 - c0) / ((w1 - w0) / (wall_khz * 1e3)) / 1e6
+
+
+def clock_sample(torch, crp):
+    """Shader clock right now: a one-block matrix-core probe of ~0.1 ms,
+    enqueued behind whatever the stream is running."""
+    sink = torch.empty(512, dtype=torch.int32, device="cuda")
+    stamps = torch.zeros(4, dtype=torch.int64, device="cuda")
+    crp.probe_mfma_i8(1, 2000, sink, stamps)
+    torch.cuda.synchronize()
+    return _sclk_mhz(stamps.cpu().tolist(), crp.probe_wall_clock_khz())
+
+
+def measure_ceilings(torch, crp, read_bytes: int, copies: int):
+    """Probe ceilings: the int8 matrix-core rate (8 and 16 waves per CU, at the
+    chip's power limit after a warm-up of the same launch), the rate of one
+    kernel reading a cold buffer of ``read_bytes`` (cycled through ``copies``
+    distinct buffers, by graph replay, as the cold-weight rows are), and a
+    512 MiB device copy."""
+    dev = "cuda"
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = crp.probe_wall_clock_khz()
+    out = {"wall_clock_khz": khz, "cus": ncu}
+    sink = torch.empty(2 * ncu * 512, dtype=torch.int32, device=dev)
+    stamps = torch.zeros(4, dtype=torch.int64, device=dev)
+    best = None
+    for blocks, iters in ((ncu, 400), (2 * ncu, 200)):
+        for _ in range(3):                              # warm-up: clock settles under this load
+            crp.probe_mfma_i8(blocks, iters, sink, stamps)
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            e0, e1 = _events(torch)
+            e0.record()
+            crp.probe_mfma_i8(blocks, iters, sink, stamps)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3
+            runs.append((us, _sclk_mhz(stamps.cpu().tolist(), khz)))
+        us, mhz = sorted(runs)[1]
+        ops = blocks * 8.0 * iters * 4 * 65536
+        r = {"waves_per_cu": 8 * blocks // ncu, "us": round(us, 1), "tops": round(ops / (us * 1e-6) / 1e12, 1),
+             "sclk_mhz": round(mhz, 1) if mhz else None}
+        out[f"mfma_i8_{r['waves_per_cu']}w"] = r
+        if best is None or r["tops"] > best["tops"]:
+            best = r
+    out["mfma_i8_tops"] = best["tops"]
+    out["mfma_i8_sclk_mhz"] = best["sclk_mhz"]
+    del sink
+
+    n16 = read_bytes // 16 * 16
+    bufs = [torch.empty(n16, dtype=torch.uint8, device=dev).fill_(i & 0xFF) for i in range(copies)]
+    rsink = torch.empty(crp.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    read_us = graph_time_us(torch, [lambda i=i: crp.probe_read(bufs[i], rsink) for i in range(copies)])
+    out["cold_read"] = {"bytes": n16, "copies": copies, "us": round(read_us, 3),
+                        "gbs": round(n16 / (read_us * 1e-6) / 1e9, 1)}
+    del bufs
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    crp.probe_copy(src, dst)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(5):
+        crp.probe_copy(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    cus = e0.elapsed_time(e1) * 1e3 / 5
+    out["copy"] = {"bytes": COPY_BYTES, "us": round(cus, 1), "gbs_read_plus_write": round(2 * COPY_BYTES / (cus * 1e-6) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a row sample of the headline layer
 # ---------------------------------------------------------------------------
 
@@ -299,6 +388,7 @@ def main():
     ap.add_argument("--repeat", type=int, default=20, help="calls per captured graph")
     ap.add_argument("--rows", default="all", help="all | none | comma-separated row names")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the probe ceilings")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--prewarm-ms", type=float, default=150.0,
                     help="untimed run of the step before the warm-up steps (clock ramp)")
@@ -392,6 +482,7 @@ def main():
         evs[k][1].record()
     torch.cuda.synchronize()
     step_gemm_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    sclk_headline = clock_sample(torch, crp)
     _log(f"headline: {ms_per_step * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events; "
          f"GEMM {step_gemm_us:.1f} us per launch")
     # --- kernels of the headline step: GEMM and activation kernel -----------
@@ -422,22 +513,33 @@ def main():
                  f"weights {rows[name]['weight_gbs']:.0f} GB/s)")
             torch.cuda.empty_cache()
 
+    ceil = None
+    if not args.no_ceilings:
+        _log("ceilings: int8 matrix-core probe, cold read, copy")
+        ceil = measure_ceilings(torch, crp, int(9728 * 2560 // 2), COLD_COPIES)
+        _log(f"  mfma {ceil['mfma_i8_tops']} TOPS at {ceil['mfma_i8_sclk_mhz']} MHz; cold read "
+             f"{ceil['cold_read']['us']} us = {ceil['cold_read']['gbs']} GB/s; copy {ceil['copy']['gbs_read_plus_write']} GB/s")
+
     achieved = head.ops() / (step_gemm_us * 1e-6) / 1e12
     roofline = {
         "bound": "mfma",
         "kernel": "k_gemm_big<W4> (DiT W1, M=4096 K=3072 N=12288)",
         "achieved": round(achieved, 2),
         "peak": PEAK_INT8_TOPS,
-        "unit": "TFLOP/s",
+        "unit": "TOP/s",
         "frac": round(achieved / PEAK_INT8_TOPS, 4),
+        "ceiling": ceil["mfma_i8_tops"] if ceil else None,
+        "frac_of_ceiling": round(achieved / ceil["mfma_i8_tops"], 4) if ceil else None,
+        "ceiling_note": "ceiling: int8 matrix-core probe of the library (register operands, no memory "
+                        "traffic, 8 or 16 waves per CU, best), measured in this run at the chip's power limit",
         "traffic": load_traffic(khash),
         "algorithmic_bytes": head.gemm_bytes(),
         "avg_launch_us": round(step_gemm_us, 3),
         "graph_replay_us": round(hrow["gemm_us"], 3),
         "note": "int8 MFMA ops (2*M*N*K per launch) / the GEMM's average launch duration, from HIP "
                 "events on the launch stream around each GEMM launch of K steps run right after the "
-                "timed ones; unit is int TOPS.  graph_replay_us: the same kernel over a replayed "
-                "graph of back-to-back launches",
+                "timed ones; unit: tera integer ops per second.  graph_replay_us: the same kernel over "
+                "a replayed graph of back-to-back launches",
     }
     small = rows.get("te_gate_up_M76")
     small_m = None
@@ -452,6 +554,11 @@ def main():
             "frac": round(small["weight_gbs"] / PEAK_HBM_GBS, 4),
             "gemm_us": round(small["gemm_us"], 3),
             "linear_us": round(small["linear_us"], 3),
+            "ceiling": ceil["cold_read"]["gbs"] if ceil else None,
+            "frac_of_ceiling": round(small["weight_gbs"] / ceil["cold_read"]["gbs"], 4) if ceil else None,
+            "floor_us": ceil["cold_read"]["us"] if ceil else None,
+            "ceiling_note": "ceiling: one probe kernel of the library reading a cold 12.45 MB buffer (the "
+                            "gate/up weight's size), cycled over 48 copies by graph replay like the GEMM",
         }
 
     cpu = None
@@ -481,6 +588,12 @@ def main():
         "small_m": small_m,
         "cpu_baseline": cpu,
         "step_events_us": round(ev_ms * 1e3, 3),
+        "clocks": {"sclk_mhz_after_headline": round(sclk_headline, 1) if sclk_headline else None,
+                   "sclk_mhz_mfma_probe": ceil["mfma_i8_sclk_mhz"] if ceil else None,
+                   "note": "shader clock from the probe kernels' cycle counter over the real-time "
+                           "counter: right after the headline's event-timed steps (same stream), and "
+                           "under the full-chip matrix-core probe"},
+        "ceilings": ceil,
         "prewarm": {"ms": args.prewarm_ms, "steps": prewarm_steps},
         "rows": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in rows.items()},

@@ -33,6 +33,7 @@ __all__ = [
     "dbg_quant_act", "dbg_unpack_weight", "dbg_linear_acc",
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
+    "probe_mfma_i8", "probe_read", "probe_copy", "probe_wall_clock_khz",
 ]
 
 W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
@@ -53,6 +54,8 @@ EXPORTS = [
     "cr_pack_weight_w4_group", "cr_linear_w4a4_group",
     "cr_pack_weight_w4_regular", "cr_linear_w4a4_regular",
     "cr_mlp_workspace_bytes", "cr_mlp_w4a4", "cr_dbg_quant_swiglu", "cr_dbg_silu_mul",
+    # measurement probes (include/convrot_probe.h)
+    "cr_probe_mfma_i8", "cr_probe_read", "cr_probe_copy", "cr_probe_wall_clock_khz",
 ]
 
 
@@ -100,6 +103,10 @@ def lib() -> ctypes.CDLL:
         "cr_dbg_linear_acc": (i, [i, vp, i, i, vp, i, vp, vp, sz, vp]),
         "cr_quantize_activations": (i, [i, vp, i, i, vp, sz, vp]),
         "cr_gemm_quantized": (i, [i, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_probe_mfma_i8": (i, [i, i, vp, vp, vp]),
+        "cr_probe_read": (i, [vp, sz, vp, vp]),
+        "cr_probe_copy": (i, [vp, vp, sz, vp]),
+        "cr_probe_wall_clock_khz": (i, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -491,3 +498,47 @@ def linear(x: torch.Tensor, pw: PackedWeight, out=None, workspace=None) -> torch
     fn = {W4A4: linear_w4a4, INT8TW: linear_int8tw, W4A8: linear_w4a8, INT8ROT: linear_int8rot,
           W4A4_RH: linear_w4a4_regular}[pw.kind]
     return fn(x, pw.packed, pw.scale, pw.N, pw.bias, out, workspace)
+
+
+# ---------------------------------------------------------------------------
+# Measurement probes (include/convrot_probe.h): ceilings of the machine at
+# hand, not part of the method
+# ---------------------------------------------------------------------------
+
+PROBE_SINK_WORDS = 4096
+
+
+def probe_mfma_i8(blocks: int, iters: int, sink: torch.Tensor, stamps: torch.Tensor):
+    """Launch the int8 matrix-core probe: blocks * 8 * iters * 4 * 65536 int
+    ops; ``sink`` int32 [blocks * 512], ``stamps`` int64 [4] (shader clock
+    counter start/end, real-time counter start/end)."""
+    _dev(sink, "sink", torch.int32)
+    _dev(stamps, "stamps", torch.int64)
+    if sink.numel() < blocks * 512 or stamps.numel() < 4:
+        raise ValueError("sink needs blocks * 512 words and stamps 4")
+    _check(lib().cr_probe_mfma_i8(blocks, iters, _ptr(sink), _ptr(stamps), _stream()))
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor):
+    """One kernel reading all of ``src`` (bytes a multiple of 16)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _dev(sink, "sink", torch.int32)
+    if sink.numel() < PROBE_SINK_WORDS:
+        raise ValueError(f"sink needs {PROBE_SINK_WORDS} words")
+    _check(lib().cr_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream()))
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor):
+    """dst = src, one kernel with 16-byte loads and stores."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nb:
+        raise ValueError("dst is smaller than src")
+    _check(lib().cr_probe_copy(_ptr(src), _ptr(dst), nb, _stream()))
+
+
+def probe_wall_clock_khz() -> int:
+    return int(lib().cr_probe_wall_clock_khz())

@@ -7,14 +7,15 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "convrot.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADER = os.path.join(INCLUDE, "convrot.h")
 LIBPATH = os.path.join(ROOT, "rotated_bit_quantized_convrot_amd", "libconvrot.so")
 
 CR = dict(OK=0, NULL=1, SHAPE=2, GROUP=3, ALIGN=4, WORKSPACE=5, DEVICE=6, LAUNCH=7, KIND=8)
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cr_[a-z0-9_]+)\s*\(", text)))
 
@@ -256,3 +257,4 @@ def test_swiglu_hooks_check_shapes(monkeypatch, L):
         crp.dbg_quant_swiglu(torch.zeros(256, dtype=torch.bfloat16), torch.zeros(256, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="same shape"):
         crp.dbg_silu_mul(g, torch.zeros((4, 128), dtype=torch.bfloat16))
+
