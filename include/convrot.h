@@ -122,6 +122,22 @@ cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed,
                          const float* w_scale, int N, const void* bias_bf16,
                          void* y_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): cr_linear_w4a4
+ * with no workspace argument.  Its workspace is a static device array of the
+ * library, CR_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends);
+ * the call allocates nothing.  Same kernels, same results bit for bit.
+ * Shapes whose workspace (cr_workspace_bytes(CR_W4A4, M, N, K)) exceeds the
+ * scratch return CR_ERR_WORKSPACE before any launch (e.g. M = 4096, K = 3072
+ * fits; a layer that splits K across blocks at large M may not).  All calls
+ * on one GPU share that GPU's scratch: two calls that can overlap on one GPU
+ * (different streams, no ordering between them) race and give undefined
+ * results; calls in one stream are safe. */
+#define CR_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+cr_status cr_linear_w4a4_noalloc(const void* x_bf16, int M, int K, const void* w_packed,
+                                 const float* w_scale, int N, const void* bias_bf16,
+                                 void* y_bf16, hipStream_t stream);
+
 /* ---- W4A4 with smaller rotation groups ([ZIT] "Where Z-Image sits": the
  *      ConvRot group-size sweep 256 / 64 / 16) ------------------------------
  * As cr_pack_weight_w4 / cr_linear_w4a4 with the Hadamard rotation applied

@@ -34,6 +34,7 @@ __all__ = [
     "quantize_activations", "gemm_quantized",
     "PackedWeight", "pack_linear", "linear",
     "probe_mfma_i8", "probe_read", "probe_copy", "probe_wall_clock_khz",
+    "linear_w4a4_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
@@ -56,6 +57,7 @@ EXPORTS = [
     "cr_mlp_workspace_bytes", "cr_mlp_w4a4", "cr_dbg_quant_swiglu", "cr_dbg_silu_mul",
     # measurement probes (include/convrot_probe.h)
     "cr_probe_mfma_i8", "cr_probe_read", "cr_probe_copy", "cr_probe_wall_clock_khz",
+    "cr_linear_w4a4_noalloc",
 ]
 
 
@@ -94,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "cr_dbg_quant_swiglu": (i, [vp, vp, i, i, vp, vp, vp]),
         "cr_dbg_silu_mul": (i, [vp, vp, sz, vp, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
+        "cr_linear_w4a4_noalloc": (i, [vp, i, i, vp, vp, i, vp, vp, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_status_str": (ctypes.c_char_p, [i]),
@@ -292,6 +295,37 @@ def linear_w4a4(x, packed, scale, N, bias=None, out=None, workspace=None, group:
         return _linear("cr_linear_w4a4", W4A4, x, packed, scale, N, bias, out, workspace)
     return _linear("cr_linear_w4a4_group", W4_GROUP_KIND.get(group, W4A4), x, packed, scale, N, bias, out,
                    workspace, group=group)
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def linear_w4a4_noalloc(x, packed, scale, N, bias=None, out=None):
+    """cr_linear_w4a4_noalloc: the W4A4 linear with the library's static
+    scratch as its workspace (the C call allocates nothing; ``out`` is
+    allocated here when not given).  Shapes whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(packed, "packed", torch.uint8)
+    _dev(scale, "scale", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    _check_weight(W4A4, packed, scale, N, K)
+    _same_device(x, packed=packed, scale=scale, bias=bias, out=out)
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16)
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check(lib().cr_linear_w4a4_noalloc(_ptr(x), M, K, _ptr(packed), _ptr(scale), N, _ptr(bias), _ptr(out),
+                                        _stream()))
+    return out
 
 
 def linear_w4a4_regular(x, packed, scale, N, bias=None, out=None, workspace=None):

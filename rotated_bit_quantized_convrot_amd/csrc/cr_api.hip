@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "convrot.h"
 #include "cr_internal.h"
@@ -234,6 +235,40 @@ cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, cons
     return gemm_phase(kind, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
 }
 
+// ---- static scratch of cr_linear_w4a4_noalloc ----------------------------
+// For callers that cannot allocate: the workspace of one W4A4 linear lives in
+// this file-scope device array (one copy per GPU, held until the process
+// ends).  Host code never passes the array's name to a kernel: its device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static_assert(kScratchBytes == CR_NOALLOC_SCRATCH_BYTES, "header and library agree on the scratch size");
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];          // device address of `scratch` per device id, under g_scratch_mu
+
+cr_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(CR_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev >= 64) return fail(CR_ERR_DEVICE, "device id %d beyond the 64 the static scratch table covers", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(CR_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CR_OK;
+}
+
 // Gated MLP block workspace: [x codes + gate/up partials | g | u | h codes +
 // down partials], each region at a 256-byte boundary.
 struct MlpLayout {
@@ -444,6 +479,26 @@ cr_status cr_linear_w4a4(const void* x_bf16, int M, int K, const void* w_packed,
                          hipStream_t stream) {
     return run_linear(CR_W4A4, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws,
                       ws_bytes, stream);
+}
+
+cr_status cr_linear_w4a4_noalloc(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
+                                 int N, const void* bias_bf16, void* y_bf16, hipStream_t stream) {
+    // the same checks as cr_linear_w4a4 (the workspace pointer stands in as non-null)
+    cr_status s = check_linear_args(CR_W4A4, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, w_packed);
+    if (s != CR_OK) return s;
+    if (M == 0) return ok();
+    if (x_bf16 == nullptr) return fail(CR_ERR_NULL, "x is NULL");
+    if (!aligned16(x_bf16)) return fail(CR_ERR_ALIGN, "x not 16-byte aligned");
+    const size_t need = ws_layout(CR_W4A4, M, N, K).total;
+    if (need > kScratchBytes)
+        return fail(CR_ERR_WORKSPACE, "M=%d N=%d K=%d needs %zu bytes of workspace; the static scratch of the "
+                    "no-allocation entry point holds %zu (use cr_linear_w4a4 with a workspace)",
+                    M, N, K, need, kScratchBytes);
+    if ((s = check_device()) != CR_OK) return s;
+    void* ws = nullptr;
+    if ((s = scratch_address(&ws)) != CR_OK) return s;
+    if ((s = quantize_phase(CR_W4A4, x_bf16, M, K, ws, kScratchBytes, stream)) != CR_OK) return s;
+    return gemm_phase(CR_W4A4, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, kScratchBytes, stream);
 }
 
 cr_status cr_linear_int8tw(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,

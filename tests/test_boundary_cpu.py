@@ -258,3 +258,15 @@ def test_swiglu_hooks_check_shapes(monkeypatch, L):
     with pytest.raises(ValueError, match="same shape"):
         crp.dbg_silu_mul(g, torch.zeros((4, 128), dtype=torch.bfloat16))
 
+
+def test_noalloc_rejects_oversized_shapes_before_any_launch(L):
+    """The no-allocation entry point's static scratch is 8 MiB: a shape that
+    needs more workspace is refused (CR_ERR_WORKSPACE) before the device is
+    touched."""
+    vp = ctypes.c_void_p(16)
+    assert L.cr_workspace_bytes(0, 4096, 12288, 3072) <= 8 << 20
+    assert L.cr_workspace_bytes(0, 4096, 2560, 9728) > 8 << 20
+    assert L.cr_linear_w4a4_noalloc(vp, 4096, 9728, vp, vp, 2560, None, vp, None) == CR["WORKSPACE"]
+    assert b"static scratch" in L.cr_last_error()
+    assert L.cr_linear_w4a4_noalloc(vp, 4, 300, vp, vp, 64, None, vp, None) == CR["GROUP"]
+    assert L.cr_linear_w4a4_noalloc(None, 0, 256, vp, vp, 64, None, None, None) == CR["OK"]
