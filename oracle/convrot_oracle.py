@@ -59,10 +59,16 @@ R9  fp8 is OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF are NaN, max 448).
 R10 W4A8 encode (offline): s_channel[n] = absmax_k |W~[n,:]| / 127;
     s_rel[n,g] = e4m3_rne(min(absmax_{k in g} |W~| / s_channel[n], 127));
     u = W~ / (s_channel * s_rel) (0 where the divisor is 0); 16-level
-    Lloyd-Max quantiser of all u of the tensor, decision thresholds at the
-    midpoints, levels at the cell means, initialised at the (j+1/2)/16
-    quantiles, at most 100 iterations; idx = the cell of u (a value on a
-    threshold goes to the lower level).
+    Lloyd-Max quantiser of all u of the tensor (as float32): levels start
+    evenly spread over [min u, max u], cells by the midpoints of adjacent
+    levels (a value on a midpoint goes to the lower level), each level moved
+    to its cell's exact mean (samples summed as the integers rint(u 2^24),
+    one float64 division), at most 100 iterations or until no level moves;
+    the codebook is the levels rounded to float32; idx = the cell of u by
+    the midpoints of the float32 codebook.  (The pages fix only "16
+    Lloyd-Max levels fit to the tensor"; the start and the exact sums make
+    the fit one definite result that a parallel encoder reproduces bit for
+    bit.)
 R17 ConvRot INT8 row-scaled ([Q3N] file table: INT8 with group-256 Hadamard
     rotation and row-wise scaling; converter flags: int8, row scaling,
     dynamic ConvRot, group 256): the weight is rotated like R2, then
@@ -98,10 +104,11 @@ R20 Text-encoder MLP block ([Q3N] file table and the "qwen3vl_4b" page:
 R21 Canonical 4-bit storage: two values per byte, low nibble = even k;
     signed codes in two's complement, codebook indices unsigned.
 
-Parity notes: the Lloyd-Max codebook fit (R10) is parity unpinned - several
-codebooks are correct and the GPU consumes whatever codebook it is given; its
-tests check only properties (sorted levels, non-increasing distortion,
-plausible weight error).
+Parity notes: the Lloyd-Max fit (R10) is defined to be deterministic (exact
+integer cell sums, a fixed start), so the GPU encoder is compared with it bit
+for bit; it is pinned by the closed-form optimum of a uniform source, the
+textbook 16-level Gaussian quantiser, non-increasing distortion and the
+pages' ~7% weight error.
 """
 from __future__ import annotations
 
@@ -542,37 +549,59 @@ def linear_w4a8(x_bits, idx_packed, s_rel, codebook, s_channel, bias_bits=None,
                 y=epilogue(acc, sx, np.asarray(s_channel, F32), bias_bits))
 
 
+LLOYD_FRAC_BITS = 24        # samples enter the cell sums as integers rint(u * 2^24)
+
+
 def lloyd_max_16(u: np.ndarray, iters: int = 100):
     """16-level Lloyd-Max scalar quantiser of the samples ``u`` (reading R10).
 
-    Thresholds are midpoints of adjacent levels, levels are the means of their
-    cells.  Works on sorted samples with prefix sums, which gives the same
-    cells as assigning each sample to its nearest level.  Returns
-    (levels float32 [16] sorted, list of distortion per iteration)."""
-    s = np.sort(np.asarray(u, dtype=np.float64).ravel())
-    n = s.size
+    The samples are taken as float32.  Levels start evenly spread over
+    [min u, max u]: c_j = lo + (j + 1/2) * ((hi - lo) / 16) in float64.  An
+    iteration assigns every sample to a cell by the midpoints t_j =
+    (c_j + c_{j+1}) / 2 (float64; a sample on a midpoint goes to the lower
+    cell) and moves every non-empty cell's level to the cell mean, taken
+    exactly: each sample enters the sum as the integer q = rint(u * 2^24)
+    (exact for float32 |u| < 2^29), so the sums are exact integers and do not
+    depend on the order of summation, and the level is
+    fl(float64(S) / float64(n)) * 2^-24.  Empty cells keep their level; the
+    levels are then sorted.  Stops when an iteration changes no level, or
+    after ``iters`` iterations.  Returns (levels float32 [16], list of the
+    distortion at each iteration).
+
+    Computed here on the sorted samples with prefix sums (of q, exact in
+    int64), which gives the same cells and sums as visiting every sample."""
+    u32 = np.asarray(u, dtype=np.float32).ravel()
+    n = u32.size
     if n == 0:
         return np.zeros(16, F32), []
-    csum = np.concatenate([[0.0], np.cumsum(s)])
+    if np.max(np.abs(u32)) >= 2.0 ** 28:
+        raise ValueError("samples too large for the exact fixed-point sums")
+    s = np.sort(u32.astype(np.float64))
+    q = np.rint(np.sort(u32) * F32(2.0 ** LLOYD_FRAC_BITS)).astype(np.int64)
+    cq = np.concatenate([[0], np.cumsum(q)])                  # exact int64 prefix sums
+    if abs(int(cq[-1])) >= 2 ** 53 or int(np.sum(np.abs(q))) >= 2 ** 53:
+        raise ValueError("too many samples for exact float64 sums")
+    csum = np.concatenate([[0.0], np.cumsum(s)])             # distortion bookkeeping only
     csq = np.concatenate([[0.0], np.cumsum(s * s)])
-    q = (np.arange(16) + 0.5) / 16.0
-    levels = np.quantile(s, q)
+    lo, hi = s[0], s[-1]
+    w = (hi - lo) / 16.0
+    levels = np.array([lo + (j + 0.5) * w for j in range(16)], dtype=np.float64)
     hist = []
 
     def cells(lv):
         thr = 0.5 * (lv[:-1] + lv[1:])
-        # a sample equal to a threshold belongs to the lower cell
-        return np.concatenate([[0], np.searchsorted(s, thr, side="right"), [n]])
+        # a sample equal to a midpoint belongs to the lower cell
+        return np.concatenate([[0], np.searchsorted(s, thr, side="left"), [n]])
 
     for _ in range(iters):
         b = cells(levels)
         cnt = b[1:] - b[:-1]
         sums = csum[b[1:]] - csum[b[:-1]]
         sq = csq[b[1:]] - csq[b[:-1]]
-        dist = float(np.sum(sq - 2 * levels * sums + cnt * levels ** 2))
-        hist.append(dist)
-        new = np.where(cnt > 0, sums / np.maximum(cnt, 1), levels)
-        new = np.sort(new)
+        hist.append(float(np.sum(sq - 2 * levels * sums + cnt * levels ** 2)))
+        qs = cq[b[1:]] - cq[b[:-1]]                           # exact integer cell sums
+        mean = qs.astype(np.float64) / np.maximum(cnt, 1).astype(np.float64) * 2.0 ** -LLOYD_FRAC_BITS
+        new = np.sort(np.where(cnt > 0, mean, levels))
         if np.array_equal(new, levels):
             break
         levels = new
