@@ -591,7 +591,7 @@ def lloyd_max_16(u: np.ndarray, iters: int = 100):
     def cells(lv):
         thr = 0.5 * (lv[:-1] + lv[1:])
         # a sample equal to a midpoint belongs to the lower cell
-        return np.concatenate([[0], np.searchsorted(s, thr, side="left"), [n]])
+        return np.concatenate([[0], np.searchsorted(s, thr, side="right"), [n]])
 
     for _ in range(iters):
         b = cells(levels)

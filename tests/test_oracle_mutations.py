@@ -155,6 +155,39 @@ def _silu_no_up(g_bits, u_bits):
     return O.f32_to_bf16_rne((g / (1.0 + np.exp(-g))).astype(F32))
 
 
+_real_lloyd = O.lloyd_max_16
+
+
+def _lloyd_ties_up(u, iters=100):
+    """R10 with a sample on a midpoint sent to the upper cell."""
+    real_ss = np.searchsorted
+
+    def ss(a, v, side="left", sorter=None):
+        return real_ss(a, v, side="left" if side == "right" else "right", sorter=sorter)
+    np.searchsorted = ss
+    try:
+        return _real_lloyd(u, iters)
+    finally:
+        np.searchsorted = real_ss
+
+
+def _lloyd_float_sums(u, iters=100):
+    """R10 with float32 cell means in place of the exact integer sums."""
+    u32 = np.sort(np.asarray(u, np.float32).ravel())
+    lo, hi = float(u32[0]), float(u32[-1])
+    lv = np.array([lo + (j + 0.5) * ((hi - lo) / 16.0) for j in range(16)])
+    for _ in range(iters):
+        thr = 0.5 * (lv[:-1] + lv[1:])
+        cell = np.searchsorted(thr, u32.astype(np.float64), side="left")
+        new = np.array([u32[cell == j].mean(dtype=np.float32) if np.any(cell == j) else lv[j] for j in range(16)],
+                       dtype=np.float64)
+        new = np.sort(new)
+        if np.array_equal(new, lv):
+            break
+        lv = new
+    return lv.astype(F32), [0.0]
+
+
 MUTATIONS = {
     "fwht_descending_order": ("fwht", lambda v, group=256, dtype=np.float32:
                               _fwht_generic(v, group, dtype, order="desc")),
@@ -184,6 +217,8 @@ MUTATIONS = {
     "w4a8_act_unrotated": ("quant_act_w4a8", _rot_act_unrotated),
     "w4a8_act_div7": ("quant_act_w4a8", _rot_act_div7),
     # both directions swapped consistently: a round trip alone cannot see it
+    "lloyd_ties_to_upper_cell": ("lloyd_max_16", _lloyd_ties_up),
+    "lloyd_float32_means": ("lloyd_max_16", _lloyd_float_sums),
     "uint4_high_first": [("pack_uint4", _pack_uint4_high_first), ("unpack_uint4", _unpack_uint4_high_first)],
 }
 
@@ -227,6 +262,7 @@ PINS = [
     lambda: P.test_rotated_int8_act_constant_rows("w4a8", -2.0),
     P.test_linear_int8rot_close_to_float_linear,
     P.test_uint4_nibble_order_hand_bytes,
+    P.test_lloyd_max_hand_fixture,
 ]
 
 

@@ -354,6 +354,25 @@ def test_lloyd_max_gaussian_textbook_levels():
     assert np.max(np.abs(cb[:8][::-1] + want)) < 0.03
 
 
+def test_lloyd_max_hand_fixture():
+    """R10 by hand: samples 0..31 and 1.9375 (float32).  lo = 0, hi = 31, so
+    the start is c_j = (j + 1/2) * 1.9375 with midpoints (j + 1) * 1.9375;
+    the sample 1.9375 sits on the first midpoint and goes to the lower cell:
+    after one iteration cell 0 = {0, 1, 1.9375} (mean 2.9375 / 3), cell j >= 1
+    = {2j, 2j + 1} (mean 2j + 1/2).  Then the first midpoint drops to
+    (2.9375/3 + 2.5) / 2 < 1.9375 and the sample moves up: cell 0 = {0, 1}
+    (0.5), cell 1 = {1.9375, 2, 3} (6.9375 / 3 = 2.3125), and nothing moves
+    after that."""
+    u = np.concatenate([np.arange(32), [1.9375]]).astype(F32)
+    one, _ = O.lloyd_max_16(u, iters=1)
+    want1 = np.array([2.9375 / 3] + [2 * j + 0.5 for j in range(1, 16)])
+    assert np.array_equal(one, want1.astype(F32))
+    cb, hist = O.lloyd_max_16(u, iters=100)
+    want = np.array([0.5, 2.3125] + [2 * j + 0.5 for j in range(2, 16)])
+    assert np.array_equal(cb, want.astype(F32))
+    assert len(hist) == 3                     # two moves, then a pass that changes nothing
+
+
 def test_w4a8_encode_weight_error_near_page_figure():
     facts = _golden("page_facts.json")
     L = si.random_layer(1, 1024, 256, seed=8)
