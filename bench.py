@@ -17,7 +17,8 @@ Also measured in the same run, each by replaying a HIP graph of repeated
 calls and timing it with HIP events on the launch stream:
   * the GEMM kernel alone (roofline: int8 MFMA peak 5.0 POPS dense) and the
     activation kernel alone (roofline: HBM 8 TB/s);
-  * every other row of the hot path: DiT W2, text-encoder gate/up and down
+  * every other row of the hot path (the W4A8 layer's weight encoded from
+    its bf16 values by the library's GPU encoder): DiT W2, text-encoder gate/up and down
     at M=76 (weight-stream GB/s with cold weights cycled through 48 copies,
     more than twice the 256 MB last-level cache) and M=1220, the
     int8_tensorwise V/O and K=2688 layers, the W4A8 codebook layer, and the
@@ -98,11 +99,23 @@ class Layer:
         self.bias = None
         if L.bias is not None:
             self.bias = torch.from_numpy(L.bias.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.encode_ms = None
         if kind == 2:
-            idx, s_rel, cb, s_ch = si.random_w4a8_format(L.N, L.K, seed=0)
-            p = crp.pack_weight_w4a8(torch.from_numpy(idx).to(dev), torch.from_numpy(s_rel).to(dev),
-                                     torch.from_numpy(cb).to(dev), L.N, L.K)
-            s = torch.from_numpy(s_ch).to(dev)
+            # the layer's own weight, encoded on the GPU (Lloyd-Max codebook,
+            # E4M3 group scales, channel scales), then laid out for the GEMM
+            w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
+            ews = torch.empty(crp.encode_w4a8_workspace_bytes(L.N, L.K), dtype=torch.uint8, device=dev)
+            crp.encode_w4a8(w, workspace=ews)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            idx, s_rel, cb, s_ch = crp.encode_w4a8(w, workspace=ews)
+            e1.record()
+            torch.cuda.synchronize()
+            self.encode_ms = e0.elapsed_time(e1)
+            del ews, w
+            p = crp.pack_weight_w4a8(idx, s_rel, cb, L.N, L.K)
+            s = s_ch
         else:
             w = torch.from_numpy(L.w.view(np.int16)).view(torch.bfloat16).to(dev)
             p, s = {0: crp.pack_weight_w4, 1: crp.pack_weight_int8tw, 3: crp.pack_weight_int8rot,
@@ -205,6 +218,8 @@ def measure_row(torch, lay: Layer, cold: bool, reps: int):
     out["linear_alg_gbs"] = lay.linear_bytes() / (out["linear_us"] * 1e-6) / 1e9
     out["quant_gbs"] = lay.quant_bytes() / (out["quant_us"] * 1e-6) / 1e9
     out["cold_weights"] = bool(cold)
+    if lay.encode_ms is not None:
+        out["encode_ms"] = lay.encode_ms     # offline: the GPU encoder of this layer's weight
     out["shape"] = {"M": lay.M, "K": lay.K, "N": lay.N}
     return out
 

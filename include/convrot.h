@@ -222,6 +222,38 @@ cr_status cr_pack_weight_w4a8(const void* idx, const void* s_rel_e4m3,
                               const float* codebook, int N, int K, void* w_packed,
                               hipStream_t stream);
 
+/* On-GPU encoder of the W4A8 format ([REB] "What's inside a file": 4-bit
+ * codebook indices, an fp8 scale per group of 16 along K, a scale per output
+ * channel, 16 Lloyd-Max levels fit to the tensor).  Offline conversion of a
+ * bf16 weight [N,K] (K % 256 == 0, N*K <= 2^28):
+ *   W~ = each 256-block of each row rotated as in cr_pack_weight_w4;
+ *   s_channel[n] = absmax_k |W~[n,k]| / 127;
+ *   s_rel[n,g] = E4M3 of min(absmax over the 16-group g of |W~| / s_channel[n],
+ *                127), nearest with ties to the even code (0 if s_channel = 0);
+ *   u = W~ / fl(e4m3(s_rel) * s_channel), 0 where that product is 0;
+ *   codebook: 16-level Lloyd-Max fit of all u, levels starting evenly over
+ *     [min u, max u] (float64), each iteration moving every non-empty cell's
+ *     level to the exact mean of its samples (sums of rint(u * 2^24) as
+ *     integers, one float64 division, times 2^-24), cells bounded by the
+ *     midpoints of adjacent levels (a sample on one goes to the lower cell),
+ *     levels sorted after each iteration; stops when no level moves or after
+ *     `iters` (1..1000) iterations; the codebook is the levels rounded to
+ *     float32;
+ *   idx[n,k] = the cell of u[n,k] by the float64 midpoints of the float32
+ *     codebook.
+ * Every quantity is one definite value whatever the launch shape (integer
+ * sums are exact), so the output is reproducible bit for bit.
+ *   w_bf16     [N,K] bf16 (in)
+ *   idx        [N,K/2] uint8 (out), low nibble = even k, as cr_pack_weight_w4a8 takes it
+ *   s_rel_e4m3 [N,K/16] uint8 (out)
+ *   codebook   16 float (out)
+ *   s_channel  [N] float (out)
+ *   ws/ws_bytes at least cr_encode_w4a8_workspace_bytes(N,K) (~4 N K bytes). */
+size_t cr_encode_w4a8_workspace_bytes(int N, int K);
+cr_status cr_encode_w4a8(const void* w_bf16, int N, int K, int iters, void* idx, void* s_rel_e4m3,
+                         float* codebook, float* s_channel, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* y = W4A8 linear: rotated per-row int8 activations (absmax/127) times the
  * decoded int8 weight w8[n,k] = T[s_rel[n,k/16]][idx[n,k]], int32 accumulation,
  * epilogue with s_channel[n] (float [N]) in place of s_w. */
@@ -306,6 +338,10 @@ cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int
  * quantiser computes it. */
 cr_status cr_dbg_silu_mul(const void* g_bf16, const void* u_bf16, size_t n, void* h_bf16,
                           hipStream_t stream);
+
+/* E4M3FN codes of n non-negative floats (at most 448), nearest with ties to
+ * the even code, as the W4A8 encoder rounds its group scales. */
+cr_status cr_dbg_e4m3_encode(const float* v, size_t n, void* codes, hipStream_t stream);
 
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */

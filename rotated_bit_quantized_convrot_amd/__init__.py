@@ -35,6 +35,7 @@ __all__ = [
     "PackedWeight", "pack_linear", "linear",
     "probe_mfma_i8", "probe_read", "probe_copy", "probe_wall_clock_khz",
     "linear_w4a4_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "encode_w4a8", "encode_w4a8_workspace_bytes", "dbg_e4m3_encode",
 ]
 
 W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
@@ -58,6 +59,7 @@ EXPORTS = [
     # measurement probes (include/convrot_probe.h)
     "cr_probe_mfma_i8", "cr_probe_read", "cr_probe_copy", "cr_probe_wall_clock_khz",
     "cr_linear_w4a4_noalloc",
+    "cr_encode_w4a8_workspace_bytes", "cr_encode_w4a8", "cr_dbg_e4m3_encode",
 ]
 
 
@@ -97,6 +99,9 @@ def lib() -> ctypes.CDLL:
         "cr_dbg_silu_mul": (i, [vp, vp, sz, vp, vp]),
         "cr_linear_w4a4": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a4_noalloc": (i, [vp, i, i, vp, vp, i, vp, vp, vp]),
+        "cr_encode_w4a8_workspace_bytes": (sz, [i, i]),
+        "cr_encode_w4a8": (i, [vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
+        "cr_dbg_e4m3_encode": (i, [vp, sz, vp, vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_status_str": (ctypes.c_char_p, [i]),
@@ -228,6 +233,42 @@ def pack_weight_w4a8(idx: torch.Tensor, s_rel: torch.Tensor, codebook: torch.Ten
         _check(lib().cr_pack_weight_w4a8(_ptr(idx), _ptr(s_rel), _ptr(codebook), N, K, None, None) or 2)
     out = _empty_u8(nb, idx.device)
     _check(lib().cr_pack_weight_w4a8(_ptr(idx), _ptr(s_rel), _ptr(codebook), N, K, _ptr(out), _stream()))
+    return out
+
+
+def encode_w4a8_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().cr_encode_w4a8_workspace_bytes(N, K))
+
+
+def encode_w4a8(w: torch.Tensor, iters: int = 100, workspace=None):
+    """bf16 [N,K] -> the stored W4A8 tensors (idx uint8 [N,K/2], s_rel e4m3
+    uint8 [N,K/16], codebook float32 [16], s_channel float32 [N]), encoded on
+    the GPU with at most ``iters`` Lloyd-Max iterations."""
+    _dev(w, "w", torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    need = encode_w4a8_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = _empty_u8(max(need, 256), w.device)
+    else:
+        _dev(workspace, "workspace", torch.uint8)
+        _same_device(w, workspace=workspace)
+    idx = torch.empty((N, max(K // 2, 1)), dtype=torch.uint8, device=w.device)
+    s_rel = torch.empty((N, max(K // 16, 1)), dtype=torch.uint8, device=w.device)
+    cb = torch.empty(16, dtype=torch.float32, device=w.device)
+    sch = torch.empty(max(N, 1), dtype=torch.float32, device=w.device)
+    _check(lib().cr_encode_w4a8(_ptr(w), N, K, iters, _ptr(idx), _ptr(s_rel), _ptr(cb), _ptr(sch),
+                                _ptr(workspace), workspace.numel(), _stream()))
+    return idx, s_rel, cb, sch[:N]
+
+
+def dbg_e4m3_encode(v: torch.Tensor) -> torch.Tensor:
+    """E4M3FN codes (uint8) of non-negative float32 values <= 448, as the
+    encoder rounds its group scales."""
+    _dev(v, "v", torch.float32)
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(lib().cr_dbg_e4m3_encode(_ptr(v), v.numel(), _ptr(out), _stream()))
     return out
 
 

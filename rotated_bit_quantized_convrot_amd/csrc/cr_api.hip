@@ -458,6 +458,45 @@ cr_status cr_pack_weight_w4a8(const void* idx, const void* s_rel_e4m3, const flo
                       "W4A8 weight packing");
 }
 
+static cr_status check_encode_shape(int N, int K) {
+    cr_status s;
+    if ((s = check_nk(CR_W4A8, N, K)) != CR_OK) return s;
+    if ((size_t)N * (size_t)K > ((size_t)1 << 28))
+        return fail(CR_ERR_SHAPE, "N*K = %zu exceeds 2^28 (the exact integer sums of the codebook fit)",
+                    (size_t)N * (size_t)K);
+    return CR_OK;
+}
+
+size_t cr_encode_w4a8_workspace_bytes(int N, int K) {
+    if (check_encode_shape(N, K) != CR_OK) return 0;
+    return cr::encode_w4a8_workspace(N, K);
+}
+
+cr_status cr_encode_w4a8(const void* w_bf16, int N, int K, int iters, void* idx, void* s_rel_e4m3,
+                         float* codebook, float* s_channel, void* ws, size_t ws_bytes, hipStream_t stream) {
+    cr_status s;
+    if ((s = check_encode_shape(N, K)) != CR_OK) return s;
+    if (iters < 1 || iters > 1000) return fail(CR_ERR_SHAPE, "iters=%d (need 1..1000)", iters);
+    if (!w_bf16 || !idx || !s_rel_e4m3 || !codebook || !s_channel || !ws) return fail(CR_ERR_NULL, "NULL argument");
+    if (!aligned16(w_bf16) || !aligned16(ws)) return fail(CR_ERR_ALIGN, "weight or workspace not 16-byte aligned");
+    const size_t need = cr::encode_w4a8_workspace(N, K);
+    if (ws_bytes < need) return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::launch_encode_w4a8(static_cast<const uint16_t*>(w_bf16), N, K, iters,
+                                             static_cast<uint8_t*>(idx), static_cast<uint8_t*>(s_rel_e4m3), codebook,
+                                             s_channel, ws, stream),
+                      "W4A8 encoder");
+}
+
+cr_status cr_dbg_e4m3_encode(const float* v, size_t n, void* codes, hipStream_t stream) {
+    if (n == 0) return ok();
+    if (!v || !codes) return fail(CR_ERR_NULL, "NULL argument");
+    if (n > ((size_t)1 << 32)) return fail(CR_ERR_SHAPE, "n=%zu too large", n);
+    cr_status s;
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::launch_e4m3_encode(v, n, static_cast<uint8_t*>(codes), stream), "e4m3 encode");
+}
+
 cr_status cr_pack_weight_int8rot(const void* w_bf16, int N, int K, void* w_packed, float* w_scale,
                                  hipStream_t stream) {
     cr_status s = pack_common_checks(CR_INT8ROT, w_bf16, N, K, w_packed, w_scale);

@@ -357,4 +357,66 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     return (c & 0x80u) ? -v : v;
 }
 
+// ---------------------------------------------------------------------------
+// Rows rotated 256-block by 256-block (each block as 256 / GS rotation
+// groups of GS).  One block per row; half-wave h handles 256-blocks h,
+// h + NHW, ... (at most GPL of them), each lane 8 consecutive values.
+// ---------------------------------------------------------------------------
+template <int GPL, int GS = 256>
+struct RotRow {
+    float v[GPL][8];
+
+    // Loads and rotates the row's groups; returns this lane's absmax.
+    __device__ __forceinline__ float load_rotate(const uint16_t* __restrict__ row, int G, int hw,
+                                                 int nhw, int lane32) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GPL; ++i) {
+            const int g = hw + i * nhw;
+            if (g < G) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(row + (size_t)g * 256 + lane32 * 8);
+                v[i][0] = bf16_lo(raw.x); v[i][1] = bf16_hi(raw.x);
+                v[i][2] = bf16_lo(raw.y); v[i][3] = bf16_hi(raw.y);
+                v[i][4] = bf16_lo(raw.z); v[i][5] = bf16_hi(raw.z);
+                v[i][6] = bf16_lo(raw.w); v[i][7] = bf16_hi(raw.w);
+                fwht8<GS>(v[i], lane32);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+            }
+        }
+        return amax;
+    }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Max over the block (blockDim.x <= 1024); every thread gets the result.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const int nw = (blockDim.x + 63) >> 6;
+    float r = 0.0f;
+    for (int i = 0; i < nw; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+
+// Threads of a one-block-per-row rotation kernel for G 256-blocks per row
+// (RotRow): up to 16 half-waves, GPL 256-blocks each (a power of two).
+inline int rot_threads(int G, int* gpl) {
+    int nhw = G < 16 ? G : 16;
+    int per = (G + nhw - 1) / nhw;
+    int g = 1;
+    while (g < per) g <<= 1;
+    *gpl = g;
+    return round_up(nhw * 32, 64);      // whole waves (half-waves past G idle)
+}
+
 }  // namespace cr

@@ -92,6 +92,16 @@ hipError_t launch_w4a8_expand(const uint8_t* packed, int N, int K, uint8_t* out,
 hipError_t launch_unpack_weight(int kind, const uint8_t* packed, int N, int K, int8_t* out,
                                 hipStream_t st);
 
+// W4A8 encoder (cr_encode.hip): bf16 weight [N, K] (K % 256 == 0) to the
+// stored W4A8 tensors (idx [N, K/2], s_rel [N, K/16], codebook [16],
+// s_channel [N]), at most `iters` Lloyd-Max iterations; workspace of
+// encode_w4a8_workspace(N, K) bytes.
+size_t encode_w4a8_workspace(int N, int K);
+hipError_t launch_encode_w4a8(const uint16_t* w, int N, int K, int iters, uint8_t* idx, uint8_t* s_rel,
+                              float* codebook, float* s_channel, void* ws, hipStream_t st);
+// E4M3FN codes (nearest, ties to the even code) of n non-negative floats <= 448.
+hipError_t launch_e4m3_encode(const float* v, size_t n, uint8_t* out, hipStream_t st);
+
 struct GemmArgs {
     int kind;              // WKind
     const int8_t* qx;      // [M, Kp]
