@@ -115,7 +115,7 @@ int wkind(int kind) {
 // against several weights (with the workspace sized for the largest need
 // over their N).
 struct WsLayout {
-    size_t qx, sx, ra, part, wexp, quant_end, total;
+    size_t qx, sx, ra, sync, part, wexp, quant_end, total;
 };
 
 // W4A8 at large M: the GEMM's per-16-weight table decode is the costly part
@@ -135,7 +135,8 @@ WsLayout ws_layout(int kind, int M, int N, int K) {
     l.qx = 0;
     l.sx = a256(cr::act_bytes(wk, M, K));
     l.ra = l.sx + a256((size_t)M * 4);
-    l.part = l.ra + (cr::act_packed(wk) ? a256((size_t)M * 4) : 0);
+    l.sync = l.ra + (cr::act_packed(wk) ? a256((size_t)M * 4) : 0);
+    l.part = l.sync + (size_t)cr::kSyncWords * 4;
     l.quant_end = l.part;
     const cr::SmallPlan sp = cr::plan_small(gk, M, N, K);
     l.wexp = l.part + a256(sp.use ? sp.part_bytes : cr::plan_big(gk, M, N, K).part_bytes);
@@ -164,7 +165,8 @@ cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t
     hipError_t e = cr::launch_quant_act(wkind(kind), group_of(kind), static_cast<const uint16_t*>(x), M, K,
                                         kp_of(kind, K),
                                         reinterpret_cast<int8_t*>(w + l.qx), reinterpret_cast<float*>(w + l.sx),
-                                        reinterpret_cast<int32_t*>(w + l.ra), cr::act_packed(wkind(kind)), st);
+                                        reinterpret_cast<int32_t*>(w + l.ra), cr::act_packed(wkind(kind)),
+                                        reinterpret_cast<uint32_t*>(w + l.sync), st);
     return launch_err(e, "activation quantisation");
 }
 
@@ -193,6 +195,7 @@ cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale
     a.y = static_cast<uint16_t*>(y);
     a.acc_out = acc;
     a.part = reinterpret_cast<int32_t*>(w + l.part);
+    a.sync = reinterpret_cast<uint32_t*>(w + l.sync);
     if (cr::act_packed(a.kind)) {
         a.ra = reinterpret_cast<const int32_t*>(w + l.ra);
         a.cw = reinterpret_cast<const int32_t*>(a.wp + cr::w4_cw_offset(N, K));
@@ -329,7 +332,8 @@ cr_status cr_mlp_w4a4(const void* x_bf16, int M, int K, const void* wg_packed, c
     s = launch_err(cr::launch_quant_swiglu(reinterpret_cast<const uint16_t*>(w + l.g),
                                            reinterpret_cast<const uint16_t*>(w + l.u), M, F,
                                            reinterpret_cast<int8_t*>(wb + lb.qx), reinterpret_cast<float*>(wb + lb.sx),
-                                           reinterpret_cast<int32_t*>(wb + lb.ra), true, stream),
+                                           reinterpret_cast<int32_t*>(wb + lb.ra), true,
+                                           reinterpret_cast<uint32_t*>(wb + lb.sync), stream),
                    "MLP activation quantisation");
     if (s != CR_OK) return s;
     return gemm_phase(CR_W4A4, M, F, wd_packed, wd_scale, N, nullptr, y_bf16, nullptr, wb, lb.total, stream);
@@ -357,7 +361,7 @@ cr_status cr_dbg_quant_swiglu(const void* g_bf16, const void* u_bf16, int M, int
         return fail(CR_ERR_ALIGN, "pointer not 16-byte aligned");
     if ((s = check_device()) != CR_OK) return s;
     return launch_err(cr::launch_quant_swiglu(static_cast<const uint16_t*>(g_bf16), static_cast<const uint16_t*>(u_bf16),
-                                              M, K, static_cast<int8_t*>(codes), scales, nullptr, false, stream),
+                                              M, K, static_cast<int8_t*>(codes), scales, nullptr, false, nullptr, stream),
                       "MLP activation quantisation");
 }
 
@@ -606,7 +610,7 @@ cr_status cr_dbg_quant_act(int kind, const void* x_bf16, int M, int K, void* cod
     if ((s = check_device()) != CR_OK) return s;
     const int wk = wkind(kind);
     return launch_err(cr::launch_quant_act(wk, group_of(kind), static_cast<const uint16_t*>(x_bf16), M, K, K,
-                                           static_cast<int8_t*>(codes), scales, nullptr, false, stream),
+                                           static_cast<int8_t*>(codes), scales, nullptr, false, nullptr, stream),
                       "activation quantisation");
 }
 

@@ -40,6 +40,13 @@ namespace cr {
 // (4-bit tiles, rows = m, activation nibble forms), the others as int8.
 // ---------------------------------------------------------------------------
 constexpr int SM_W = 8;   // waves per block
+constexpr int SM_MAX_SPLITS = 16;   // K slices across blocks, at most
+
+// Cache policy of a buffer access at device scope (the SC1 bit): a store is
+// written through to the level every XCD reads, a load does not take a line
+// another XCD may have left stale.
+constexpr int kDeviceScope = 16;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // Loads of one chunk: NT weight fragments + MT activation fragments.
 template <int WK> struct SmW;
@@ -223,6 +230,12 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
 
     const Epi epi = make_epi(p);
     const float sw0 = (wk_chan(WK) || acc_mode) ? 0.0f : p.wscale[0];
+    // K split across blocks: with arrival counters (in-kernel completion) the
+    // last of a weight block's `splits` blocks to arrive adds the others'
+    // partial tiles and runs the epilogue; without, k_small_reduce does.
+    const bool inkernel = splits > 1 && p.sync != nullptr && (int)gridDim.x <= kSyncWords;
+    const size_t slice_i4 = (size_t)nt16 * MT * 64;                    // int4 per K slice
+    int4 keep[QPW];
 #pragma unroll
     for (int k = 0; k < QPW; ++k) {
         const int q = wave + SM_W * k;
@@ -233,12 +246,78 @@ __global__ void __launch_bounds__(512) k_gemm_small(GemmArgs p, int splits, int 
             const int4 v = red[(w * NT * MT + q) * 64 + lane];
             sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
         }
+        keep[k] = sum;
         const int t = q / MT, j = q % MT;
         const int nt = blockIdx.x * NT + t;
         if (nt >= nt16) continue;
         if (splits > 1) {
-            reinterpret_cast<int4*>(p.part)[(((size_t)s * nt16 + nt) * MT + j) * 64 + lane] = sum;
+            const size_t at = ((size_t)nt * MT + j) * 64 + lane;
+            if (inkernel) {
+                // device-scope store: written through to where every XCD reads it
+                const auto rs = buf_rsrc(reinterpret_cast<int4*>(p.part) + (size_t)s * slice_i4,
+                                         (uint32_t)(slice_i4 * 16));
+                __builtin_amdgcn_raw_buffer_store_b128(v4u{(uint32_t)sum.x, (uint32_t)sum.y, (uint32_t)sum.z,
+                                                           (uint32_t)sum.w},
+                                                       rs, (int)(at * 16), 0, kDeviceScope);
+            } else {
+                reinterpret_cast<int4*>(p.part)[(size_t)s * slice_i4 + at] = sum;
+            }
             continue;
+        }
+        const int m = j * 16 + r16, n = nt * 16 + 4 * g;
+        if (m >= p.M || n >= p.N) continue;
+        if (acc_mode)
+            store4<WK, true>(epi, m, n, 0.0f, 0.0f, sum.x, sum.y, sum.z, sum.w);
+        else if (pre[k].full)
+            store4_pre<WK>(epi, pre[k], m, n, sum.x, sum.y, sum.z, sum.w);
+        else
+            store4<WK, false>(epi, m, n, p.sx[m], sw0, sum.x, sum.y, sum.z, sum.w);
+    }
+    if (!inkernel) return;
+    // Every wave's partial stores are acknowledged at device scope before the
+    // block counts itself in; the block that brings the count to `splits` is
+    // the last, resets the counter for the next GEMM on this workspace and
+    // finishes the tiles.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(&p.sync[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) __hip_atomic_store(&p.sync[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // device-scope loads (the other XCDs' stores, not a stale cached copy),
+    // all issued before the first is used; the other slices' tiles in a
+    // fixed order (integer sums: the order does not change the result)
+    const auto rs_part = buf_rsrc(p.part, (uint32_t)(slice_i4 * 16 * splits));
+    v4u oth[QPW][SM_MAX_SPLITS];
+#pragma unroll
+    for (int s2 = 0; s2 < SM_MAX_SPLITS; ++s2) {
+#pragma unroll
+        for (int k = 0; k < QPW; ++k) {
+            const int q = wave + SM_W * k;
+            const int nt = blockIdx.x * NT + q / MT;
+            oth[k][s2] = v4u{0u, 0u, 0u, 0u};
+            if (s2 < splits && s2 != s && q < NT * MT && nt < nt16) {
+                const size_t at = ((size_t)nt * MT + q % MT) * 64 + lane;
+                oth[k][s2] = __builtin_amdgcn_raw_buffer_load_b128(rs_part, (int)((s2 * slice_i4 + at) * 16), 0,
+                                                                   kDeviceScope);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < QPW; ++k) {
+        const int q = wave + SM_W * k;
+        if (q >= NT * MT) break;
+        const int t = q / MT, j = q % MT;
+        const int nt = blockIdx.x * NT + t;
+        if (nt >= nt16) continue;
+        int4 sum = keep[k];
+#pragma unroll
+        for (int s2 = 0; s2 < SM_MAX_SPLITS; ++s2) {
+            sum.x += (int)oth[k][s2].x; sum.y += (int)oth[k][s2].y;
+            sum.z += (int)oth[k][s2].z; sum.w += (int)oth[k][s2].w;
         }
         const int m = j * 16 + r16, n = nt * 16 + 4 * g;
         if (m >= p.M || n >= p.N) continue;
@@ -306,7 +385,6 @@ static hipError_t launch_small_reduce(const GemmArgs& a, int splits, int mt, int
 // point holds SM_W * NT * MT KiB).
 __host__ __device__ constexpr int small_nt(int mt) { return mt <= 5 ? 3 : 2; }
 constexpr int SM_CPW_MAX = 8;
-constexpr int SM_MAX_SPLITS = 16;
 
 // VGPRs of one step's loads; a wave holds at most 128 of them.
 __host__ __device__ constexpr int small_regs_per_chunk(int wk, int mt, int nt) {
@@ -345,7 +423,10 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
         const double bytes = (double)cps * 64.0 * (sp.nt * 16 * wbytes + sp.mt * 16 * abytes);
         const double mfma = 2.0 * cpw * ck * sp.nt * sp.mt * 16.0;
         double cost = rounds * (std::max(bytes / 64.0, mfma) + 2000.0);
-        if (splits > 1) cost += (double)splits * sp.mt * 16 * N * 8 / 4000.0 + 3000.0;
+        // (the last-arriving block finishes the tiles: ~800 cycles for its
+        // dependent reads; a second kernel where the counters cannot cover
+        // the blocks: ~3000)
+        if (splits > 1) cost += (double)splits * sp.mt * 16 * N * 8 / 4000.0 + (nblk <= kSyncWords ? 800.0 : 3000.0);
         if (cost < best) {
             best = cost;
             sp.splits = splits;
@@ -378,7 +459,9 @@ static hipError_t launch_small_c(const GemmArgs& a, const SmallPlan& sp, hipStre
     }
     const int acc_mode = a.acc_out != nullptr ? 1 : 0;
     kern<<<dim3(sp.nblk, sp.splits), dim3(64 * SM_W), sp.lds, st>>>(a, sp.splits, sp.cps, acc_mode);
-    if (sp.splits > 1) return launch_small_reduce<WK>(a, sp.splits, MT, acc_mode, st);
+    // the kernel completes split tiles itself when it has the arrival counters
+    if (sp.splits > 1 && (a.sync == nullptr || sp.nblk > kSyncWords))
+        return launch_small_reduce<WK>(a, sp.splits, MT, acc_mode, st);
     return hipGetLastError();
     }
 }

@@ -64,14 +64,19 @@ __host__ __device__ inline size_t w4a8_bytes(int N, int K) { return w4a8_table_o
 // Sylvester Hadamard over groups of 256, 64 or 16, or kRotRegular (1) for the
 // group-256 regular Hadamard; the other kinds rotate, if at all, with the
 // group-256 Sylvester matrix.
+//
+// `sync` (nullable): kSyncWords uint32 arrival counters of the split-K GEMMs
+// that read this quantisation; the kernel zeroes them (the GEMMs leave them
+// zero again), so a workspace needs no initialisation.
+constexpr int kSyncWords = 4096;
 hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, int32_t* ra, bool packed, hipStream_t st);
+                            float* sx, int32_t* ra, bool packed, uint32_t* sync, hipStream_t st);
 
 // W4A4 activations (group-256 Sylvester rotation) of h = silu(g) * u, the
 // gated MLP's input to its down projection, from the bf16 gate and up
 // outputs g, u [M, K]; outputs as launch_quant_act(WK_W4, 256, ...).
 hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
-                               int32_t* ra, bool packed, hipStream_t st);
+                               int32_t* ra, bool packed, uint32_t* sync, hipStream_t st);
 
 // h = silu(g) * u of n bf16 pairs, as launch_quant_swiglu forms it.
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, size_t n, uint16_t* h, hipStream_t st);
@@ -113,6 +118,7 @@ struct GemmArgs {
     uint16_t* y;           // [M, N] bf16 (null when acc_out is set)
     int32_t* acc_out;      // [M, N] int32 accumulators instead of y
     int32_t* part;         // split-K partial sums (workspace)
+    uint32_t* sync;        // split-K arrival counters (kSyncWords, zero on entry and on exit; workspace)
     const int32_t* ra;     // W4A4: activation high-nibble code sums [M]
     const int32_t* cw;     // W4A4: weight high-nibble code sums [Np]
 };

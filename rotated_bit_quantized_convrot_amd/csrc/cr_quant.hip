@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
 }
 
 // Codes of a lane's 16 rotated values (unscaled, sign-tracked), see below.
+// The split-K arrival counters of the GEMMs that read this quantisation
+// start at zero: the first block clears them (the GEMM kernels run after this
+// kernel on the same stream).
+__device__ __forceinline__ void zero_sync(uint32_t* __restrict__ sync) {
+    if (sync != nullptr && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) sync[i] = 0u;
+}
+
 template <int QMAX, int LO, int HI, int GS>
 __device__ __forceinline__ void codes16(const float (&v)[16], bool fast, float rinv, float sigma, float s_u,
                                         float s, float (&r)[16]) {
@@ -135,9 +143,11 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ x, const uin
 template <int GPL, int QMAX, int LO, int HI, bool PACKED, int GS, bool GLU>
 __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
                                                         int M, int K, int seg_log2, int8_t* __restrict__ qx,
-                                                        float* __restrict__ sx, int32_t* __restrict__ ra) {
+                                                        float* __restrict__ sx, int32_t* __restrict__ ra,
+                                                        uint32_t* __restrict__ sync) {
     __shared__ float red[16];
     __shared__ int ired[16];
+    zero_sync(sync);
     const int tid = threadIdx.x;
     int m, l, seg;
     if (seg_log2 >= 0) {
@@ -225,9 +235,10 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
 template <int GPL, int GS, bool GLU>
 __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
                                                          int M, int K, int8_t* __restrict__ qx, float* __restrict__ sx,
-                                                         int32_t* __restrict__ ra) {
+                                                         int32_t* __restrict__ ra, uint32_t* __restrict__ sync) {
     __shared__ float redm[16][4];
     __shared__ int reds[16][4];
+    zero_sync(sync);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6, nw = blockDim.x >> 6;
     const int r = lane >> 4, j = lane & 15;
@@ -285,8 +296,9 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
 // in [K, Kp).  Two passes over the row (the second one hits the cache).
 __global__ void __launch_bounds__(256) k_quant_act_plain(const uint16_t* __restrict__ x, int M,
                                                          int K, int Kp, int8_t* __restrict__ qx,
-                                                         float* __restrict__ sx) {
+                                                         float* __restrict__ sx, uint32_t* __restrict__ sync) {
     __shared__ float red[16];
+    zero_sync(sync);
     const int m = blockIdx.x;
     const uint16_t* row = x + (size_t)m * K;
     int8_t* out = qx + (size_t)m * Kp;
@@ -326,13 +338,13 @@ __global__ void __launch_bounds__(256) k_quant_act_plain(const uint16_t* __restr
 
 template <int QMAX, int LO, int HI, bool PACKED, int GS = 256, bool GLU = false>
 static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K, int8_t* qx, float* sx, int32_t* ra,
-                             hipStream_t st) {
+                             uint32_t* sync, hipStream_t st) {
     const int T = K / 16;              // lanes per row
     if (T <= 64) {
         int lg = 4;
         while ((1 << lg) < T) ++lg;
         const int rows = 256 >> lg;
-        k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, u, M, K, lg, qx, sx, ra);
+        k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, u, M, K, lg, qx, sx, ra, sync);
         return hipGetLastError();
     }
     int gpl = 1;
@@ -345,9 +357,9 @@ static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K,
     const int threads = round_up((T + gpl - 1) / gpl, 64);
     dim3 grid(M), block(threads);
     switch (gpl) {
-        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
-        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
-        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra); break;
+        case 1: k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra, sync); break;
+        case 2: k_quant_act_rot<2, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra, sync); break;
+        case 4: k_quant_act_rot<4, QMAX, LO, HI, PACKED, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, -1, qx, sx, ra, sync); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -356,7 +368,7 @@ static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K,
 // W4A4 activations with rotation GS (GLU: of silu(x) * u).
 template <int GS, bool GLU = false>
 static hipError_t launch_w4_act(const uint16_t* x, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
-                                int32_t* ra, bool packed, hipStream_t st) {
+                                int32_t* ra, bool packed, uint32_t* sync, hipStream_t st) {
     const int G = K >> 8;
     // four rows per block where there are rows enough to fill the chip
     // with such blocks (at smaller M one row per block keeps more lanes busy;
@@ -372,33 +384,33 @@ static hipError_t launch_w4_act(const uint16_t* x, const uint16_t* u, int M, int
         const int nw = (G + gpl - 1) / gpl;
         const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
         switch (gpl) {
-            case 1: k_quant_w4_rows4<1, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
-            case 2: k_quant_w4_rows4<2, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
-            case 4: k_quant_w4_rows4<4, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra); break;
+            case 1: k_quant_w4_rows4<1, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
+            case 2: k_quant_w4_rows4<2, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
+            case 4: k_quant_w4_rows4<4, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
-    return packed ? launch_rot<7, -8, 7, true, GS, GLU>(x, u, M, K, qx, sx, ra, st)
-                  : launch_rot<7, -8, 7, false, GS, GLU>(x, u, M, K, qx, sx, nullptr, st);
+    return packed ? launch_rot<7, -8, 7, true, GS, GLU>(x, u, M, K, qx, sx, ra, sync, st)
+                  : launch_rot<7, -8, 7, false, GS, GLU>(x, u, M, K, qx, sx, nullptr, sync, st);
 }
 
 hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K, int Kp, int8_t* qx,
-                            float* sx, int32_t* ra, bool packed, hipStream_t st) {
+                            float* sx, int32_t* ra, bool packed, uint32_t* sync, hipStream_t st) {
     if (kind == WK_W4) {
         if (packed && ra == nullptr) return hipErrorInvalidValue;
         switch (group) {
-            case 256: return launch_w4_act<256>(x, nullptr, M, K, qx, sx, ra, packed, st);
-            case 64: return launch_w4_act<64>(x, nullptr, M, K, qx, sx, ra, packed, st);
-            case 16: return launch_w4_act<16>(x, nullptr, M, K, qx, sx, ra, packed, st);
-            case kRotRegular: return launch_w4_act<kRotRegular>(x, nullptr, M, K, qx, sx, ra, packed, st);
+            case 256: return launch_w4_act<256>(x, nullptr, M, K, qx, sx, ra, packed, sync, st);
+            case 64: return launch_w4_act<64>(x, nullptr, M, K, qx, sx, ra, packed, sync, st);
+            case 16: return launch_w4_act<16>(x, nullptr, M, K, qx, sx, ra, packed, sync, st);
+            case kRotRegular: return launch_w4_act<kRotRegular>(x, nullptr, M, K, qx, sx, ra, packed, sync, st);
             default: return hipErrorInvalidValue;
         }
     }
     // W4A8 and ConvRot INT8: rotated, per-row int8
-    if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, nullptr, M, K, qx, sx, nullptr, st);
+    if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, nullptr, M, K, qx, sx, nullptr, sync, st);
     // two waves per row when four per row would exceed what the chip holds at once
-    k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx);
+    k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx, sync);
     return hipGetLastError();
 }
 
@@ -417,9 +429,9 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, size_t n, uint1
 }
 
 hipError_t launch_quant_swiglu(const uint16_t* g, const uint16_t* u, int M, int K, int8_t* qx, float* sx,
-                               int32_t* ra, bool packed, hipStream_t st) {
+                               int32_t* ra, bool packed, uint32_t* sync, hipStream_t st) {
     if (packed && ra == nullptr) return hipErrorInvalidValue;
-    return launch_w4_act<256, true>(g, u, M, K, qx, sx, ra, packed, st);
+    return launch_w4_act<256, true>(g, u, M, K, qx, sx, ra, packed, sync, st);
 }
 
 // ---------------------------------------------------------------------------
