@@ -32,7 +32,10 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates no memory, keeps no device state and never synchronises.
+ *     allocates no memory and never synchronises.  Its only device state is
+ *     the static scratch of cr_linear_w4a4_noalloc (one array per GPU); on
+ *     the host it caches, per device id, whether the device is a gfx950 and
+ *     which kernels have been given their LDS size (set once, idempotent).
  *   - Work is enqueued on `stream` (NULL = the null stream) in order; results
  *     are valid once the stream reaches that point.
  *   - bf16 tensors are row-major uint16 bit patterns; x is [M,K], W is [N,K]

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "convrot.h"
@@ -28,19 +29,20 @@ cr_status ok() {
     return CR_OK;
 }
 
-// 0 = unknown, 1 = gfx950, 2 = other.
-int g_dev_state[64];
+// Per device id: 0 = unknown, 1 = gfx950, 2 = other (set once; calls from
+// several host threads may race to set the same value).
+std::atomic<int> g_dev_state[64];
 
 cr_status check_device() {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0) return fail(CR_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
-    if (dev < 64 && g_dev_state[dev] == 1) return CR_OK;
+    if (dev < 64 && g_dev_state[dev].load(std::memory_order_relaxed) == 1) return CR_OK;
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail(CR_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < 64) g_dev_state[dev] = good ? 1 : 2;
+    if (dev < 64) g_dev_state[dev].store(good ? 1 : 2, std::memory_order_relaxed);
     if (!good) return fail(CR_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
     return CR_OK;
 }
