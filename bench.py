@@ -75,6 +75,8 @@ def row_specs():
         "dit_w1_group64": dict(kind=4, gen=lambda: si.dit_w1(), cold=False),
         "dit_w1_group16": dict(kind=5, gen=lambda: si.dit_w1(), cold=False),
         "dit_w1_regular": dict(kind=6, gen=lambda: si.dit_w1(), cold=False),
+        "te_gate_up_M1": dict(kind=0, gen=lambda: si.te_gate_up(1), cold=True),
+        "te_down_M1": dict(kind=0, gen=lambda: si.te_down(1), cold=True),
         "te_gate_up_M76": dict(kind=0, gen=lambda: si.te_gate_up(76), cold=True),
         "te_down_M76": dict(kind=0, gen=lambda: si.te_down(76), cold=True),
         "te_gate_up_M1220": dict(kind=0, gen=lambda: si.te_gate_up(1220), cold=False),
@@ -253,7 +255,9 @@ def measure_mlp(torch, crp, M: int, cold: bool, reps: int):
     ops = 2.0 * M * K * F * 2 + 2.0 * M * F * N
     wbytes = (2 * F * K + N * F) / 2
     return {"mlp_us": us, "tops": ops / (us * 1e-6) / 1e12, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
-            "cold_weights": bool(cold), "shape": {"M": M, "K": K, "F": F, "N": N}, "launches": 5}
+            "cold_weights": bool(cold), "shape": {"M": M, "K": K, "F": F, "N": N},
+            # gate and down GEMMs quantise their own inputs at M <= 8
+            "launches": 3 if M <= 8 else 5}
 
 
 # ---------------------------------------------------------------------------
@@ -520,7 +524,7 @@ def main():
         del lay
         torch.cuda.empty_cache()
 
-    for name, M, cold in (("te_mlp_M76", 76, True), ("te_mlp_M1220", 1220, False)):
+    for name, M, cold in (("te_mlp_M1", 1, True), ("te_mlp_M76", 76, True), ("te_mlp_M1220", 1220, False)):
         if args.rows == "all" or name in args.rows.split(","):
             _log(f"row {name}")
             rows[name] = measure_mlp(torch, crp, M, cold, args.repeat)

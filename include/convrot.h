@@ -301,7 +301,10 @@ cr_status cr_gemm_quantized(int kind, int M, int K, const void* w_packed, const 
  * projection.  g and u are the bf16 outputs cr_linear_w4a4 gives; h =
  * bf16(float(g / (1 + exp(-g)) * u)) with the quotient and products in
  * float64 (both roundings to nearest even).  x is quantised once for the
- * gate and up GEMMs.  All launches go on `stream`, none allocates.
+ * gate and up GEMMs.  At M <= 8 (see cr_dbg_fused_config) the gate GEMM
+ * quantises x inside its own launch and the down GEMM forms and quantises
+ * h inside its own: three launches instead of five, same results bit for
+ * bit.  All launches go on `stream`, none allocates.
  *   x_bf16 [M,K]; wg, wu: [F,K] packed + tensor scale; wd: [N,F] packed +
  *   tensor scale; y_bf16 [M,N] (out); ws / ws_bytes: at least
  *   cr_mlp_workspace_bytes(M,K,F,N) (g and u live there).
@@ -345,6 +348,33 @@ cr_status cr_dbg_silu_mul(const void* g_bf16, const void* u_bf16, size_t n, void
 /* E4M3FN codes of n non-negative floats (at most 448), nearest with ties to
  * the even code, as the W4A8 encoder rounds its group scales. */
 cr_status cr_dbg_e4m3_encode(const float* v, size_t n, void* codes, hipStream_t stream);
+
+/* Path selection of the fused small-M W4A4 linear.  cr_linear_w4a4, its
+ * no-allocation variant, cr_dbg_linear_acc(CR_W4A4) and the gate and down
+ * GEMMs of cr_mlp_w4a4 can run as ONE launch each where M <= 128,
+ * K <= 16384, N % 4 == 0 and the small-M plan fits one round of blocks: the
+ * grid's first blocks rotate and quantise the rows of x, or of h for the
+ * down GEMM ([QIE] "Speed": rotation, 4-bit MMA and rescale in one kernel),
+ * while the other blocks load their weight tiles; a GEMM block waits, with a
+ * bounded number of polls, until every row is in.  Results are bit for bit
+ * those of the two-launch path (activation quantiser, then GEMM).
+ *   mode: 1 = fused where it applies and M <= 8 (the default: the range
+ *         where it is measured faster), 2 = fused wherever it applies,
+ *         0 = always two launches; any other value -> CR_ERR_SHAPE.
+ *   spin_limit: polls of the bounded wait for later launches (default
+ *         4194304, seconds of waiting); < 0 keeps the current value.
+ * A GEMM block whose wait runs out writes none of its outputs and counts
+ * one timeout (cr_dbg_fused_timeouts); the producers never wait and come
+ * first in dispatch order, so this takes a stalled device.  At most 1024
+ * fused launches may be in flight at once (a graph holds one of those
+ * counter slots for its lifetime).  The setting is process-wide and read at
+ * each call; for inspection and timing. */
+cr_status cr_dbg_fused_config(int mode, int spin_limit);
+
+/* Number of fused-linear GEMM blocks whose wait ran out since the library
+ * was loaded on the current device (reads a device counter; synchronises
+ * the device).  count: host pointer, out. */
+cr_status cr_dbg_fused_timeouts(uint32_t* count);
 
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */

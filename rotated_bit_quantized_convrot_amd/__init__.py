@@ -36,6 +36,7 @@ __all__ = [
     "probe_mfma_i8", "probe_read", "probe_copy", "probe_wall_clock_khz",
     "linear_w4a4_noalloc", "NOALLOC_SCRATCH_BYTES",
     "encode_w4a8", "encode_w4a8_workspace_bytes", "dbg_e4m3_encode",
+    "dbg_fused_config", "dbg_fused_timeouts",
 ]
 
 W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
@@ -60,6 +61,7 @@ EXPORTS = [
     "cr_probe_mfma_i8", "cr_probe_read", "cr_probe_copy", "cr_probe_wall_clock_khz",
     "cr_linear_w4a4_noalloc",
     "cr_encode_w4a8_workspace_bytes", "cr_encode_w4a8", "cr_dbg_e4m3_encode",
+    "cr_dbg_fused_config", "cr_dbg_fused_timeouts",
 ]
 
 
@@ -102,6 +104,8 @@ def lib() -> ctypes.CDLL:
         "cr_encode_w4a8_workspace_bytes": (sz, [i, i]),
         "cr_encode_w4a8": (i, [vp, i, i, i, vp, vp, vp, vp, vp, sz, vp]),
         "cr_dbg_e4m3_encode": (i, [vp, sz, vp, vp]),
+        "cr_dbg_fused_config": (i, [i, i]),
+        "cr_dbg_fused_timeouts": (i, [vp]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_status_str": (ctypes.c_char_p, [i]),
@@ -270,6 +274,22 @@ def dbg_e4m3_encode(v: torch.Tensor) -> torch.Tensor:
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     _check(lib().cr_dbg_e4m3_encode(_ptr(v), v.numel(), _ptr(out), _stream()))
     return out
+
+
+def dbg_fused_config(mode: int, spin_limit: int = -1) -> None:
+    """Path of the small-M W4A4 linear: 1 = one launch that quantises its own
+    activations where it applies and M <= 8 (the default), 2 = that launch
+    wherever it applies, 0 = always the activation quantiser and the GEMM;
+    ``spin_limit >= 0`` sets the polls of the fused launch's bounded wait."""
+    _check(lib().cr_dbg_fused_config(int(mode), int(spin_limit)))
+
+
+def dbg_fused_timeouts() -> int:
+    """GEMM blocks of the fused linear whose wait ran out, on the current
+    device, since the library was loaded (synchronises the device)."""
+    n = ctypes.c_uint32(0)
+    _check(lib().cr_dbg_fused_timeouts(ctypes.byref(n)))
+    return int(n.value)
 
 
 # ---------------------------------------------------------------------------

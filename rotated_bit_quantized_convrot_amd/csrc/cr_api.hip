@@ -172,20 +172,9 @@ cr_status quantize_phase(int kind, const void* x, int M, int K, void* ws, size_t
     return launch_err(e, "activation quantisation");
 }
 
-// Phase 2: GEMM + epilogue from the workspace.
-cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale, int N, const void* bias,
-                     void* y, int32_t* acc, void* ws, size_t ws_bytes, hipStream_t st) {
-    const WsLayout l = ws_layout(kind, M, N, K);
-    if (ws_bytes < l.total)
-        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
-    char* w = static_cast<char*>(ws);
-    if (w4a8_expands(kind, M)) {
-        cr_status s = launch_err(cr::launch_w4a8_expand(static_cast<const uint8_t*>(wp), N, K,
-                                                        reinterpret_cast<uint8_t*>(w + l.wexp), st),
-                                 "W4A8 weight decode");
-        if (s != CR_OK) return s;
-        wp = w + l.wexp;
-    }
+// Arguments of the GEMM kernels for a linear whose workspace is at w.
+cr::GemmArgs gemm_args(int kind, int M, int K, const void* wp, const float* wscale, int N, const void* bias,
+                       void* y, int32_t* acc, char* w, const WsLayout& l) {
     cr::GemmArgs a{};
     a.kind = gemm_wkind(kind, M);
     a.qx = reinterpret_cast<const int8_t*>(w + l.qx);
@@ -202,7 +191,66 @@ cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale
         a.ra = reinterpret_cast<const int32_t*>(w + l.ra);
         a.cw = reinterpret_cast<const int32_t*>(a.wp + cr::w4_cw_offset(N, K));
     }
+    return a;
+}
+
+// Phase 2: GEMM + epilogue from the workspace.
+cr_status gemm_phase(int kind, int M, int K, const void* wp, const float* wscale, int N, const void* bias,
+                     void* y, int32_t* acc, void* ws, size_t ws_bytes, hipStream_t st) {
+    const WsLayout l = ws_layout(kind, M, N, K);
+    if (ws_bytes < l.total)
+        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    char* w = static_cast<char*>(ws);
+    if (w4a8_expands(kind, M)) {
+        cr_status s = launch_err(cr::launch_w4a8_expand(static_cast<const uint8_t*>(wp), N, K,
+                                                        reinterpret_cast<uint8_t*>(w + l.wexp), st),
+                                 "W4A8 weight decode");
+        if (s != CR_OK) return s;
+        wp = w + l.wexp;
+    }
+    const cr::GemmArgs a = gemm_args(kind, M, K, wp, wscale, N, bias, y, acc, w, l);
     return launch_err(cr::launch_gemm(a, st), "integer GEMM");
+}
+
+// The fused small-M W4A4 linear (rotation and quantisation by the GEMM
+// launch's own first blocks): mode 1 takes it where it applies and M <= 8,
+// mode 2 wherever it applies, mode 0 never.  Measured by graph replay with
+// cold weights (K x N = 3072 x 3072, 2560 x 9728, 9728 x 2560): it saves up
+// to 2 us at M = 1 and ties or wins up to M = 8; from M = 12 on its in-launch
+// hand-off (producer stores, arrival counter, polls, device-scope code
+// loads, all queued behind the weight stream) costs more than the second
+// launch does.
+constexpr int kFusedAutoMaxM = 8;
+std::atomic<int> g_fused_mode{1};
+bool use_fused(int kind, int M, int N, int K) {
+    const int mode = g_fused_mode.load(std::memory_order_relaxed);
+    if (kind != CR_W4A4 || mode == 0 || (mode == 1 && M > kFusedAutoMaxM)) return false;
+    return cr::fused_small_ok(cr::WK_W4, M, N, K);
+}
+
+// Phases 1 and 2 in one launch (use_fused holds); writes the same workspace
+// regions as the two phases.  xu non-NULL: the rows are silu(x) * xu (the MLP
+// block's down projection).
+cr_status fused_phase(int kind, const void* x, const void* xu, int M, int K, const void* wp, const float* wscale,
+                      int N, const void* bias, void* y, int32_t* acc, void* ws, size_t ws_bytes, hipStream_t st) {
+    const WsLayout l = ws_layout(kind, M, N, K);
+    if (ws_bytes < l.total)
+        return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
+    cr::GemmArgs a = gemm_args(kind, M, K, wp, wscale, N, bias, y, acc, static_cast<char*>(ws), l);
+    a.x = static_cast<const uint16_t*>(x);
+    a.xu = static_cast<const uint16_t*>(xu);
+    return launch_err(cr::launch_small_fused(a, st), "fused W4A4 linear");
+}
+
+// Both phases of a linear: one fused launch where it applies, else the
+// activation quantiser and the GEMM.
+cr_status linear_phases(int kind, const void* x, int M, int K, const void* wp, const float* wscale, int N,
+                        const void* bias, void* y, int32_t* acc, void* ws, size_t ws_bytes, hipStream_t st) {
+    if (use_fused(kind, M, N, K))
+        return fused_phase(kind, x, nullptr, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
+    cr_status s = quantize_phase(kind, x, M, K, ws, ws_bytes, st);
+    if (s != CR_OK) return s;
+    return gemm_phase(kind, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
 }
 
 // Checks shared by the linears and the GEMM phase.
@@ -236,8 +284,7 @@ cr_status run_linear(int kind, const void* x, int M, int K, const void* wp, cons
     if (ws_bytes < l.total)
         return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
     if ((s = check_device()) != CR_OK) return s;
-    if ((s = quantize_phase(kind, x, M, K, ws, ws_bytes, st)) != CR_OK) return s;
-    return gemm_phase(kind, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
+    return linear_phases(kind, x, M, K, wp, wscale, N, bias, y, acc, ws, ws_bytes, st);
 }
 
 // ---- static scratch of cr_linear_w4a4_noalloc ----------------------------
@@ -322,15 +369,20 @@ cr_status cr_mlp_w4a4(const void* x_bf16, int M, int K, const void* wg_packed, c
     if (ws_bytes < l.total) return fail(CR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, l.total);
     if ((s = check_device()) != CR_OK) return s;
     char* w = static_cast<char*>(ws);
-    // x quantised once for the gate and up GEMMs
-    if ((s = quantize_phase(CR_W4A4, x_bf16, M, K, w, l.g, stream)) != CR_OK) return s;
-    if ((s = gemm_phase(CR_W4A4, M, K, wg_packed, wg_scale, F, nullptr, w + l.g, nullptr, w, l.g, stream)) != CR_OK)
+    // x quantised once for the gate and up GEMMs (at small M by the gate
+    // GEMM's own launch)
+    if ((s = linear_phases(CR_W4A4, x_bf16, M, K, wg_packed, wg_scale, F, nullptr, w + l.g, nullptr, w, l.g,
+                           stream)) != CR_OK)
         return s;
     if ((s = gemm_phase(CR_W4A4, M, K, wu_packed, wu_scale, F, nullptr, w + l.u, nullptr, w, l.g, stream)) != CR_OK)
         return s;
-    // h = silu(g) * u, rotated and quantised for the down GEMM
+    // h = silu(g) * u, rotated and quantised for the down GEMM (at small M
+    // by the down GEMM's own launch)
     const WsLayout lb = ws_layout(CR_W4A4, M, N, F);
     char* wb = w + l.b;
+    if (use_fused(CR_W4A4, M, N, F))
+        return fused_phase(CR_W4A4, w + l.g, w + l.u, M, F, wd_packed, wd_scale, N, nullptr, y_bf16, nullptr, wb,
+                           lb.total, stream);
     s = launch_err(cr::launch_quant_swiglu(reinterpret_cast<const uint16_t*>(w + l.g),
                                            reinterpret_cast<const uint16_t*>(w + l.u), M, F,
                                            reinterpret_cast<int8_t*>(wb + lb.qx), reinterpret_cast<float*>(wb + lb.sx),
@@ -542,8 +594,8 @@ cr_status cr_linear_w4a4_noalloc(const void* x_bf16, int M, int K, const void* w
     if ((s = check_device()) != CR_OK) return s;
     void* ws = nullptr;
     if ((s = scratch_address(&ws)) != CR_OK) return s;
-    if ((s = quantize_phase(CR_W4A4, x_bf16, M, K, ws, kScratchBytes, stream)) != CR_OK) return s;
-    return gemm_phase(CR_W4A4, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, kScratchBytes, stream);
+    return linear_phases(CR_W4A4, x_bf16, M, K, w_packed, w_scale, N, bias_bf16, y_bf16, nullptr, ws, kScratchBytes,
+                         stream);
 }
 
 cr_status cr_linear_int8tw(const void* x_bf16, int M, int K, const void* w_packed, const float* w_scale,
@@ -635,6 +687,20 @@ cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K, const vo
     if (acc == nullptr && M > 0) return fail(CR_ERR_NULL, "accumulator output is NULL");
     return run_linear(kind, x_bf16, M, K, w_packed, nullptr, N, nullptr, nullptr, acc, ws, ws_bytes,
                       stream);
+}
+
+cr_status cr_dbg_fused_config(int mode, int spin_limit) {
+    if (mode < 0 || mode > 2) return fail(CR_ERR_SHAPE, "mode must be 0, 1 or 2, got %d", mode);
+    g_fused_mode.store(mode);
+    if (spin_limit >= 0) cr::set_fused_spin_limit(spin_limit);
+    return ok();
+}
+
+cr_status cr_dbg_fused_timeouts(uint32_t* count) {
+    if (count == nullptr) return fail(CR_ERR_NULL, "count is NULL");
+    cr_status s;
+    if ((s = check_device()) != CR_OK) return s;
+    return launch_err(cr::fused_timeouts(count), "reading the fused linear's timeout counter");
 }
 
 }  // extern "C"

@@ -110,8 +110,10 @@ struct Epi4 {
 // used: indices are clamped to valid elements (rows past M read row M - 1,
 // columns past N the last ones), and an absent operand (no bias; no weight
 // scale, as in the accumulator hook) is read from s_x instead, its value
-// unused.  `sx` must be valid.
-template <int WK>
+// unused.  `sx` must be valid.  COHERENT: s_x and ra were written by other
+// blocks of the same kernel; they are read at device scope (not from a line
+// a cache may hold from before).
+template <int WK, bool COHERENT = false>
 __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M, int m, int n) {
     Epi4 r;
     const int N = e.N;
@@ -120,7 +122,8 @@ __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M,
     r.full = vec && m < M && n < N && has_w;
     const int mc = min(m, M - 1);
     const int nc = vec ? min(n, N - 4) : 0;
-    r.sx = sx[mc];
+    if constexpr (COHERENT) r.sx = __hip_atomic_load(sx + mc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else r.sx = sx[mc];
     const float* wsp = has_w ? e.wscale : sx;
     if constexpr (wk_chan(WK)) {
         const float* sc = wsp + (has_w ? nc : 0);
@@ -138,7 +141,8 @@ __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M,
                          ((uint32_t)bp[e.bias != nullptr ? min(3, N - 1 - nc) : 0] << 16);
     r.b[0] = bf16_lo(b01); r.b[1] = bf16_hi(b01); r.b[2] = bf16_lo(b23); r.b[3] = bf16_hi(b23);
     if constexpr (WK == WK_W4) {
-        r.rn = -128 * e.ra[mc];
+        if constexpr (COHERENT) r.rn = -128 * __hip_atomic_load(e.ra + mc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else r.rn = -128 * e.ra[mc];
         const int4 c = *reinterpret_cast<const int4*>(e.cw + (vec ? nc : 0));
         r.cn[0] = -128 * c.x; r.cn[1] = -128 * c.y; r.cn[2] = -128 * c.z; r.cn[3] = -128 * c.w;
     }

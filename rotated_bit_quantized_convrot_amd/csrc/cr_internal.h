@@ -121,6 +121,13 @@ struct GemmArgs {
     uint32_t* sync;        // split-K arrival counters (kSyncWords, zero on entry and on exit; workspace)
     const int32_t* ra;     // W4A4: activation high-nibble code sums [M]
     const int32_t* cw;     // W4A4: weight high-nibble code sums [Np]
+    // fused small-M W4A4 linear: the bf16 activations, quantised by the
+    // GEMM launch's own producer blocks into qx / sx / ra
+    const uint16_t* x;
+    const uint16_t* xu;    // MLP down projection: x is g, xu is u, the row is silu(g) * u (else NULL)
+    int fused_producers;   // producer blocks (the first in the grid)
+    int fused_slot;        // its slot of the library's arrival counters
+    int spin_limit;        // polls of the bounded wait for the producers
 };
 
 // Large-M path plan: block tiles 256 x bn (bn = 256, or 192 where that fills
@@ -155,6 +162,21 @@ struct SmallPlan {
 };
 SmallPlan plan_small(int kind, int M, int N, int K);
 hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st);
+
+// Fused small-M W4A4 linear (group-256 Sylvester rotation): one launch whose
+// first blocks rotate and quantise the rows of a.x (or silu(a.x) * a.xu) into
+// a.qx / a.sx / a.ra (and clear a.sync) while the GEMM blocks load their
+// weights; a GEMM block waits (bounded by the spin limit's polls) for every
+// row before it reads them.  Taken where fused_small_ok() holds; the outputs
+// and accumulators are those of the two-kernel linear.
+bool fused_small_ok(int kind, int M, int N, int K);
+hipError_t launch_small_fused(GemmArgs a, hipStream_t st);
+// Polls of the fused linear's bounded wait (default 1 << 22, ~seconds);
+// set_fused_spin_limit changes it for later launches (inspection/testing).
+void set_fused_spin_limit(int polls);
+// GEMM blocks of the fused linear whose wait ran out (device counter; reading it
+// synchronises the device).
+hipError_t fused_timeouts(uint32_t* count);
 
 // Whether the activations of a linear are stored packed 4-bit (W4A4)
 // rather than as int8 [M, Kp].

@@ -10,108 +10,12 @@
 
 namespace cr {
 
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-           ((uint32_t)(d & 0xFF) << 24);
-}
-
-// Max over the `seg` lanes (16, 32 or 64; aligned) of each lane's segment.
-__device__ __forceinline__ float seg_max(float a, int seg) {
-    a = fmaxf(a, lane_xor<1>(a));
-    a = fmaxf(a, lane_xor<2>(a));
-    a = fmaxf(a, lane_xor<4>(a));
-    a = fmaxf(a, lane_xor<8>(a));
-    if (seg >= 32) a = fmaxf(a, lane_xor<16>(a));
-    if (seg >= 64) a = fmaxf(a, __shfl_xor(a, 32, 64));
-    return a;
-}
-
-// Four codes (int, -128..127) -> one dword, first code in the low byte.
-__device__ __forceinline__ uint32_t pack4_codes(int a, int b, int c, int d) {
-    const uint32_t ab = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0400u);
-    const uint32_t cd = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0C0C0400u);
-    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
-}
-
-// Codes of a lane's 16 rotated values (unscaled, sign-tracked), see below.
 // The split-K arrival counters of the GEMMs that read this quantisation
 // start at zero: the first block clears them (the GEMM kernels run after this
 // kernel on the same stream).
 __device__ __forceinline__ void zero_sync(uint32_t* __restrict__ sync) {
     if (sync != nullptr && blockIdx.x == 0)
         for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) sync[i] = 0u;
-}
-
-template <int QMAX, int LO, int HI, int GS>
-__device__ __forceinline__ void codes16(const float (&v)[16], bool fast, float rinv, float sigma, float s_u,
-                                        float s, float (&r)[16]) {
-    if (fast) {
-        float dmax = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const float q = v[t] * rinv;
-            r[t] = __builtin_rintf(q);
-            dmax = fmaxf(dmax, fabsf(q - r[t]));
-        }
-        if (dmax > 0.5f - (float)QMAX * 9.5367431640625e-07f) {   // within QMAX * 2^-20 of a tie
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const float q = __builtin_rintf((sigma * v[t]) / s_u);
-                r[t] = fminf(fmaxf(q, (float)LO), (float)HI);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) r[t] = (float)quant_code<LO, HI>((sigma * v[t]) * rot_norm<GS>(), s);
-    }
-}
-
-// W4A4 codes of 16 consecutive k (k0 % 16 == 0) in the activation nibble
-// forms: the two dwords of the 4-bit tile layout, byte b of dword d holding
-// k0 + 8d + b (low nibble, code ^ 8) and k0 + 8d + 4 + b (high nibble).
-__device__ __forceinline__ uint2 pack_act16(const float (&r)[16]) {
-    const uint32_t x0 = pack4_codes((int)r[0], (int)r[1], (int)r[2], (int)r[3]);
-    const uint32_t x1 = pack4_codes((int)r[4], (int)r[5], (int)r[6], (int)r[7]);
-    const uint32_t x2 = pack4_codes((int)r[8], (int)r[9], (int)r[10], (int)r[11]);
-    const uint32_t x3 = pack4_codes((int)r[12], (int)r[13], (int)r[14], (int)r[15]);
-    uint2 pk;
-    pk.x = ((x0 ^ 0x08080808u) & 0x0F0F0F0Fu) | ((x1 << 4) & 0xF0F0F0F0u);
-    pk.y = ((x2 ^ 0x08080808u) & 0x0F0F0F0Fu) | ((x3 << 4) & 0xF0F0F0F0u);
-    return pk;
-}
-
-// Byte offset of the 8 bytes of row m, k0..k0+15 (k0 % 16 == 0) in the 4-bit
-// tile layout with rows = m: dwords (t, d = 0, 1) of half h of chunk k0 / 64.
-__device__ __forceinline__ size_t act4_offset(int m, int k0, int K) {
-    const int kc = k0 >> 6, t = (k0 >> 5) & 1, h = (k0 >> 4) & 1;
-    return ((size_t)(m >> 5) * (K >> 6) + kc) * 1024 + (m & 31) * 32 + 16 * h + 8 * t;
-}
-
-// The 16 values of x at x + off (16-byte aligned), as float; with GLU, x is
-// the gate output g, u the up output, and the values are silu(g) * u
-// rounded to bf16 (silu_mul_bf16).
-template <bool GLU>
-__device__ __forceinline__ void load16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u, size_t off,
-                                       float (&v)[16]) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + off);
-    const uint4 r0 = src[0], r1 = src[1];
-    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    if constexpr (GLU) {
-        const uint4* su = reinterpret_cast<const uint4*>(u + off);
-        const uint4 q0 = su[0], q1 = su[1];
-        const uint32_t z[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            v[2 * t] = silu_mul_bf16(bf16_lo(w[t]), bf16_lo(z[t]));
-            v[2 * t + 1] = silu_mul_bf16(bf16_hi(w[t]), bf16_hi(z[t]));
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            v[2 * t] = bf16_lo(w[t]);
-            v[2 * t + 1] = bf16_hi(w[t]);
-        }
-    }
 }
 
 // Rotated activations: codes [M, K] int8 (natural order) and scales [M].

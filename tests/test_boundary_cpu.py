@@ -91,6 +91,17 @@ def test_argument_errors(L):
     assert L.cr_linear_w4a4(vp, 4, 1 << 21, vp, vp, 64, None, vp, vp, 1 << 20, None) == CR["SHAPE"]
 
 
+def test_fused_config_arguments(L):
+    """The fused small-M path switch takes 0, 1 or 2 and keeps the wait's limit
+    when given a negative one; the timeout counter needs an output and a
+    device."""
+    assert L.cr_dbg_fused_config(3, -1) == CR["SHAPE"]
+    assert L.cr_dbg_fused_config(-1, -1) == CR["SHAPE"]
+    for mode in (0, 2, 1):
+        assert L.cr_dbg_fused_config(mode, -1) == CR["OK"]
+    assert L.cr_dbg_fused_timeouts(None) == CR["NULL"]
+
+
 def test_m_zero_is_a_noop(L):
     vp = ctypes.c_void_p(16)
     assert L.cr_linear_w4a4(None, 0, 256, vp, vp, 64, None, None, None, 0, None) == CR["OK"]
