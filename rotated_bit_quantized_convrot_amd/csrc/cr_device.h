@@ -308,7 +308,12 @@ __device__ __forceinline__ v4i unpack_wt4(uint32_t p0, uint32_t p1) {
 
 // Exact W4A4 dot product from the MFMA sum and the two correction terms
 // rn = -128 ra[m], cn = -128 cw[n].
-__device__ __forceinline__ int w4_exact(int acc, int rn, int cn) { return (acc + rn + cn) >> 4; }
+__device__ __forceinline__ int w4_exact(int acc, int rn, int cn) {
+    // one three-operand add (the compiler otherwise splits it in two)
+    int t;
+    asm("v_add3_u32 %0, %1, %2, %3" : "=v"(t) : "v"(acc), "v"(rn), "v"(cn));
+    return t >> 4;
+}
 
 // Four codebook indices (one per byte, 0..15, in `sel`) looked up in a
 // 16-byte table row t0..t3: v_perm picks from the low and the high 8 entries

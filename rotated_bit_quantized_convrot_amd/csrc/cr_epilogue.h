@@ -140,6 +140,10 @@ __device__ __forceinline__ Epi4 epi4_fetch(const Epi& e, const float* sx, int M,
     const uint32_t b23 = (uint32_t)bp[e.bias != nullptr ? min(2, N - 1 - nc) : 0] |
                          ((uint32_t)bp[e.bias != nullptr ? min(3, N - 1 - nc) : 0] << 16);
     r.b[0] = bf16_lo(b01); r.b[1] = bf16_hi(b01); r.b[2] = bf16_lo(b23); r.b[3] = bf16_hi(b23);
+    // no bias: -0.0, which leaves every sum as it is (x + -0 == x, zeros
+    // included), so store4_pre adds without a test
+    if (e.bias == nullptr)
+        for (int j = 0; j < 4; ++j) r.b[j] = -0.0f;
     if constexpr (WK == WK_W4) {
         if constexpr (COHERENT) r.rn = -128 * __hip_atomic_load(e.ra + mc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else r.rn = -128 * e.ra[mc];
@@ -158,13 +162,12 @@ __device__ __forceinline__ void store4_pre(const Epi& e, const Epi4& r, int m, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[j] = w4_exact(a[j], r.rn, r.cn[j]);
     }
-    const bool has_bias = e.bias != nullptr;
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         v[j] = (float)a[j] * r.sx;
         v[j] = v[j] * r.sw[j];
-        if (has_bias) v[j] = v[j] + r.b[j];
+        v[j] = v[j] + r.b[j];          // -0.0 without a bias
     }
     *reinterpret_cast<uint2*>(e.y + (size_t)m * e.N + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }

@@ -130,9 +130,9 @@ struct BigCfg {
     static constexpr int CB = C_BYTES / NW;
     static constexpr int LPS = LA + LW + (WK == WK_W4A8 ? 1 : 0);
     // LDS-staged epilogue: per wave 32 rows of EPI_TR bytes, then its FN * 32
-    // columns' bias (bf16), scale (fp32) and (W4A4) weight correction (int32)
+    // columns' bias (fp32), scale (fp32) and (W4A4) weight correction (int32)
     static constexpr int EPI_TR = 80;
-    static constexpr int EPI_OPB = FN * 32 * (2 + 4 + (PA ? 4 : 0));
+    static constexpr int EPI_OPB = FN * 32 * (4 + 4 + (PA ? 4 : 0));
     static constexpr int EPI_BYTES = NW * (32 * EPI_TR + EPI_OPB);
     // W4A4 stages are too small to hold it: its own region after the ring
     static constexpr size_t EPI_OFF = (size_t)NS * STAGE;
@@ -482,14 +482,16 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 }
                 const int nw0 = n0 + wn * FN * 32;            // the wave's first column
                 constexpr int NCW = FN * 32;                  // the wave's columns
-                constexpr int OS = NCW * 2, OC = NCW * 6;     // scale and correction offsets in sop
-                uint16_t bl[(NCW + 63) / 64];
+                constexpr int OS = NCW * 4, OC = NCW * 8;     // scale and correction offsets in sop
+                // bias as float; with no bias -0.0, which leaves every sum as
+                // it is (x + -0 == x, zeros included), so the add needs no test
+                float bl[(NCW + 63) / 64];
                 float cl[(NCW + 63) / 64];
                 int cnl[(NCW + 63) / 64];
 #pragma unroll
                 for (int c = 0; c < (NCW + 63) / 64; ++c) {
                     const int col = min(c * 64 + lane, NCW - 1);
-                    bl[c] = p.bias != nullptr ? p.bias[nw0 + col] : (uint16_t)0;
+                    bl[c] = p.bias != nullptr ? bf16_lo(p.bias[nw0 + col]) : -0.0f;
                     cl[c] = sw0;
                     if constexpr (wk_chan(WK)) cl[c] = p.wscale[nw0 + col];
                     cnl[c] = 0;
@@ -499,13 +501,13 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
 #pragma unroll
                 for (int c = 0; c < (NCW + 63) / 64; ++c) {
                     if (NCW % 64 == 0 || c * 64 + lane < NCW) {
-                        reinterpret_cast<uint16_t*>(sop)[c * 64 + lane] = bl[c];
+                        reinterpret_cast<float*>(sop)[c * 64 + lane] = bl[c];
                         reinterpret_cast<float*>(sop + OS)[c * 64 + lane] = cl[c];
                         if constexpr (C::PA) reinterpret_cast<int*>(sop + OC)[c * 64 + lane] = cnl[c];
                     }
                 }
                 // per-lane bases; every other offset below is a constant
-                const int8_t* sbias = sop + 8 * h;            // bias of column 4h (+ 32f + 8q)
+                const int8_t* sbias = sop + 16 * h;           // bias of column 4h (+ 32f + 8q)
                 const int8_t* sscale = sop + OS + 16 * h;     // scale of column 4h
                 const int8_t* scorr = sop + OC + 16 * h;      // correction of column 4h
                 int8_t* swr = scr + l32 * TR + 8 * h;         // this lane's row, its 4 columns
@@ -516,10 +518,10 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                     for (int f = 0; f < FN; ++f) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const uint2 bq = *reinterpret_cast<const uint2*>(sbias + 2 * (32 * f + 8 * q));
+                            const float4 bq = *reinterpret_cast<const float4*>(sbias + 4 * (32 * f + 8 * q));
                             const float4 cq = *reinterpret_cast<const float4*>(sscale + 4 * (32 * f + 8 * q));
                             const float c[4] = {cq.x, cq.y, cq.z, cq.w};
-                            const float b[4] = {bf16_lo(bq.x), bf16_hi(bq.x), bf16_lo(bq.y), bf16_hi(bq.y)};
+                            const float b[4] = {bq.x, bq.y, bq.z, bq.w};
                             int a[4] = {acc[i][f][4 * q], acc[i][f][4 * q + 1], acc[i][f][4 * q + 2], acc[i][f][4 * q + 3]};
                             if constexpr (C::PA) {
                                 const int4 rq = *reinterpret_cast<const int4*>(scorr + 4 * (32 * f + 8 * q));
@@ -533,7 +535,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                             for (int j = 0; j < 4; ++j) {
                                 v[j] = (float)a[j] * sxv[i];
                                 v[j] = v[j] * c[j];
-                                if (p.bias != nullptr) v[j] = v[j] + b[j];
+                                v[j] = v[j] + b[j];
                             }
                             *reinterpret_cast<uint2*>(swr + q * 16) =
                                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
