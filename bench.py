@@ -447,6 +447,10 @@ def main():
         probe.quant()
         for i in range(5):
             probe.gemm(i % len(probe.packed))
+        if probe.kind == 0 and probe.M <= 8:
+            # the whole linear too: one fused launch at this size
+            for i in range(5):
+                probe.linear(i % len(probe.packed))
         torch.cuda.synchronize()
         src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)

@@ -126,3 +126,58 @@ def test_fused_mlp_block(crp, M, K, F, N):
     ref = O.f32_to_bf16_rne(O.mlp_w4a4(L.x, wg, wu, wd)["y"])
     for y in yf + [y5]:
         assert np.array_equal(_bits(y), ref)
+
+
+def test_default_routing_by_m(crp):
+    """Mode 1 (the default) takes the fused launch at M <= 8 and two launches
+    above: with a wait of zero polls only the fused launch counts timeouts."""
+    K, N = 3072, 1024
+    L = si.random_layer(16, K, N, seed=5)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    crp.dbg_fused_config(1, 0)
+    try:
+        for M, fused in ((1, True), (8, True), (9, False), (16, False)):
+            x = to_dev_bf16(L.x[:M])
+            before = crp.dbg_fused_timeouts()
+            crp.linear_w4a4(x, p, s, N)
+            torch.cuda.synchronize()
+            assert (crp.dbg_fused_timeouts() > before) == fused, M
+    finally:
+        crp.dbg_fused_config(1, 1 << 22)
+
+
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_under_graph_capture(crp, M):
+    """The fused launch (its counter slot fixed at capture) in a replayed
+    graph, eager work and synchronisation between replays, every replay equal
+    to the eager result and to the oracle; the MLP block too."""
+    K, N = 2560, 3072
+    L = si.random_layer(M, K, N, seed=40 + M, bias=True, outlier_count=5)
+    x = to_dev_bf16(L.x)
+    p, s = crp.pack_weight_w4(to_dev_bf16(L.w))
+    b = to_dev_bf16(L.bias)
+    ws = torch.empty(crp.workspace_bytes(0, M, N, K), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ref = crp.linear_w4a4(x, p, s, N, b).clone()
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(ref), O.f32_to_bf16_rne(O.linear_w4a4(L.x, L.w, L.bias)["y"]))
+    F = 768
+    wg, wu, wd = _w((F, K), 7), _w((F, K), 8), _w((N, F), 9)
+    (pg, sg), (pu, su), (pd, sd) = [crp.pack_weight_w4(to_dev_bf16(w)) for w in (wg, wu, wd)]
+    wsm = torch.empty(crp.mlp_workspace_bytes(M, K, F, N), dtype=torch.uint8, device="cuda")
+    ym = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    refm = crp.mlp_w4a4(x, pg, sg, pu, su, F, pd, sd, N).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        crp.linear_w4a4(x, p, s, N, b, out=y, workspace=ws)
+        crp.mlp_w4a4(x, pg, sg, pu, su, F, pd, sd, N, out=ym, workspace=wsm)
+    for i in range(4):
+        y.zero_()
+        ym.zero_()
+        crp.linear_w4a4(x, p, s, N, None)       # eager fused launches between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref) and torch.equal(ym, refm), f"replay {i}"
+    assert np.array_equal(_bits(refm), O.f32_to_bf16_rne(O.mlp_w4a4(L.x, wg, wu, wd)["y"]))
