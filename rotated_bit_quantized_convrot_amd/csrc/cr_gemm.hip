@@ -106,11 +106,12 @@ __device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_
 
 // 8 waves, block tile 256 (m) x BN (n), NS-stage LDS ring.  BN = 256: 2
 // waves along m x 4 along n, wave tile 128 x 64; BN = 192 (fills the chip
-// where 256-wide tiles leave CUs idle): 4 x 2, wave tile 64 x 96.
+// where 256-wide tiles leave CUs idle): 4 x 2, wave tile 64 x 96; BN = 128
+// (layers with few output tiles): 4 x 2, wave tile 64 x 64.
 template <int WK, int NW, int NS, int BN_>
 struct BigCfg {
     static_assert(NW == 8, "8 waves");
-    static_assert(BN_ == 256 || BN_ == 192, "block tile width");
+    static_assert(BN_ == 256 || BN_ == 192 || BN_ == 128, "block tile width");
     static constexpr int BN = BN_;
     static constexpr int NWT = BN / 32;                                // 32-row weight tiles per stage
     static constexpr int WM = BN == 256 ? 2 : 4;                       // waves along m
@@ -685,15 +686,19 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
 
 // Large-M plan: the block tile width and the K slices per tile.  Rough time
 // model in microseconds: per 64-k stage of a 256 x 256 tile about 0.8 us for
-// 4-bit weights, 1.0 for int8, 1.3 for W4A8, and 0.9 of that for a 256 x 192
+// 4-bit weights, 1.0 for int8, 1.3 for W4A8, 0.9 of that for a 256 x 192
 // tile (three quarters of the work; its 64 x 96 wave tiles read more LDS bytes
-// and widen more operands per MFMA, measured ~1.2x the time per op);
+// and widen more operands per MFMA, measured ~1.2x the time per op) and 0.6
+// for a 256 x 128 tile (half the work on 64 x 64 wave tiles; it lets layers
+// with few output tiles fill the chip with fewer K slices: ConvRot INT8 2560^2
+// at M = 1220 29.2 -> 25.9 us without a split instead of 4 slices);
 // rounds of one unit per CU; plus, for a split, the int32 partial tiles
 // written and read back at about 4.5 TB/s and a second launch.  Anything
 // other than 256-wide whole tiles has to win by 5%.  Slices divide the K
 // chunks evenly, at most 16.  W4A8 keeps 256-wide tiles (its LDS has no room
-// for the narrower tile's epilogue scratch).
+// for the narrower tiles' epilogue scratch).
 constexpr int BIG_CUS = 256;
+constexpr double BIG_T128 = 0.6;    // a 256 x 128 tile's stage, relative to 256 x 256
 constexpr int BIG_MAX_SPLITS = 16;
 
 BigPlan plan_big(int kind, int M, int N, int K) {
@@ -705,10 +710,10 @@ BigPlan plan_big(int kind, int M, int N, int K) {
     const double t_stage = kind == WK_W4 ? 0.8 : (wk_i8w(kind) ? 1.0 : 1.3);
     const double tiles_m = (double)((M + BIG_BM - 1) / BIG_BM);
     double best = std::ceil(tiles_m * ((N + 255) / 256) / BIG_CUS) * nkc * t_stage;
-    for (int bn : {256, 192}) {
-        if (bn == 192 && kind == WK_W4A8) continue;
+    for (int bn : {256, 192, 128}) {
+        if (bn != 256 && kind == WK_W4A8) continue;
         const double total = tiles_m * ((N + bn - 1) / bn);
-        const double ts = t_stage * (bn == 256 ? 1.0 : 0.9);
+        const double ts = t_stage * (bn == 256 ? 1.0 : (bn == 192 ? 0.9 : BIG_T128));
         for (int S = 1; S <= BIG_MAX_SPLITS && S <= nkc; ++S) {
             if (nkc % S != 0 || (bn == 256 && S == 1)) continue;
             double cost = std::ceil(total * S / BIG_CUS) * (nkc / S) * ts;
@@ -761,6 +766,7 @@ static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
     const BigPlan bp = plan_big(WK, a.M, a.N, a.K);
     if constexpr (WK != WK_W4A8) {
         if (bp.bn == 192) return launch_big_bn<WK, ACC, 192>(a, bp, st);
+        if (bp.bn == 128) return launch_big_bn<WK, ACC, 128>(a, bp, st);
     }
     if (bp.bn != 256) return hipErrorInvalidValue;
     return launch_big_bn<WK, ACC, 256>(a, bp, st);
