@@ -412,8 +412,15 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
         // after the epilogue instead (fewer registers live across it; the
         // other formats have them to spare and keep the plain schedule).
         constexpr bool DEFER = WK == WK_W4A8;
-        if (!DEFER || kc + 1 != cps) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
-        __builtin_amdgcn_sched_barrier(0);   // the next stage's reads go out before the MFMAs
+        // The next stage's fragment reads: before the MFMAs (W4A4), or after
+        // the first four of them (int8 operands, twice the bytes per read:
+        // W4A8 178.8 -> 173.8 us, int8_tensorwise K=2688 34.5 -> 33.7 us; for
+        // W4A4 it measured slower)
+        constexpr bool READ_LATE = !C::PA;
+        if constexpr (!READ_LATE) {
+            if (!DEFER || kc + 1 != cps) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // W4A8: the table decode makes the MFMA block VALU-heavy; a raised
         // priority keeps the other wave of the SIMD from starving it (-2%)
         if constexpr (WK == WK_W4A8) __builtin_amdgcn_s_setprio(1);
@@ -428,6 +435,11 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 for (int f = 0; f < FN; ++f) {
                     acc[i][f] = mfma32(bt[f], aop(cur, t, i), acc[i][f]);
                     const int done = (t * FM + i) * FN + f + 1;   // a constant once unrolled
+                    if (READ_LATE && done == 4) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (!DEFER || kc + 1 != cps) read_frags(ring + ((B + 1) % NS) * C::STAGE, nxt);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     if ((ISS || !PAIR) && done == N1) {
                         __builtin_amdgcn_sched_barrier(0);
                         issue_stage(IntC<(B + NS - 1) % NS>{});
