@@ -700,17 +700,20 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
 // model in microseconds: per 64-k stage of a 256 x 256 tile about 0.8 us for
 // 4-bit weights, 1.0 for int8, 1.3 for W4A8, 0.9 of that for a 256 x 192
 // tile (three quarters of the work; its 64 x 96 wave tiles read more LDS bytes
-// and widen more operands per MFMA, measured ~1.2x the time per op) and 0.6
+// and widen more operands per MFMA, measured ~1.2x the time per op) and 0.55
 // for a 256 x 128 tile (half the work on 64 x 64 wave tiles; it lets layers
 // with few output tiles fill the chip with fewer K slices: ConvRot INT8 2560^2
-// at M = 1220 29.2 -> 25.9 us without a split instead of 4 slices);
+// at M = 1220 29.2 -> 25.9 us without a split instead of 4 slices; and it
+// fills the last round where 256-wide tiles leave half of it idle: the W4A8
+// layer's int8 GEMM, 640 tiles of 256 x 256 against 1280 of 256 x 128,
+// 186.5 -> 182.0 us);
 // rounds of one unit per CU; plus, for a split, the int32 partial tiles
 // written and read back at about 4.5 TB/s and a second launch.  Anything
 // other than 256-wide whole tiles has to win by 5%.  Slices divide the K
 // chunks evenly, at most 16.  W4A8 keeps 256-wide tiles (its LDS has no room
 // for the narrower tiles' epilogue scratch).
 constexpr int BIG_CUS = 256;
-constexpr double BIG_T128 = 0.6;    // a 256 x 128 tile's stage, relative to 256 x 256
+constexpr double BIG_T128 = 0.55;   // a 256 x 128 tile's stage, relative to 256 x 256
 constexpr int BIG_MAX_SPLITS = 16;
 
 BigPlan plan_big(int kind, int M, int N, int K) {
