@@ -376,6 +376,18 @@ cr_status cr_dbg_fused_config(int mode, int spin_limit);
  * the device).  count: host pointer, out. */
 cr_status cr_dbg_fused_timeouts(uint32_t* count);
 
+/* Large-M GEMM plan override (M > 128), for inspection and timing: later
+ * calls use block tiles 256 x bn and K split into `splits` equal slices
+ * across blocks, in place of the planner's choice.
+ *   bn: 256, 192 or 128 (W4A8's own GEMM keeps 256), 0 = the planner's.
+ *   splits: 1..16, 0 = the planner's; a count that does not divide the
+ *           layer's 64-k chunks leaves the planner's split for that layer.
+ * Any other value -> CR_ERR_SHAPE.  The workspace a call needs follows the
+ * plan (cr_workspace_bytes reflects the override), so size it after setting
+ * one.  Results do not depend on the plan (exact integer sums).  The setting
+ * is process-wide and read at each call. */
+cr_status cr_dbg_big_plan(int bn, int splits);
+
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */
 cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K,

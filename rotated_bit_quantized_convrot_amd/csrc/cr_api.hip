@@ -696,6 +696,13 @@ cr_status cr_dbg_fused_config(int mode, int spin_limit) {
     return ok();
 }
 
+cr_status cr_dbg_big_plan(int bn, int splits) {
+    if (bn != 0 && bn != 128 && bn != 192 && bn != 256) return fail(CR_ERR_SHAPE, "bn must be 0, 128, 192 or 256, got %d", bn);
+    if (splits < 0 || splits > 16) return fail(CR_ERR_SHAPE, "splits must be 0..16, got %d", splits);
+    cr::set_big_plan_override(bn, splits);
+    return ok();
+}
+
 cr_status cr_dbg_fused_timeouts(uint32_t* count) {
     if (count == nullptr) return fail(CR_ERR_NULL, "count is NULL");
     cr_status s;

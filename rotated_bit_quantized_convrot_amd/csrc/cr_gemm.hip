@@ -716,6 +716,14 @@ constexpr int BIG_CUS = 256;
 constexpr double BIG_T128 = 0.55;   // a 256 x 128 tile's stage, relative to 256 x 256
 constexpr int BIG_MAX_SPLITS = 16;
 
+// Plan override for inspection and timing (cr_dbg_big_plan): block tile width
+// and K slices; 0 leaves the planner's choice.
+static std::atomic<int> g_big_force_bn{0}, g_big_force_splits{0};
+void set_big_plan_override(int bn, int splits) {
+    g_big_force_bn.store(bn);
+    g_big_force_splits.store(splits);
+}
+
 BigPlan plan_big(int kind, int M, int N, int K) {
     BigPlan bp{1, 0, 0, 256};
     if (M <= 0 || N <= 0 || K <= 0) return bp;
@@ -740,6 +748,12 @@ BigPlan plan_big(int kind, int M, int N, int K) {
                 bp.cps = nkc / S;
             }
         }
+    }
+    const int fbn = g_big_force_bn.load(), fs = g_big_force_splits.load();
+    if (fbn > 0 && (kind != WK_W4A8 || fbn == 256)) bp.bn = fbn;
+    if (fs > 0 && fs <= nkc && nkc % fs == 0) {
+        bp.splits = fs;
+        bp.cps = nkc / fs;
     }
     const double total = tiles_m * ((N + bp.bn - 1) / bp.bn);
     bp.part_bytes = bp.splits > 1 ? (size_t)total * bp.splits * BIG_BM * bp.bn * 4 : 0;

@@ -142,6 +142,10 @@ struct BigPlan {
     int bn;
 };
 BigPlan plan_big(int kind, int M, int N, int K);
+// Overrides the large-M plan's tile width (256, 192 or 128) and K slices (a
+// divisor of the 64-k chunks, at most 16) for later calls; 0 keeps the
+// planner's choice (inspection and timing).
+void set_big_plan_override(int bn, int splits);
 
 // Small-M path, used for M <= kSmallMaxM: 16-row MFMA tiles, blocks of 8
 // waves over 16 * nt weight rows that split their K range between the

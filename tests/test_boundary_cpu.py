@@ -41,6 +41,26 @@ def test_library_exports_every_declared_symbol(L):
     assert sorted(crp.EXPORTS) == _declared()
 
 
+def test_big_plan_override_arguments_and_workspace(L):
+    """The large-M plan override takes tile widths 0/128/192/256 and 0..16 K
+    slices; the workspace size follows the forced plan (int32 partial tiles
+    of every slice) and returns to the planner's once cleared."""
+    assert L.cr_dbg_big_plan(100, 0) == CR["SHAPE"]
+    assert L.cr_dbg_big_plan(128, 17) == CR["SHAPE"]
+    assert L.cr_dbg_big_plan(0, -1) == CR["SHAPE"]
+    M, N, K = 1220, 2560, 2560
+    base = L.cr_workspace_bytes(3, M, N, K)
+    try:
+        assert L.cr_dbg_big_plan(128, 4) == CR["OK"]
+        tiles = -(-M // 256) * -(-N // 128)
+        assert L.cr_workspace_bytes(3, M, N, K) >= 4 * tiles * 256 * 128 * 4
+        assert L.cr_dbg_big_plan(128, 3) == CR["OK"]          # 40 chunks: 3 does not divide, no split
+        assert L.cr_workspace_bytes(3, M, N, K) < 2 * tiles * 256 * 128 * 4
+    finally:
+        assert L.cr_dbg_big_plan(0, 0) == CR["OK"]
+    assert L.cr_workspace_bytes(3, M, N, K) == base
+
+
 def test_sizes(L):
     # W4A4: N rounded to 32 rows, two codes per byte, one int32 per row
     assert L.cr_packed_bytes(0, 12288, 3072) == 12288 * 3072 // 2 + 12288 * 4
