@@ -388,6 +388,15 @@ cr_status cr_dbg_fused_timeouts(uint32_t* count);
  * is process-wide and read at each call. */
 cr_status cr_dbg_big_plan(int bn, int splits);
 
+/* Small-M GEMM plan override (M <= 128), for inspection and timing: later
+ * calls split K into `splits` slices across blocks (1..16) where that count
+ * fits the plan (each wave holds its whole share of the loads in registers;
+ * a count that does not fit, or 0, leaves the planner's split).  Any other
+ * value -> CR_ERR_SHAPE.  The workspace follows the plan (size it after
+ * setting one); results do not depend on it.  Process-wide, read at each
+ * call. */
+cr_status cr_dbg_small_plan(int splits);
+
 /* The int32 accumulators [M,N] of the linear of `kind` (same kernels as the
  * linear, epilogue replaced by a plain int32 store). */
 cr_status cr_dbg_linear_acc(int kind, const void* x_bf16, int M, int K,

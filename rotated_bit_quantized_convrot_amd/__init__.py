@@ -36,7 +36,7 @@ __all__ = [
     "probe_mfma_i8", "probe_read", "probe_copy", "probe_wall_clock_khz",
     "linear_w4a4_noalloc", "NOALLOC_SCRATCH_BYTES",
     "encode_w4a8", "encode_w4a8_workspace_bytes", "dbg_e4m3_encode",
-    "dbg_fused_config", "dbg_fused_timeouts", "dbg_big_plan",
+    "dbg_fused_config", "dbg_fused_timeouts", "dbg_big_plan", "dbg_small_plan",
 ]
 
 W4A4, INT8TW, W4A8, INT8ROT, W4A4_G64, W4A4_G16, W4A4_RH = 0, 1, 2, 3, 4, 5, 6
@@ -61,7 +61,7 @@ EXPORTS = [
     "cr_probe_mfma_i8", "cr_probe_read", "cr_probe_copy", "cr_probe_wall_clock_khz",
     "cr_linear_w4a4_noalloc",
     "cr_encode_w4a8_workspace_bytes", "cr_encode_w4a8", "cr_dbg_e4m3_encode",
-    "cr_dbg_fused_config", "cr_dbg_fused_timeouts", "cr_dbg_big_plan",
+    "cr_dbg_fused_config", "cr_dbg_fused_timeouts", "cr_dbg_big_plan", "cr_dbg_small_plan",
 ]
 
 
@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
         "cr_dbg_fused_config": (i, [i, i]),
         "cr_dbg_fused_timeouts": (i, [vp]),
         "cr_dbg_big_plan": (i, [i, i]),
+        "cr_dbg_small_plan": (i, [i]),
         "cr_linear_int8tw": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_linear_w4a8": (i, [vp, i, i, vp, vp, i, vp, vp, vp, sz, vp]),
         "cr_status_str": (ctypes.c_char_p, [i]),
@@ -290,6 +291,13 @@ def dbg_big_plan(bn: int = 0, splits: int = 0) -> None:
     or 128) and ``splits`` K slices across blocks; 0 keeps the planner's
     choice.  Size workspaces after setting it."""
     _check(lib().cr_dbg_big_plan(int(bn), int(splits)))
+
+
+def dbg_small_plan(splits: int = 0) -> None:
+    """Small-M GEMM plan for later calls: ``splits`` K slices across blocks
+    where that count fits the plan; 0 keeps the planner's choice.  Size
+    workspaces after setting it."""
+    _check(lib().cr_dbg_small_plan(int(splits)))
 
 
 def dbg_fused_timeouts() -> int:

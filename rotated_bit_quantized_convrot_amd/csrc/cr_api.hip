@@ -703,6 +703,12 @@ cr_status cr_dbg_big_plan(int bn, int splits) {
     return ok();
 }
 
+cr_status cr_dbg_small_plan(int splits) {
+    if (splits < 0 || splits > 16) return fail(CR_ERR_SHAPE, "splits must be 0..16, got %d", splits);
+    cr::set_small_plan_override(splits);
+    return ok();
+}
+
 cr_status cr_dbg_fused_timeouts(uint32_t* count) {
     if (count == nullptr) return fail(CR_ERR_NULL, "count is NULL");
     cr_status s;

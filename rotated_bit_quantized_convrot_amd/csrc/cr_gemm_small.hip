@@ -582,6 +582,11 @@ __host__ __device__ constexpr int small_regs_per_chunk(int wk, int mt, int nt) {
 }
 constexpr int SM_LOAD_REGS = 128;
 
+// Plan override for inspection and timing (cr_dbg_small_plan): K slices
+// across blocks; 0 leaves the planner's choice.
+static std::atomic<int> g_small_force_splits{0};
+void set_small_plan_override(int splits) { g_small_force_splits.store(splits); }
+
 SmallPlan plan_small(int kind, int M, int N, int K) {
     SmallPlan sp{};
     sp.use = M > 0 && M <= kSmallMaxM;
@@ -598,7 +603,10 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
     const double wbytes = kind == WK_W4 ? 0.5 : (wk_i8w(kind) ? 1.0 : 0.5625);
     const double abytes = kind == WK_W4 ? 0.5 : 1.0;
     double best = 1e30;
+    const int forced = g_small_force_splits.load();
+    for (int pass = forced > 0 ? 0 : 1; pass < 2 && best >= 1e30; ++pass)
     for (int S = 1; S <= nsteps && S <= SM_MAX_SPLITS; ++S) {
+        if (pass == 0 && S != forced) continue;  // the forced count, where it fits
         const int sps = (nsteps + S - 1) / S;    // steps per slice
         const int splits = (nsteps + sps - 1) / sps;
         if (splits != S) continue;
@@ -615,8 +623,13 @@ SmallPlan plan_small(int kind, int M, int N, int K) {
         double cost = rounds * (std::max(bytes / 64.0, mfma) + 2000.0);
         // (the last-arriving block finishes the tiles: ~800 cycles for its
         // dependent reads; a second kernel where the counters cannot cover
-        // the blocks: ~3000)
-        if (splits > 1) cost += (double)splits * sp.mt * 16 * N * 8 / 4000.0 + (nblk <= kSyncWords ? 800.0 : 3000.0);
+        // the blocks: ~3000; and ~300 per slice for its partial tile's
+        // device-scope store and acknowledgement.  Forced splits at M = 76,
+        // cold weights: ConvRot INT8 2560^2 10.1 us with 3 slices against
+        // 10.9 with 4 and 11.6 with 2; the down projection, K = 9728, 11.0
+        // with 4 against 11.4 with 3)
+        if (splits > 1)
+            cost += (double)splits * (sp.mt * 16 * N * 8 / 4000.0 + 300.0) + (nblk <= kSyncWords ? 800.0 : 3000.0);
         if (cost < best) {
             best = cost;
             sp.splits = splits;

@@ -165,6 +165,10 @@ struct SmallPlan {
     size_t lds;          // dynamic LDS bytes of the GEMM kernel
 };
 SmallPlan plan_small(int kind, int M, int N, int K);
+// Overrides the small-M plan's K slices across blocks (1..16) for later calls
+// where that count fits the plan's register budget; 0 keeps the planner's
+// choice (inspection and timing).
+void set_small_plan_override(int splits);
 hipError_t launch_small(const GemmArgs& a, const SmallPlan& sp, hipStream_t st);
 
 // Fused small-M W4A4 linear (group-256 Sylvester rotation): one launch whose

@@ -61,6 +61,28 @@ def test_big_plan_override_arguments_and_workspace(L):
     assert L.cr_workspace_bytes(3, M, N, K) == base
 
 
+def test_small_plan_override_arguments_and_workspace(L):
+    """The small-M split override takes 0..16; a count that fits changes the
+    workspace's partial tiles, one that does not (K = 9728 at M = 76 needs at
+    least 3 slices for its loads to fit the registers) keeps the planner's."""
+    assert L.cr_dbg_small_plan(17) == CR["SHAPE"]
+    assert L.cr_dbg_small_plan(-1) == CR["SHAPE"]
+    M, N, K = 76, 2560, 9728
+    base = L.cr_workspace_bytes(0, M, N, K)
+    try:
+        assert L.cr_dbg_small_plan(8) == CR["OK"]
+        eight = L.cr_workspace_bytes(0, M, N, K)
+        assert L.cr_dbg_small_plan(3) == CR["OK"]
+        three = L.cr_workspace_bytes(0, M, N, K)
+        # partial tiles: [splits][N / 16][5 activation tiles][64 lanes] x 16 B
+        assert eight - three == (8 - 3) * (N // 16) * 5 * 64 * 16
+        assert L.cr_dbg_small_plan(1) == CR["OK"]
+        assert L.cr_workspace_bytes(0, M, N, K) == base
+    finally:
+        assert L.cr_dbg_small_plan(0) == CR["OK"]
+    assert L.cr_workspace_bytes(0, M, N, K) == base
+
+
 def test_sizes(L):
     # W4A4: N rounded to 32 rows, two codes per byte, one int32 per row
     assert L.cr_packed_bytes(0, 12288, 3072) == 12288 * 3072 // 2 + 12288 * 4

@@ -58,3 +58,32 @@ def test_small_m_split_k_calls_in_a_row(crp, kind, M, K, N, bias):
         r = ref(xb)
         assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(r["y"]))
     assert np.array_equal(acc.cpu().numpy(), ref(xs[-1])["acc"])
+
+
+# forced split counts (cr_dbg_small_plan), including ones the planner would
+# not take: 2 to 16 slices
+FORCED = [(0, 76, 9728, 2560, True, 3), (0, 76, 9728, 2560, False, 8), (3, 76, 2560, 2560, True, 2),
+          (3, 76, 2560, 2560, False, 5), (0, 76, 2560, 9728, True, 2), (1, 50, 4096, 300, True, 16),
+          (2, 40, 3840, 256, False, 6)]
+
+
+@pytest.mark.parametrize("kind,M,K,N,bias,splits", FORCED)
+def test_small_m_forced_splits(crp, kind, M, K, N, bias, splits):
+    print(f"[splitk-small-forced] kind={kind} M={M} K={K} N={N} splits={splits}", flush=True)
+    L = si.random_layer(M, K, N, seed=M + K + N + kind + splits, bias=bias, outlier_count=5)
+    (p, s), ref = _weights(crp, kind, L)
+    b = to_dev_bf16(L.bias) if bias else None
+    fn = {0: crp.linear_w4a4, 1: crp.linear_int8tw, 2: crp.linear_w4a8, 3: crp.linear_int8rot}[kind]
+    crp.dbg_small_plan(splits)
+    try:
+        ws = torch.empty(crp.workspace_bytes(kind, M, N, K), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xA5)
+        xs = [L.x, si.random_layer(M, K, 1, seed=7 + kind, outlier_count=5).x]
+        ys = [fn(to_dev_bf16(xb), p, s, N, b, workspace=ws).clone() for xb in xs]
+        acc = crp.dbg_linear_acc(kind, to_dev_bf16(xs[0]), p, N, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        crp.dbg_small_plan(0)
+    for xb, y in zip(xs, ys):
+        assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), O.f32_to_bf16_rne(ref(xb)["y"]))
+    assert np.array_equal(acc.cpu().numpy(), ref(xs[0])["acc"])
