@@ -379,7 +379,7 @@ cr_status cr_dbg_fused_timeouts(uint32_t* count);
 /* Large-M GEMM plan override (M > 128), for inspection and timing: later
  * calls use block tiles 256 x bn and K split into `splits` equal slices
  * across blocks, in place of the planner's choice.
- *   bn: 256, 192 or 128 (W4A8's own GEMM keeps 256), 0 = the planner's.
+ *   bn: 256, 192, 128 or 64 (W4A8's own GEMM keeps 256), 0 = the planner's.
  *   splits: 1..16, 0 = the planner's; a count that does not divide the
  *           layer's 64-k chunks leaves the planner's split for that layer.
  * Any other value -> CR_ERR_SHAPE.  The workspace a call needs follows the

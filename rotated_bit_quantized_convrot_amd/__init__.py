@@ -287,8 +287,8 @@ def dbg_fused_config(mode: int, spin_limit: int = -1) -> None:
 
 
 def dbg_big_plan(bn: int = 0, splits: int = 0) -> None:
-    """Large-M GEMM plan for later calls: block tiles 256 x ``bn`` (256, 192
-    or 128) and ``splits`` K slices across blocks; 0 keeps the planner's
+    """Large-M GEMM plan for later calls: block tiles 256 x ``bn`` (256, 192,
+    128 or 64) and ``splits`` K slices across blocks; 0 keeps the planner's
     choice.  Size workspaces after setting it."""
     _check(lib().cr_dbg_big_plan(int(bn), int(splits)))
 

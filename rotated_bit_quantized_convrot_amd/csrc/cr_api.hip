@@ -697,7 +697,8 @@ cr_status cr_dbg_fused_config(int mode, int spin_limit) {
 }
 
 cr_status cr_dbg_big_plan(int bn, int splits) {
-    if (bn != 0 && bn != 128 && bn != 192 && bn != 256) return fail(CR_ERR_SHAPE, "bn must be 0, 128, 192 or 256, got %d", bn);
+    if (bn != 0 && bn != 64 && bn != 128 && bn != 192 && bn != 256)
+        return fail(CR_ERR_SHAPE, "bn must be 0, 64, 128, 192 or 256, got %d", bn);
     if (splits < 0 || splits > 16) return fail(CR_ERR_SHAPE, "splits must be 0..16, got %d", splits);
     cr::set_big_plan_override(bn, splits);
     return ok();

@@ -107,11 +107,12 @@ __device__ __forceinline__ void big_tile_origin(int lid, int tiles_m, int tiles_
 // 8 waves, block tile 256 (m) x BN (n), NS-stage LDS ring.  BN = 256: 2
 // waves along m x 4 along n, wave tile 128 x 64; BN = 192 (fills the chip
 // where 256-wide tiles leave CUs idle): 4 x 2, wave tile 64 x 96; BN = 128
-// (layers with few output tiles): 4 x 2, wave tile 64 x 64.
+// (layers with few output tiles): 4 x 2, wave tile 64 x 64; BN = 64 (fewer
+// still): 4 x 2, wave tile 64 x 32.
 template <int WK, int NW, int NS, int BN_>
 struct BigCfg {
     static_assert(NW == 8, "8 waves");
-    static_assert(BN_ == 256 || BN_ == 192 || BN_ == 128, "block tile width");
+    static_assert(BN_ == 256 || BN_ == 192 || BN_ == 128 || BN_ == 64, "block tile width");
     static constexpr int BN = BN_;
     static constexpr int NWT = BN / 32;                                // 32-row weight tiles per stage
     static constexpr int WM = BN == 256 ? 2 : 4;                       // waves along m
@@ -135,9 +136,14 @@ struct BigCfg {
     static constexpr int EPI_TR = 80;
     static constexpr int EPI_OPB = FN * 32 * (4 + 4 + (PA ? 4 : 0));
     static constexpr int EPI_BYTES = NW * (32 * EPI_TR + EPI_OPB);
-    // W4A4 stages are too small to hold it: its own region after the ring
+    // W4A4 stages are too small to hold it: its own region after the ring.
+    // int8 operands: in the ring buffer of the stage just consumed, or (64-wide
+    // tiles, whose stage holds the staging rows only) the rows there and the
+    // column operands in a region after the ring.
+    static constexpr bool EPI_OPS_IN_RING = !PA && EPI_BYTES <= STAGE;
     static constexpr size_t EPI_OFF = (size_t)NS * STAGE;
-    static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0) + (PA ? EPI_BYTES : 0);
+    static constexpr size_t LDS = (size_t)NS * STAGE + (WK == WK_W4A8 ? 4096 : 0) +
+                                  (PA ? EPI_BYTES : (EPI_OPS_IN_RING ? 0 : NW * EPI_OPB));
     static_assert(A_BYTES % (NW * 1024) == 0 && WB % 16 == 0 && CB % 16 == 0 && CB <= 1024, "load split");
 };
 
@@ -496,14 +502,20 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_big(GemmArgs p, int tiles_m, i
                 // 44.2 us, W4A8 at M = 4096 195.9 -> 190.2 us.)
                 constexpr int TR = C::EPI_TR, OPB = C::EPI_OPB;
                 int8_t* ebase;
+                int8_t* obase;
                 if constexpr (C::PA) {
                     ebase = ring + C::EPI_OFF;
-                } else {
-                    static_assert(C::EPI_BYTES <= C::STAGE, "epilogue scratch fits one stage buffer");
+                    obase = ebase + NW * 32 * TR;
+                } else if constexpr (C::EPI_OPS_IN_RING) {
                     ebase = ring + B * C::STAGE;
+                    obase = ebase + NW * 32 * TR;
+                } else {
+                    static_assert(NW * 32 * TR <= C::STAGE, "staging rows fit one stage buffer");
+                    ebase = ring + B * C::STAGE;
+                    obase = ring + C::EPI_OFF + (WK == WK_W4A8 ? 4096 : 0);
                 }
                 int8_t* scr = ebase + wave * 32 * TR;
-                int8_t* sop = ebase + NW * 32 * TR + wave * OPB;
+                int8_t* sop = obase + wave * OPB;
                 float sxv[FM];
                 int rnv[FM];                                  // W4A4: -128 ra[m]
 #pragma unroll
@@ -706,7 +718,7 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
 // at M = 1220 29.2 -> 25.9 us without a split instead of 4 slices; and it
 // fills the last round where 256-wide tiles leave half of it idle: the W4A8
 // layer's int8 GEMM, 640 tiles of 256 x 256 against 1280 of 256 x 128,
-// 186.5 -> 182.0 us);
+// 186.5 -> 182.0 us), and 0.41 for a 256 x 64 tile (below);
 // rounds of one unit per CU; plus, for a split, the int32 partial tiles
 // written and read back at about 4.5 TB/s and a second launch.  Anything
 // other than 256-wide whole tiles has to win by 5%.  Slices divide the K
@@ -714,6 +726,11 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
 // for the narrower tiles' epilogue scratch).
 constexpr int BIG_CUS = 256;
 constexpr double BIG_T128 = 0.55;   // a 256 x 128 tile's stage, relative to 256 x 256
+// a 256 x 64 tile's stage: 64 x 32 wave tiles, 1.5x the LDS bytes per MFMA
+// of 64 x 64; measured with forced plans, ConvRot INT8 2560^2 at M = 1220
+// (200 whole tiles against 100 of 256 x 128): 19.8-20.5 us against
+// 26.9-27.1 us; slower on every other bench layer
+constexpr double BIG_T64 = 0.41;
 constexpr int BIG_MAX_SPLITS = 16;
 
 // Plan override for inspection and timing (cr_dbg_big_plan): block tile width
@@ -733,10 +750,10 @@ BigPlan plan_big(int kind, int M, int N, int K) {
     const double t_stage = kind == WK_W4 ? 0.8 : (wk_i8w(kind) ? 1.0 : 1.3);
     const double tiles_m = (double)((M + BIG_BM - 1) / BIG_BM);
     double best = std::ceil(tiles_m * ((N + 255) / 256) / BIG_CUS) * nkc * t_stage;
-    for (int bn : {256, 192, 128}) {
+    for (int bn : {256, 192, 128, 64}) {
         if (bn != 256 && kind == WK_W4A8) continue;
         const double total = tiles_m * ((N + bn - 1) / bn);
-        const double ts = t_stage * (bn == 256 ? 1.0 : (bn == 192 ? 0.9 : BIG_T128));
+        const double ts = t_stage * (bn == 256 ? 1.0 : (bn == 192 ? 0.9 : (bn == 128 ? BIG_T128 : BIG_T64)));
         for (int S = 1; S <= BIG_MAX_SPLITS && S <= nkc; ++S) {
             if (nkc % S != 0 || (bn == 256 && S == 1)) continue;
             double cost = std::ceil(total * S / BIG_CUS) * (nkc / S) * ts;
@@ -796,6 +813,7 @@ static hipError_t launch_big_t(const GemmArgs& a, hipStream_t st) {
     if constexpr (WK != WK_W4A8) {
         if (bp.bn == 192) return launch_big_bn<WK, ACC, 192>(a, bp, st);
         if (bp.bn == 128) return launch_big_bn<WK, ACC, 128>(a, bp, st);
+        if (bp.bn == 64) return launch_big_bn<WK, ACC, 64>(a, bp, st);
     }
     if (bp.bn != 256) return hipErrorInvalidValue;
     return launch_big_bn<WK, ACC, 256>(a, bp, st);

@@ -130,8 +130,8 @@ struct GemmArgs {
     int spin_limit;        // polls of the bounded wait for the producers
 };
 
-// Large-M path plan: block tiles 256 x bn (bn = 256, or 192 where that fills
-// more of the chip), K split into `splits` equal slices of `cps` 64-k chunks
+// Large-M path plan: block tiles 256 x bn (bn = 256, or 192, 128 or 64 where
+// that fills more of the chip), K split into `splits` equal slices of `cps` 64-k chunks
 // when the output has too few tiles to fill the chip; the slices' int32
 // partial tiles ([splits][tiles][256 x bn] in fragment order) are added by a
 // second kernel.

@@ -46,6 +46,7 @@ def test_big_plan_override_arguments_and_workspace(L):
     slices; the workspace size follows the forced plan (int32 partial tiles
     of every slice) and returns to the planner's once cleared."""
     assert L.cr_dbg_big_plan(100, 0) == CR["SHAPE"]
+    assert L.cr_dbg_big_plan(32, 0) == CR["SHAPE"]
     assert L.cr_dbg_big_plan(128, 17) == CR["SHAPE"]
     assert L.cr_dbg_big_plan(0, -1) == CR["SHAPE"]
     M, N, K = 1220, 2560, 2560

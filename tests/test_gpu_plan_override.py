@@ -1,5 +1,5 @@
 """Large-M GEMMs on plans the planner would not take, forced with
-cr_dbg_big_plan: other block tile widths (256, 192, 128) and K splits (2..8
+cr_dbg_big_plan: other block tile widths (256, 192, 128, 64) and K splits (2..8
 slices, added by the second kernel), on ragged shapes, for W4A4,
 int8_tensorwise, ConvRot INT8 and W4A8.  The int32 sums are exact, so the
 outputs and accumulators must equal the oracle's bit for bit whatever the
@@ -32,6 +32,9 @@ CASES = [
     (0, 300, 4096, 512, 128, 2), (0, 520, 2560, 300, 192, 4), (0, 1220, 2560, 2560, 256, 2),
     (0, 257, 9728, 1024, 128, 8), (1, 260, 2688, 200, 128, 3), (1, 300, 1000, 37, 192, 2),
     (3, 1220, 2560, 2560, 128, 4), (3, 700, 1536, 900, 256, 3), (2, 400, 1024, 264, 256, 2),
+    # 256 x 64 tiles: whole tiles and K slices, ragged M and N (N % 8 != 0)
+    (3, 1220, 2560, 2560, 64, 1), (0, 1220, 9728, 2560, 64, 1), (1, 300, 1000, 37, 64, 2),
+    (0, 520, 2560, 300, 64, 1), (1, 4096, 3072, 3072, 64, 1), (0, 257, 9728, 1024, 64, 4),
 ]
 
 
