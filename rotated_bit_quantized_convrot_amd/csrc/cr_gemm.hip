@@ -695,11 +695,46 @@ __global__ void __launch_bounds__(256) k_big_fixup(GemmArgs p, int tiles_m, int 
             sum[q].x += v.x; sum[q].y += v.y; sum[q].z += v.z; sum[q].w += v.w;
         }
     }
-    if (m >= p.M) return;
     const Epi epi = make_epi(p);
+    const int mrow0 = m0 + (wave % WM) * WROWS + i * 32;            // the fragment's first row and column
+    const int ncol0 = n0 + ((wave / WM) * FN + f) * 32;
+    const int nbase = ncol0 + 4 * h;
+    if (!ACC && mrow0 + 32 <= p.M && ncol0 + 32 <= p.N && (p.N & 7) == 0) {
+        // Whole fragment: the outputs pass through LDS so that each store
+        // writes 64-byte row segments (4 lanes x 16 bytes, 16 rows per
+        // store) instead of 16-byte pieces of 32 rows; same arithmetic as
+        // store4.  Rows of 64 bytes padded to 80.
+        __shared__ __attribute__((aligned(16))) uint8_t stg[4][32 * 80];
+        uint8_t* stw = stg[threadIdx.x >> 6];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const Epi4 op = epi4_fetch<WK>(epi, p.sx, p.M, m, nbase + 8 * q);
+            int a[4] = {sum[q].x, sum[q].y, sum[q].z, sum[q].w};
+            if constexpr (WK == WK_W4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = w4_exact(a[j], op.rn, op.cn[j]);
+            }
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = (float)a[j] * op.sx;
+                v[j] = v[j] * op.sw[j];
+                v[j] = v[j] + op.b[j];          // -0.0 without a bias
+            }
+            *reinterpret_cast<uint2*>(stw + l32 * 80 + 8 * h + 16 * q) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            const int lr = (lane >> 2) + 16 * sg;
+            const uint4 o = *reinterpret_cast<const uint4*>(stw + lr * 80 + (lane & 3) * 16);
+            *reinterpret_cast<uint4*>(p.y + (size_t)(mrow0 + lr) * p.N + ncol0 + (lane & 3) * 8) = o;
+        }
+        return;
+    }
+    if (m >= p.M) return;
     const float sw0 = (wk_chan(WK) || ACC) ? 0.0f : p.wscale[0];
     const float sxm = ACC ? 0.0f : p.sx[m];
-    const int nbase = n0 + ((wave / WM) * FN + f) * 32 + 4 * h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int n = nbase + 8 * q;
