@@ -240,6 +240,49 @@ __global__ void __launch_bounds__(256) k_quant_act_plain(const uint16_t* __restr
 }
 
 
+// The same for K % 8 == 0 and K <= 8 * CH * blockDim.x, in one pass: each
+// thread keeps its CH 8-value chunks (chunk tid + j * blockDim.x) in
+// registers between the row maximum and the codes instead of reading the row
+// again.  Same arithmetic and outputs as k_quant_act_plain.
+template <int CH>
+__global__ void __launch_bounds__(256) k_quant_act_plain_reg(const uint16_t* __restrict__ x, int M, int K, int Kp,
+                                                             int8_t* __restrict__ qx, float* __restrict__ sx,
+                                                             uint32_t* __restrict__ sync) {
+    __shared__ float red[16];
+    zero_sync(sync);
+    const int m = blockIdx.x;
+    const uint16_t* row = x + (size_t)m * K;
+    int8_t* out = qx + (size_t)m * Kp;
+    const int nch = K >> 3;
+    uint4 raw[CH];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        raw[j] = c < nch ? reinterpret_cast<const uint4*>(row)[c] : make_uint4(0u, 0u, 0u, 0u);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(raw[j].x)), fabsf(bf16_hi(raw[j].x))),
+                                 fmaxf(fabsf(bf16_lo(raw[j].y)), fabsf(bf16_hi(raw[j].y)))));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(raw[j].z)), fabsf(bf16_hi(raw[j].z))),
+                                 fmaxf(fabsf(bf16_lo(raw[j].w)), fabsf(bf16_hi(raw[j].w)))));
+    }
+    amax = block_max(amax, red);
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) sx[m] = s;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c < nch) {
+            uint2 o;
+            o.x = pack4_i8(quant_code<-128, 127>(bf16_lo(raw[j].x), s), quant_code<-128, 127>(bf16_hi(raw[j].x), s),
+                           quant_code<-128, 127>(bf16_lo(raw[j].y), s), quant_code<-128, 127>(bf16_hi(raw[j].y), s));
+            o.y = pack4_i8(quant_code<-128, 127>(bf16_lo(raw[j].z), s), quant_code<-128, 127>(bf16_hi(raw[j].z), s),
+                           quant_code<-128, 127>(bf16_lo(raw[j].w), s), quant_code<-128, 127>(bf16_hi(raw[j].w), s));
+            *reinterpret_cast<uint2*>(out + (size_t)c * 8) = o;
+        }
+    }
+    for (int k = K + threadIdx.x; k < Kp; k += blockDim.x) out[k] = 0;
+}
+
 template <int QMAX, int LO, int HI, bool PACKED, int GS = 256, bool GLU = false>
 static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K, int8_t* qx, float* sx, int32_t* ra,
                              uint32_t* sync, hipStream_t st) {
@@ -314,7 +357,19 @@ hipError_t launch_quant_act(int kind, int group, const uint16_t* x, int M, int K
     // W4A8 and ConvRot INT8: rotated, per-row int8
     if (kind == WK_W4A8 || kind == WK_I8R) return launch_rot<127, -128, 127, false>(x, nullptr, M, K, qx, sx, nullptr, sync, st);
     // two waves per row when four per row would exceed what the chip holds at once
-    k_quant_act_plain<<<dim3(M), dim3(M * 4 > 8192 ? 128 : 256), 0, st>>>(x, M, K, Kp, qx, sx, sync);
+    const int threads = M * 4 > 8192 ? 128 : 256;
+    const int ch = (K / 8 + threads - 1) / threads;
+    if (K % 8 == 0 && ch >= 1 && ch <= 4) {
+        const dim3 grid(M), block(threads);
+        switch (ch) {
+            case 1: k_quant_act_plain_reg<1><<<grid, block, 0, st>>>(x, M, K, Kp, qx, sx, sync); break;
+            case 2: k_quant_act_plain_reg<2><<<grid, block, 0, st>>>(x, M, K, Kp, qx, sx, sync); break;
+            case 3: k_quant_act_plain_reg<3><<<grid, block, 0, st>>>(x, M, K, Kp, qx, sx, sync); break;
+            default: k_quant_act_plain_reg<4><<<grid, block, 0, st>>>(x, M, K, Kp, qx, sx, sync); break;
+        }
+        return hipGetLastError();
+    }
+    k_quant_act_plain<<<dim3(M), dim3(threads), 0, st>>>(x, M, K, Kp, qx, sx, sync);
     return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ ACT_CASES = [
     (0, 33, 512), (0, 17, 768), (0, 9, 1024), (0, 7, 1280), (0, 3, 32768), (0, 300, 3072),
     (1, 64, 2688), (1, 9, 100), (1, 17, 3072), (1, 1, 7),
     (1, 33, 512), (1, 5, 4096), (1, 130, 1000), (1, 4, 4104),
+    # int8_tensorwise rows held in registers: 1 to 4 chunks of 8 per thread
+    (1, 40, 8192), (1, 3, 6144), (1, 2049, 3072), (1, 2050, 4096),
     (2, 40, 3840), (2, 3, 256),
     # grids larger than the chip holds at once: two groups per lane (rotated)
     # or two waves per row (int8_tensorwise)
