@@ -131,13 +131,15 @@ __global__ void __launch_bounds__(1024) k_quant_act_rot(const uint16_t* __restri
     }
 }
 
-// W4A4 activations, four rows per block: lanes 16r..16r+15 of every wave
+// Rotated activations, four rows per block: lanes 16r..16r+15 of every wave
 // work on row 4 blockIdx.x + r, wave w on groups w, w + nw, ... (GPL at
-// most), so that each store instruction writes, for every 64-k chunk it
-// touches, the four rows' 32-byte pieces: one whole 128-byte line of the
-// 4-bit tile.  Same arithmetic as k_quant_act_rot (PACKED).
-template <int GPL, int GS, bool GLU>
-__global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
+// most).  PACKED (W4A4): each store instruction writes, for every 64-k chunk
+// it touches, the four rows' 32-byte pieces: one whole 128-byte line of the
+// 4-bit tile.  Otherwise (the int8 codes of W4A8 and ConvRot INT8, QMAX 127)
+// rows of [M, K] int8, 16 bytes per lane.  Same arithmetic as
+// k_quant_act_rot.
+template <int GPL, int GS, bool GLU, int QMAX = 7, int LO = -8, int HI = 7, bool PACKED = true>
+__global__ void __launch_bounds__(1024) k_quant_rows4(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
                                                          int M, int K, int8_t* __restrict__ qx, float* __restrict__ sx,
                                                          int32_t* __restrict__ ra, uint32_t* __restrict__ sync) {
     __shared__ float redm[16][4];
@@ -168,10 +170,10 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
     amax = 0.0f;
     for (int w = 0; w < nw; ++w) amax = fmaxf(amax, redm[w][r]);
 
-    const float s = (amax * rot_norm<GS>()) / 7.0f;
+    const float s = (amax * rot_norm<GS>()) / (float)QMAX;
     const float sigma = fwht16_sign<GS>(j);
     const bool fast = amax >= 0x1p-100f && amax <= 0x1p100f;
-    const float s_u = amax / 7.0f;
+    const float s_u = amax / (float)QMAX;
     const float rinv = sigma * (1.0f / s_u);
     int hsum = 0;
 #pragma unroll
@@ -179,19 +181,32 @@ __global__ void __launch_bounds__(1024) k_quant_w4_rows4(const uint16_t* __restr
         const int g = wave + i * nw;
         if (row_ok && g < G) {
             float c[16];
-            codes16<7, -8, 7, GS>(v[i], fast, rinv, sigma, s_u, s, c);
-            hsum += (int)(c[4] + c[5] + c[6] + c[7] + c[12] + c[13] + c[14] + c[15]);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + act4_offset(m, g * 256 + j * 16, K)) =
-                pack_act16(c);
+            codes16<QMAX, LO, HI, GS>(v[i], fast, rinv, sigma, s_u, s, c);
+            if constexpr (PACKED) {
+                hsum += (int)(c[4] + c[5] + c[6] + c[7] + c[12] + c[13] + c[14] + c[15]);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(qx) + act4_offset(m, g * 256 + j * 16, K)) =
+                    pack_act16(c);
+            } else {
+                uint4 o;
+                o.x = pack4_codes((int)c[0], (int)c[1], (int)c[2], (int)c[3]);
+                o.y = pack4_codes((int)c[4], (int)c[5], (int)c[6], (int)c[7]);
+                o.z = pack4_codes((int)c[8], (int)c[9], (int)c[10], (int)c[11]);
+                o.w = pack4_codes((int)c[12], (int)c[13], (int)c[14], (int)c[15]);
+                *reinterpret_cast<uint4*>(qx + (size_t)m * K + (size_t)g * 256 + j * 16) = o;
+            }
         }
     }
-    for (int o = 1; o < 16; o <<= 1) hsum += __shfl_xor(hsum, o, 64);
-    if (j == 0) reds[wave][r] = hsum;
-    __syncthreads();
+    if constexpr (PACKED) {
+        for (int o = 1; o < 16; o <<= 1) hsum += __shfl_xor(hsum, o, 64);
+        if (j == 0) reds[wave][r] = hsum;
+        __syncthreads();
+    }
     if (wave == 0 && j == 0 && row_ok) {
-        int t = 0;
-        for (int w = 0; w < nw; ++w) t += reds[w][r];
-        ra[m] = t;
+        if constexpr (PACKED) {
+            int t = 0;
+            for (int w = 0; w < nw; ++w) t += reds[w][r];
+            ra[m] = t;
+        }
         sx[m] = s;
     }
 }
@@ -294,6 +309,24 @@ static hipError_t launch_rot(const uint16_t* x, const uint16_t* u, int M, int K,
         k_quant_act_rot<1, QMAX, LO, HI, PACKED, GS, GLU><<<dim3((M + rows - 1) / rows), dim3(256), 0, st>>>(x, u, M, K, lg, qx, sx, ra, sync);
         return hipGetLastError();
     }
+    const int G = K >> 8;
+    if constexpr (!PACKED) {
+        // four rows per block where there are rows enough to fill the chip
+        // (the rule of the packed W4A4 activations)
+        if (M >= 2048 && G <= 32) {
+            int g4 = 1;
+            while ((G + g4 - 1) / g4 > 16) g4 <<= 1;
+            if (g4 == 1 && G >= 8) g4 = 2;
+            const int nw = (G + g4 - 1) / g4;
+            const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
+            switch (g4) {
+                case 1: k_quant_rows4<1, GS, GLU, QMAX, LO, HI, false><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, nullptr, sync); break;
+                case 2: k_quant_rows4<2, GS, GLU, QMAX, LO, HI, false><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, nullptr, sync); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     int gpl = 1;
     while ((T + gpl - 1) / gpl > 1024) gpl <<= 1;
     // more groups per lane (fewer waves) while the grid would exceed what the
@@ -331,9 +364,9 @@ static hipError_t launch_w4_act(const uint16_t* x, const uint16_t* u, int M, int
         const int nw = (G + gpl - 1) / gpl;
         const dim3 grid((unsigned)((M + 3) / 4)), block((unsigned)(64 * nw));
         switch (gpl) {
-            case 1: k_quant_w4_rows4<1, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
-            case 2: k_quant_w4_rows4<2, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
-            case 4: k_quant_w4_rows4<4, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
+            case 1: k_quant_rows4<1, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
+            case 2: k_quant_rows4<2, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
+            case 4: k_quant_rows4<4, GS, GLU><<<grid, block, 0, st>>>(x, u, M, K, qx, sx, ra, sync); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

@@ -45,6 +45,8 @@ ACT_CASES = [
     (1, 33, 512), (1, 5, 4096), (1, 130, 1000), (1, 4, 4104),
     # int8_tensorwise rows held in registers: 1 to 4 chunks of 8 per thread
     (1, 40, 8192), (1, 3, 6144), (1, 2049, 3072), (1, 2050, 4096),
+    # rotated int8 codes (and unpacked W4A4 codes) four rows per block at M >= 2048
+    (3, 2049, 2560), (3, 2050, 8192), (2, 2051, 256), (0, 2052, 3072),
     (2, 40, 3840), (2, 3, 256),
     # grids larger than the chip holds at once: two groups per lane (rotated)
     # or two waves per row (int8_tensorwise)
